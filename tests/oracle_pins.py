@@ -1,0 +1,446 @@
+"""Pins for the attention oracle: checks against what the pages and the
+mathematics fix, independent of the oracle's own formulas.
+
+Each ``check_*`` function takes the implementation under test (the oracle, or
+a mutant with one planted mistake) and raises AssertionError on a violation.
+``tests/test_oracle.py`` runs them on the oracle; ``tests/test_oracle_mutants.py``
+runs them on mutants and requires each mutant to fail at least one.
+
+Implementation interface (a module or a SimpleNamespace):
+  softmax_rows(S) -> P
+  additive_mask(n_q, n_k, mask_kind, key_length) -> [n_q][n_k] of 0 / -inf
+  sdpa_ref(Q, K, V, scale, mask_kind, key_lengths) -> O   (float64, [B][h][n][d])
+  mha_ref(X_q, X_kv, Wq, Wk, Wv, Wo, h, mask_kind, key_lengths) -> Y
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+NONE, CAUSAL, PAD, BOTH = 0, 1, 2, 3
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _weights(impl, Q, K, scale, mask_kind=NONE, key_lengths=None):
+    """Attention weights observed through the public sdpa call: with V the
+    n_k x n_k identity, O = P."""
+    B, h, _, _ = Q.shape
+    n_k = K.shape[2]
+    V = np.broadcast_to(np.eye(n_k), (B, h, n_k, n_k)).copy()
+    return impl.sdpa_ref(Q, K, V, scale, mask_kind, key_lengths)
+
+
+def _visible(n_q, n_k, mask_kind, L):
+    """Visibility by integer comparison (its own definition, not the oracle's)."""
+    vis = np.ones((n_q, n_k), dtype=bool)
+    for r in range(n_q):
+        for c in range(n_k):
+            if mask_kind & CAUSAL and c > r:
+                vis[r, c] = False
+            if mask_kind & PAD and c >= L:
+                vis[r, c] = False
+    return vis
+
+
+# ---------------------------------------------------------------- printed values
+
+def check_softmax_printed(impl):
+    """Printed: softmax([1,2,3]) ~ [0.090, 0.245, 0.665]; [10,20,30] puts
+    weight close to 1 on the last entry (hex4c59.cc, section
+    "为什么要按键的维度缩放？")."""
+    g = _golden("softmax_printed.json")
+    c0, c1 = g["cases"]
+    p = impl.softmax_rows(np.array([c0["scores"]], dtype=np.float64))[0]
+    assert np.array_equal(np.round(p, c0["decimals"]), np.array(c0["printed_weights"])), p
+    p = impl.softmax_rows(np.array([c1["scores"]], dtype=np.float64))[0]
+    assert p[-1] >= c1["min_last_weight"] and p[-1] < 1.0, p
+
+
+def check_worked_example(impl):
+    """Printed weights [0.4011, 0.1978, 0.4011] and output [1.6044, 1.1978]
+    for one query over three keys, d_k = 2 (hex4c59.cc, sections
+    "六步算完一行注意力" and "用几十行代码核对刚才的数值"), on a derived
+    instance consistent with them, plus the closed form of the weights."""
+    g = _golden("worked_example_one_row.json")
+    scale = 1.0 / math.sqrt(g["d_k"])
+    Q = np.array(g["q"], dtype=np.float64).reshape(1, 1, 1, 2)
+    K = np.array(g["K"], dtype=np.float64).reshape(1, 1, 3, 2)
+    V = np.array(g["V"], dtype=np.float64).reshape(1, 1, 3, 2)
+    w = _weights(impl, Q, K, scale)[0, 0, 0]
+    o = impl.sdpa_ref(Q, K, V, scale, NONE, None)[0, 0, 0]
+    assert np.array_equal(np.round(w, g["decimals"]), np.array(g["printed_weights"])), w
+    assert np.array_equal(np.round(o, g["decimals"]), np.array(g["printed_output"])), o
+    a = math.exp(1.0 / math.sqrt(2.0))
+    closed = np.array([a, 1.0, a]) / (2.0 * a + 1.0)
+    assert np.allclose(w, closed, rtol=0, atol=1e-14), (w, closed)
+
+
+def check_causal_pattern(impl):
+    """The printed 5x5 causal mask (devpress.csdn.net, section 3.1)."""
+    g = _golden("causal_mask_5x5.json")
+    want = np.array([[0.0 if x == "0" else -np.inf for x in row] for row in g["printed"]])
+    got = impl.additive_mask(g["n"], g["n"], CAUSAL, None)
+    assert np.array_equal(got, want), got
+
+
+# ---------------------------------------------------------------- invariants
+
+def check_rows_are_distributions(impl):
+    """Weights are non-negative, each row sums to 1, masked entries are
+    exactly 0 (hex4c59.cc, section "六步算完一行注意力": softmax gives
+    non-negative weights summing to 1; section "掩码必须在 softmax 之前生效":
+    future weight becomes 0)."""
+    r = _rng(1)
+    for kind, n_q, n_k in ((NONE, 5, 7), (CAUSAL, 6, 6), (PAD, 4, 9), (BOTH, 8, 8)):
+        B, h, d = 2, 2, 5
+        Q = r.standard_normal((B, h, n_q, d)) * 2
+        K = r.standard_normal((B, h, n_k, d))
+        kl = np.array([3, n_k]) if kind & PAD else None
+        P = _weights(impl, Q, K, 1 / math.sqrt(d), kind, kl)
+        assert np.all(P >= 0)
+        assert np.allclose(P.sum(-1), 1.0, atol=1e-13)
+        for b in range(B):
+            vis = _visible(n_q, n_k, kind, None if kl is None else kl[b])
+            assert np.all(P[b][:, ~vis] == 0.0)
+            assert np.all(P[b][:, vis] > 0.0)
+
+
+def check_convex_combination(impl):
+    """Each output row is a convex combination of the visible value rows
+    (hex4c59.cc, section "六步算完一行注意力"), so every coordinate lies in
+    [min, max] of that coordinate over the visible rows."""
+    r = _rng(2)
+    for kind in (NONE, CAUSAL, PAD, BOTH):
+        B, h, n, d = 2, 3, 9, 4
+        Q = r.standard_normal((B, h, n, d)) * 3
+        K = r.standard_normal((B, h, n, d))
+        V = r.standard_normal((B, h, n, d)) * 5
+        kl = np.array([2, 7]) if kind & PAD else None
+        O = impl.sdpa_ref(Q, K, V, 0.5, kind, kl)
+        for b in range(B):
+            vis = _visible(n, n, kind, None if kl is None else kl[b])
+            for hh in range(h):
+                for q in range(n):
+                    rows = V[b, hh][vis[q]]
+                    assert np.all(O[b, hh, q] >= rows.min(0) - 1e-12)
+                    assert np.all(O[b, hh, q] <= rows.max(0) + 1e-12)
+
+
+def check_permutation_equivariance(impl):
+    """Unmasked attention commutes with a permutation of the positions:
+    Attn(PQ, PK, PV) = P Attn(Q, K, V) (hex4c59.cc, section
+    "没有循环，模型怎样知道词序？").  For cross-attention, permuting K and V
+    rows jointly changes nothing."""
+    r = _rng(3)
+    B, h, n, d = 1, 2, 7, 6
+    Q = r.standard_normal((B, h, n, d))
+    K = r.standard_normal((B, h, n, d))
+    V = r.standard_normal((B, h, n, 5))
+    perm = r.permutation(n)
+    O = impl.sdpa_ref(Q, K, V, 0.4, NONE, None)
+    Op = impl.sdpa_ref(Q[:, :, perm], K[:, :, perm], V[:, :, perm], 0.4, NONE, None)
+    assert np.allclose(Op, O[:, :, perm], atol=1e-13)
+    K2 = r.standard_normal((B, h, 11, d))
+    V2 = r.standard_normal((B, h, 11, 5))
+    perm2 = r.permutation(11)
+    O2 = impl.sdpa_ref(Q, K2, V2, 0.4, NONE, None)
+    O2p = impl.sdpa_ref(Q, K2[:, :, perm2], V2[:, :, perm2], 0.4, NONE, None)
+    assert np.allclose(O2, O2p, atol=1e-13)
+
+
+def check_causal_row0_and_last(impl):
+    """Causal: query 0 sees only key 0, so output row 0 is value row 0
+    exactly; the last query sees every key, so its row equals the unmasked
+    result (hex4c59.cc, section "掩码必须在 softmax 之前生效")."""
+    r = _rng(4)
+    B, h, n, d = 2, 2, 6, 4
+    Q, K, V = (r.standard_normal((B, h, n, d)) for _ in range(3))
+    O = impl.sdpa_ref(Q, K, V, 0.5, CAUSAL, None)
+    assert np.array_equal(O[:, :, 0], V[:, :, 0])
+    U = impl.sdpa_ref(Q, K, V, 0.5, NONE, None)
+    assert np.allclose(O[:, :, -1], U[:, :, -1], atol=1e-14)
+
+
+def check_zero_query_means(impl):
+    """Q = 0 makes every visible score equal, so the weights are uniform and
+    the output is the mean of the visible value rows: all rows unmasked,
+    prefix means under the causal mask, the first L_b rows under padding
+    (closed form)."""
+    r = _rng(5)
+    B, h, n, d = 2, 1, 8, 3
+    Q = np.zeros((B, h, n, d))
+    K = r.standard_normal((B, h, n, d))
+    V = r.standard_normal((B, h, n, d))
+    kl = np.array([3, 8])
+    for kind in (NONE, CAUSAL, PAD, BOTH):
+        O = impl.sdpa_ref(Q, K, V, 1.0, kind, kl if kind & PAD else None)
+        for b in range(B):
+            vis = _visible(n, n, kind, kl[b])
+            for q in range(n):
+                assert np.allclose(O[b, 0, q], V[b, 0][vis[q]].mean(0), atol=1e-14)
+
+
+def check_identical_keys_uniform(impl):
+    """Identical key rows give identical scores, hence uniform weights for any
+    query (closed form)."""
+    r = _rng(6)
+    B, h, n, d = 1, 1, 5, 4
+    Q = r.standard_normal((B, h, 3, d)) * 4
+    K = np.broadcast_to(r.standard_normal((1, 1, 1, d)), (B, h, n, d)).copy()
+    P = _weights(impl, Q, K, 0.5)
+    assert np.allclose(P, 1.0 / n, atol=1e-15)
+
+
+def check_future_perturbation(impl):
+    """Causal: changing key/value rows j > i leaves output row i unchanged,
+    bit for bit (future positions get weight exactly 0)."""
+    r = _rng(7)
+    B, h, n, d = 1, 2, 9, 4
+    Q, K, V = (r.standard_normal((B, h, n, d)) for _ in range(3))
+    O = impl.sdpa_ref(Q, K, V, 0.5, CAUSAL, None)
+    for i in range(n - 1):
+        K2, V2 = K.copy(), V.copy()
+        K2[:, :, i + 1:] = r.standard_normal(K2[:, :, i + 1:].shape) * 10
+        V2[:, :, i + 1:] = r.standard_normal(V2[:, :, i + 1:].shape) * 10
+        O2 = impl.sdpa_ref(Q, K2, V2, 0.5, CAUSAL, None)
+        assert np.array_equal(O2[:, :, : i + 1], O[:, :, : i + 1])
+
+
+def check_padding_truncation(impl):
+    """Key padding with length L equals unmasked attention over K[:L], V[:L]
+    (the plain formula on the valid keys), and changing padded rows changes
+    nothing."""
+    r = _rng(8)
+    B, h, n_q, n_k, d = 3, 2, 5, 9, 4
+    Q = r.standard_normal((B, h, n_q, d))
+    K = r.standard_normal((B, h, n_k, d))
+    V = r.standard_normal((B, h, n_k, d))
+    kl = np.array([1, 4, 9])
+    O = impl.sdpa_ref(Q, K, V, 0.5, PAD, kl)
+    for b in range(B):
+        L = kl[b]
+        Ob = impl.sdpa_ref(Q[b:b + 1], K[b:b + 1, :, :L], V[b:b + 1, :, :L], 0.5, NONE, None)
+        assert np.allclose(O[b:b + 1], Ob, atol=1e-14)
+    K2, V2 = K.copy(), V.copy()
+    for b in range(B):
+        K2[b, :, kl[b]:] = 1e3
+        V2[b, :, kl[b]:] = -1e3
+    assert np.array_equal(impl.sdpa_ref(Q, K2, V2, 0.5, PAD, kl), O)
+
+
+def check_saturation(impl):
+    """Scores of magnitude ~1e3 must neither overflow nor give NaN: the row
+    softmax is computed stably (hex4c59.cc, section "用几十行代码核对刚才的数值");
+    the largest score takes all the weight."""
+    B, h, n, d = 1, 1, 4, 2
+    Q = np.array([[[[30.0, 0.0]] * n]])
+    K = np.array([[[[100.0, 0.0], [99.0, 0.0], [-50.0, 0.0], [98.0, 0.0]]]])
+    V = np.array([[[[1.0, 2.0], [3.0, 4.0], [5.0, 6.0], [7.0, 8.0]]]])
+    O = impl.sdpa_ref(Q, K, V, 1.0, NONE, None)
+    assert np.all(np.isfinite(O))
+    assert np.allclose(O[0, 0, 0], V[0, 0, 0], atol=1e-12)
+
+
+def check_scale_statistics(impl):
+    """For i.i.d. zero-mean unit-variance q and k components the scaled score
+    q.k / sqrt(d_k) has variance 1 (hex4c59.cc, section
+    "为什么要按键的维度缩放？"; devpress.csdn.net, section 2.1 derivation).
+    Scores are recovered from the weights: log P_j - log P_0 = s_j - s_0, whose
+    variance is 2 Var(s)."""
+    r = _rng(9)
+    d, n, rows = 64, 16, 512
+    Q = r.standard_normal((1, 1, rows, d))
+    K = r.standard_normal((1, 1, n, d))
+    P = _weights(impl, Q, K, 1.0 / math.sqrt(d))[0, 0]
+    diff = np.log(P[:, 1:]) - np.log(P[:, :1])
+    v = diff.var() / 2.0
+    assert 0.85 < v < 1.15, v
+
+
+# ---------------------------------------------------------------- brute force / library
+
+def _nested(a):
+    return a.tolist()
+
+
+def check_bruteforce_sdpa(impl):
+    """Matrix form against the pure-Python loops on tiny shapes: n_q != n_k,
+    causal, padding, both, h > 1, d_v != d_k."""
+    from oracle.bruteforce import attention_bruteforce
+    r = _rng(10)
+    for kind, n_q, n_k, d_k, d_v in ((NONE, 3, 5, 4, 2), (CAUSAL, 4, 4, 3, 5), (PAD, 2, 6, 2, 3),
+                                     (BOTH, 5, 5, 4, 4), (NONE, 1, 1, 3, 3)):
+        B, h = 2, 2
+        Q = r.standard_normal((B, h, n_q, d_k))
+        K = r.standard_normal((B, h, n_k, d_k))
+        V = r.standard_normal((B, h, n_k, d_v))
+        kl = [max(1, n_k - 2), n_k] if kind & PAD else None
+        got = impl.sdpa_ref(Q, K, V, 0.7, kind, None if kl is None else np.array(kl))
+        want = np.array(attention_bruteforce(_nested(Q), _nested(K), _nested(V), 0.7, kind, kl))
+        assert np.allclose(got, want, rtol=0, atol=1e-13), np.abs(got - want).max()
+
+
+def check_library_sdpa(impl):
+    """Cross-check against torch.nn.functional.scaled_dot_product_attention in
+    float64 on the CPU (a library routine computing the same definition; its
+    output only is used)."""
+    import torch
+    import torch.nn.functional as F
+    r = _rng(11)
+    B, h, n_q, n_k, d = 2, 3, 17, 23, 8
+    Q = r.standard_normal((B, h, n_q, d))
+    K = r.standard_normal((B, h, n_k, d))
+    V = r.standard_normal((B, h, n_k, d))
+    got = impl.sdpa_ref(Q, K, V, 0.3, NONE, None)
+    want = F.scaled_dot_product_attention(torch.from_numpy(Q), torch.from_numpy(K),
+                                          torch.from_numpy(V), scale=0.3).numpy()
+    assert np.allclose(got, want, atol=1e-12)
+    Kc, Vc = K[:, :, :n_q], V[:, :, :n_q]
+    got = impl.sdpa_ref(Q, Kc, Vc, 0.3, CAUSAL, None)
+    want = F.scaled_dot_product_attention(torch.from_numpy(Q), torch.from_numpy(Kc.copy()),
+                                          torch.from_numpy(Vc.copy()), is_causal=True,
+                                          scale=0.3).numpy()
+    assert np.allclose(got, want, atol=1e-12)
+    kl = np.array([5, 23])
+    keep = np.zeros((B, 1, 1, n_k), dtype=bool)
+    for b in range(B):
+        keep[b, :, :, : kl[b]] = True
+    got = impl.sdpa_ref(Q, K, V, 0.3, PAD, kl)
+    want = F.scaled_dot_product_attention(torch.from_numpy(Q), torch.from_numpy(K),
+                                          torch.from_numpy(V), attn_mask=torch.from_numpy(keep),
+                                          scale=0.3).numpy()
+    assert np.allclose(got, want, atol=1e-12)
+
+
+# ---------------------------------------------------------------- multi-head block
+
+def _mha_inputs(r, B, n_q, n_k, dm, h, d_k, d_v):
+    X_q = r.standard_normal((B, n_q, dm))
+    X_kv = r.standard_normal((B, n_k, dm))
+    Wq = r.standard_normal((dm, h * d_k)) / math.sqrt(dm)
+    Wk = r.standard_normal((dm, h * d_k)) / math.sqrt(dm)
+    Wv = r.standard_normal((dm, h * d_v)) / math.sqrt(dm)
+    Wo = r.standard_normal((h * d_v, dm)) / math.sqrt(h * d_v)
+    return X_q, X_kv, Wq, Wk, Wv, Wo
+
+
+def check_bruteforce_mha(impl):
+    """Multi-head block against the loop version on tiny shapes: self
+    (same array), causal, cross with padding and d_v != d_k."""
+    from oracle.bruteforce import mha_bruteforce
+    r = _rng(12)
+    for kind, n_q, n_k, self_attn in ((NONE, 4, 4, True), (CAUSAL, 5, 5, True), (PAD, 3, 6, False)):
+        B, dm, h, d_k, d_v = 2, 6, 2, 3, 4
+        X_q, X_kv, Wq, Wk, Wv, Wo = _mha_inputs(r, B, n_q, n_k, dm, h, d_k, d_v)
+        if self_attn:
+            X_kv = X_q
+        kl = [2, n_k] if kind & PAD else None
+        got = impl.mha_ref(X_q, X_kv, Wq, Wk, Wv, Wo, h, kind, None if kl is None else np.array(kl))
+        want = np.array(mha_bruteforce(_nested(X_q), _nested(X_kv), _nested(Wq), _nested(Wk),
+                                       _nested(Wv), _nested(Wo), h, kind, kl))
+        assert np.allclose(got, want, rtol=0, atol=1e-12), np.abs(got - want).max()
+
+
+def check_mha_head_blocks(impl):
+    """Head i owns column block i of W^Q, W^K, W^V and row block i of W^O
+    (head split by contiguous blocks, concat in head order; hex4c59.cc,
+    section "多头注意力让一次读取有多组投影"; devpress.csdn.net section 2.2).
+    With W^V zero outside block i only head i carries values, so: zeroing
+    row block i of W^O gives Y = 0, changing any other row block of W^O or
+    any other column block of W^Q/W^K changes nothing, and changing block i
+    of W^Q changes Y."""
+    r = _rng(13)
+    B, n, dm, h, d = 2, 5, 8, 4, 2
+    X, _, Wq, Wk, Wv, Wo = _mha_inputs(r, B, n, n, dm, h, d, d)
+    for i in (0, 2):
+        Wv_i = np.zeros_like(Wv)
+        Wv_i[:, i * d:(i + 1) * d] = Wv[:, i * d:(i + 1) * d]
+        Y = impl.mha_ref(X, X, Wq, Wk, Wv_i, Wo, h, NONE, None)
+        assert np.abs(Y).max() > 1e-3
+        Wo0 = Wo.copy()
+        Wo0[i * d:(i + 1) * d] = 0
+        assert np.abs(impl.mha_ref(X, X, Wq, Wk, Wv_i, Wo0, h, NONE, None)).max() < 1e-14
+        for j in range(h):
+            if j == i:
+                continue
+            Wo2 = Wo.copy()
+            Wo2[j * d:(j + 1) * d] = r.standard_normal((d, dm))
+            Wq2 = Wq.copy()
+            Wq2[:, j * d:(j + 1) * d] = r.standard_normal((dm, d))
+            Wk2 = Wk.copy()
+            Wk2[:, j * d:(j + 1) * d] = r.standard_normal((dm, d))
+            assert np.allclose(impl.mha_ref(X, X, Wq2, Wk2, Wv_i, Wo2, h, NONE, None), Y,
+                               atol=1e-13)
+        Wq3 = Wq.copy()
+        Wq3[:, i * d:(i + 1) * d] *= 3.0
+        assert np.abs(impl.mha_ref(X, X, Wq3, Wk, Wv_i, Wo, h, NONE, None) - Y).max() > 1e-6
+
+
+def check_mha_identity_reduction(impl):
+    """h = 1 with identity projections reduces the block to bare attention
+    SDPA(X, X, X) with scale 1/sqrt(d_model) (special case of the formula)."""
+    r = _rng(14)
+    B, n, dm = 2, 6, 5
+    X = r.standard_normal((B, n, dm))
+    I = np.eye(dm)
+    for kind in (NONE, CAUSAL):
+        Y = impl.mha_ref(X, X, I, I, I, I, 1, kind, None)
+        X4 = X[:, None]
+        O = impl.sdpa_ref(X4, X4, X4, 1.0 / math.sqrt(dm), kind, None)[:, 0]
+        assert np.allclose(Y, O, atol=1e-14)
+
+
+def check_mha_cross_sources(impl):
+    """Cross-attention: queries come from X_q only, keys and values from X_kv
+    only (hex4c59.cc, section "解码器有两种读取：看前缀，以及看源句"): rows of
+    X_q act independently, and changing X_q does not change what a fixed
+    query reads from X_kv."""
+    r = _rng(15)
+    B, n_q, n_k, dm, h, d = 1, 3, 7, 6, 2, 3
+    X_q, X_kv, Wq, Wk, Wv, Wo = _mha_inputs(r, B, n_q, n_k, dm, h, d, d)
+    Y = impl.mha_ref(X_q, X_kv, Wq, Wk, Wv, Wo, h, NONE, None)
+    X_q2 = X_q.copy()
+    X_q2[:, 1:] = r.standard_normal(X_q2[:, 1:].shape)
+    Y2 = impl.mha_ref(X_q2, X_kv, Wq, Wk, Wv, Wo, h, NONE, None)
+    assert np.allclose(Y2[:, 0], Y[:, 0], atol=1e-14)
+    X_kv2 = X_kv.copy()
+    X_kv2[:, 2] += 1.0
+    assert np.abs(impl.mha_ref(X_q, X_kv2, Wq, Wk, Wv, Wo, h, NONE, None) - Y).max() > 1e-6
+
+
+ALL_SDPA_CHECKS = [
+    check_softmax_printed,
+    check_worked_example,
+    check_causal_pattern,
+    check_rows_are_distributions,
+    check_convex_combination,
+    check_permutation_equivariance,
+    check_causal_row0_and_last,
+    check_zero_query_means,
+    check_identical_keys_uniform,
+    check_future_perturbation,
+    check_padding_truncation,
+    check_saturation,
+    check_scale_statistics,
+    check_bruteforce_sdpa,
+    check_library_sdpa,
+]
+
+ALL_MHA_CHECKS = [
+    check_bruteforce_mha,
+    check_mha_head_blocks,
+    check_mha_identity_reduction,
+    check_mha_cross_sources,
+]

@@ -1,0 +1,153 @@
+"""The pins are discriminating: each planted mistake in an oracle copy must
+fail at least one of them (CPU only; mistakes are planted in the oracle,
+never in GPU code)."""
+
+import math
+import types
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle_pins as pins
+
+
+def _build(scores=None, mask=None, softmax=None, combine=None, split=None, concat=None,
+           mha_scale=None, kv_source=None):
+    """An oracle-shaped namespace with one or more steps replaced."""
+    scores = scores or (lambda Q, K, s: oracle.scaled_scores(Q, K, s))
+    mask = mask or oracle.additive_mask
+    softmax = softmax or oracle.softmax_rows
+    combine = combine or (lambda P, V: P @ V)
+    split = split or oracle.split_heads
+    concat = concat or oracle.concat_heads
+
+    def sdpa_ref(Q, K, V, scale, mask_kind=0, key_lengths=None):
+        B, h, n_q, _ = Q.shape
+        n_k = K.shape[2]
+        S = scores(Q, K, scale)
+        for b in range(B):
+            L = None if key_lengths is None else int(key_lengths[b])
+            S[b] = S[b] + mask(n_q, n_k, mask_kind, L)[None]
+        return combine(softmax(S), V)
+
+    def mha_ref(X_q, X_kv, Wq, Wk, Wv, Wo, h, mask_kind=0, key_lengths=None):
+        d_k = Wq.shape[1] // h
+        src = X_q if kv_source == "q" else X_kv
+        Q = split(X_q @ Wq, h)
+        K = split(src @ Wk, h)
+        V = split(src @ Wv, h)
+        sc = mha_scale(Wq, h, X_q) if mha_scale else 1.0 / math.sqrt(d_k)
+        return concat(sdpa_ref(Q, K, V, sc, mask_kind, key_lengths)) @ Wo
+
+    return types.SimpleNamespace(softmax_rows=softmax, additive_mask=mask, sdpa_ref=sdpa_ref,
+                                 mha_ref=mha_ref)
+
+
+def _mask_diag_hidden(n_q, n_k, kind, L=None):
+    M = oracle.additive_mask(n_q, n_k, kind & 2, L)
+    if kind & 1:
+        M[np.arange(n_k)[None, :] >= np.arange(n_q)[:, None]] = -np.inf
+    return M
+
+
+def _mask_pad_off_by_one(n_q, n_k, kind, L=None):
+    M = oracle.additive_mask(n_q, n_k, kind & 1, None)
+    if kind & 2:
+        M[:, np.arange(n_k) > L] = -np.inf
+    return M
+
+
+def _softmax_no_shift(S):
+    e = np.exp(S)
+    return e / e.sum(-1, keepdims=True)
+
+
+def _softmax_cols(S):
+    m = np.max(S, axis=-2, keepdims=True)
+    e = np.exp(S - m)
+    return e / e.sum(-2, keepdims=True)
+
+
+def _zero_fill_sdpa():
+    base = _build()
+
+    def sdpa_ref(Q, K, V, scale, mask_kind=0, key_lengths=None):
+        B, h, n_q, _ = Q.shape
+        n_k = K.shape[2]
+        S = oracle.scaled_scores(Q, K, scale)
+        for b in range(B):
+            L = None if key_lengths is None else int(key_lengths[b])
+            S[b][:, np.isinf(oracle.additive_mask(n_q, n_k, mask_kind, L))] = 0.0
+        return oracle.softmax_rows(S) @ V
+    base.sdpa_ref = sdpa_ref
+    return base
+
+
+def _post_softmax_zero_sdpa():
+    base = _build()
+
+    def sdpa_ref(Q, K, V, scale, mask_kind=0, key_lengths=None):
+        B, h, n_q, _ = Q.shape
+        n_k = K.shape[2]
+        P = oracle.softmax_rows(oracle.scaled_scores(Q, K, scale))
+        for b in range(B):
+            L = None if key_lengths is None else int(key_lengths[b])
+            P[b][:, np.isinf(oracle.additive_mask(n_q, n_k, mask_kind, L))] = 0.0
+        return P @ V
+    base.sdpa_ref = sdpa_ref
+    return base
+
+
+def _interleaved_split(Y, h):
+    B, n, hd = Y.shape
+    d = hd // h
+    return Y.reshape(B, n, d, h).transpose(0, 3, 1, 2)
+
+
+def _reversed_concat(O):
+    return oracle.concat_heads(O[:, ::-1])
+
+
+MUTANTS = {
+    "scale_ignored": lambda: _build(scores=lambda Q, K, s: oracle.scaled_scores(Q, K, 1.0)),
+    "scale_squared": lambda: _build(scores=lambda Q, K, s: oracle.scaled_scores(Q, K, s * s)),
+    "score_sign": lambda: _build(scores=lambda Q, K, s: -oracle.scaled_scores(Q, K, s)),
+    "keys_for_queries": lambda: _build(scores=lambda Q, K, s: oracle.scaled_scores(K, K, s)[..., :Q.shape[2], :]
+                                       if K.shape[2] >= Q.shape[2] else oracle.scaled_scores(Q, K, s) * 0),
+    "causal_diagonal_hidden": lambda: _build(mask=_mask_diag_hidden),
+    "padding_off_by_one": lambda: _build(mask=_mask_pad_off_by_one),
+    "mask_zero_fill": _zero_fill_sdpa,
+    "mask_after_softmax": _post_softmax_zero_sdpa,
+    "softmax_no_max_shift": lambda: _build(softmax=_softmax_no_shift),
+    "softmax_over_queries": lambda: _build(softmax=_softmax_cols),
+    "weights_transposed": lambda: _build(combine=lambda P, V: np.swapaxes(P, -1, -2)[..., :V.shape[-2]] @ V
+                                         if P.shape[-1] == P.shape[-2] else P @ V * 0.5),
+    "values_unweighted_mean": lambda: _build(combine=lambda P, V: np.broadcast_to(
+        V.mean(-2, keepdims=True), P.shape[:-1] + V.shape[-1:]).copy()),
+    "mha_interleaved_heads": lambda: _build(split=_interleaved_split),
+    "mha_concat_reversed": lambda: _build(concat=_reversed_concat),
+    "mha_scale_dmodel": lambda: _build(mha_scale=lambda Wq, h, X: 1.0 / math.sqrt(X.shape[-1]) * 0.5),
+    "mha_kv_from_queries": lambda: _build(kv_source="q"),
+}
+
+
+def _fails_some_pin(impl):
+    failed = []
+    for check in pins.ALL_SDPA_CHECKS + pins.ALL_MHA_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check(impl)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            failed.append(check.__name__)
+    return failed
+
+
+def test_unmutated_copy_passes_every_pin():
+    assert _fails_some_pin(_build()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name):
+    failed = _fails_some_pin(MUTANTS[name]())
+    assert failed, f"planted mistake {name!r} passed every pin"
