@@ -1,0 +1,28 @@
+"""Multi-head scaled dot-product attention, forward, on AMD MI355X (gfx950).
+
+The computation lives in ``libmha.so`` (HIP kernels behind a C ABI declared
+in ``include/mha.h``); this package is its Python binding plus the seeded
+synthetic workloads used by the tests and the bench.
+"""
+
+from ._binding import (  # noqa: F401
+    MHAError,
+    alloc_workspace,
+    lib,
+    mha_attend,
+    mha_forward,
+    mha_project_in,
+    mha_project_out,
+    sdpa_forward,
+    workspace_bytes,
+    workspace_views,
+)
+from .workloads import (  # noqa: F401
+    MASK_CAUSAL,
+    MASK_CAUSAL_KEY_PADDING,
+    MASK_KEY_PADDING,
+    MASK_NONE,
+    WORKLOADS,
+    Workload,
+    generate,
+)

@@ -1,0 +1,233 @@
+"""ctypes binding of libmha's C ABI (include/mha.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current
+stream.  There is no fallback: if ``libmha.so`` is missing or the tensors
+are not on the GPU, the calls raise.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+from .workloads import MASK_CAUSAL, MASK_KEY_PADDING
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmha.so")
+
+DTYPE_BF16 = 0
+DTYPE_F32 = 1
+MAX_PADDED_BATCH = 256
+
+STATUS = {
+    0: "MHA_OK", -1: "MHA_ERR_NULL", -2: "MHA_ERR_DIM", -3: "MHA_ERR_MASK", -4: "MHA_ERR_KEYLEN",
+    -5: "MHA_ERR_UNSUPPORTED", -6: "MHA_ERR_WORKSPACE", -7: "MHA_ERR_HIP", -8: "MHA_ERR_SCALE",
+}
+
+# Every symbol include/mha.h declares, with its ctypes signature.
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_SIG = {
+    "sdpa_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _I, _P]),
+    "mha_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
+    "mha_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P,
+                         ctypes.c_size_t, _P]),
+    "mha_project_in": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
+                            ctypes.c_size_t, _P]),
+    "mha_attend": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _I, _P, ctypes.c_size_t, _P]),
+    "mha_project_out": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
+    "mha_status_str": (ctypes.c_char_p, [_I]),
+}
+
+_lib = None
+
+
+class MHAError(RuntimeError):
+    def __init__(self, fn, status):
+        self.status = status
+        self.fn = fn
+        text = lib().mha_status_str(status).decode()
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({text})")
+
+
+def lib():
+    """Load libmha.so (built in-tree by ``python -m head_attention_forward_amd.build``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m head_attention_forward_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIG.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != 0:
+        raise MHAError(fn, status)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t, name):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live in GPU memory (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _key_lengths(mask_kind, key_lengths, B):
+    """Host int32 array for the C call (None unless the padding bit is set)."""
+    if not (mask_kind & MASK_KEY_PADDING):
+        return None, None
+    if key_lengths is None:
+        return None, None  # the C layer reports MHA_ERR_KEYLEN
+    if isinstance(key_lengths, torch.Tensor):
+        vals = key_lengths.detach().to("cpu", torch.int64).tolist()
+    else:
+        vals = [int(x) for x in key_lengths]
+    arr = (ctypes.c_int32 * max(1, len(vals)))(*vals)
+    return arr, ctypes.cast(arr, ctypes.c_void_p)
+
+
+def sdpa_forward(Q, K, V, scale=None, mask_kind=0, key_lengths=None, out=None, stream=None):
+    """O = softmax(Q K^T * scale + M) V per (batch, head).
+
+    Q [B][h][n_q][d_k], K [B][h][n_k][d_k], V [B][h][n_k][d_v] on the GPU, all bf16
+    or all fp32.  scale defaults to 1/sqrt(d_k).  Returns O [B][h][n_q][d_v]."""
+    B, h, n_q, d_k = Q.shape
+    n_k, d_v = K.shape[2], V.shape[3]
+    if K.shape != (B, h, n_k, d_k) or V.shape != (B, h, n_k, d_v):
+        raise ValueError("Q, K, V shapes disagree")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((B, h, n_q, d_v), dtype=Q.dtype, device=Q.device)
+    elif out.shape != (B, h, n_q, d_v) or out.dtype != Q.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    arr, kl = _key_lengths(mask_kind, key_lengths, B)
+    st = lib().sdpa_forward(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(out, "out"),
+                            B, h, n_q, n_k, d_k, d_v, float(scale), int(mask_kind), kl,
+                            _dtype_code(Q), _stream(stream))
+    _check("sdpa_forward", st)
+    return out
+
+
+def workspace_bytes(B, n_q, n_k, h, d_k, d_v, dtype=torch.bfloat16):
+    code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
+    return int(lib().mha_workspace_bytes(B, n_q, n_k, h, d_k, d_v, code))
+
+
+def alloc_workspace(B, n_q, n_k, h, d_k, d_v, device="cuda", dtype=torch.bfloat16):
+    """A caller-owned workspace tensor (uint8) sized for the block."""
+    n = workspace_bytes(B, n_q, n_k, h, d_k, d_v, dtype)
+    if n == 0:
+        raise ValueError("invalid sizes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def _mha_dims(X_q, X_kv, Wq, Wk, Wv, Wo, h):
+    B, n_q, d_model = X_q.shape
+    n_k = X_kv.shape[1]
+    if X_kv.shape != (B, n_k, d_model):
+        raise ValueError("X_kv shape disagrees with X_q")
+    if Wq.shape[0] != d_model or Wq.shape[1] % h:
+        raise ValueError("Wq must be [d_model][h*d_k]")
+    d_k = Wq.shape[1] // h
+    d_v = Wv.shape[1] // h
+    if Wk.shape != (d_model, h * d_k) or Wv.shape != (d_model, h * d_v) or Wo.shape != (h * d_v, d_model):
+        raise ValueError("projection weight shapes disagree")
+    return B, n_q, n_k, d_model, d_k, d_v
+
+
+def mha_forward(X_q, X_kv, Wq, Wk, Wv, Wo, h, mask_kind=0, key_lengths=None, out=None,
+                workspace=None, stream=None):
+    """Y = Concat(head_1..head_h) W^O, head_i = Attention(X_q W_i^Q, X_kv W_i^K, X_kv W_i^V).
+
+    Pass the same tensor as X_q and X_kv for self-attention.  Returns Y
+    [B][n_q][d_model]."""
+    B, n_q, n_k, d_model, d_k, d_v = _mha_dims(X_q, X_kv, Wq, Wk, Wv, Wo, h)
+    if out is None:
+        out = torch.empty((B, n_q, d_model), dtype=X_q.dtype, device=X_q.device)
+    if workspace is None:
+        workspace = alloc_workspace(B, n_q, n_k, h, d_k, d_v, X_q.device, X_q.dtype)
+    arr, kl = _key_lengths(mask_kind, key_lengths, B)
+    st = lib().mha_forward(_dev(X_q, "X_q"), _dev(X_kv, "X_kv"), _dev(Wq, "Wq"), _dev(Wk, "Wk"),
+                           _dev(Wv, "Wv"), _dev(Wo, "Wo"), _dev(out, "out"),
+                           B, n_q, n_k, d_model, h, d_k, d_v, int(mask_kind), kl,
+                           _dtype_code(X_q), _dev(workspace, "workspace"),
+                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("mha_forward", st)
+    return out
+
+
+def mha_project_in(X_q, X_kv, Wq, Wk, Wv, h, workspace, stream=None):
+    B, n_q, d_model = X_q.shape
+    n_k = X_kv.shape[1]
+    d_k = Wq.shape[1] // h
+    d_v = Wv.shape[1] // h
+    st = lib().mha_project_in(_dev(X_q, "X_q"), _dev(X_kv, "X_kv"), _dev(Wq, "Wq"), _dev(Wk, "Wk"),
+                              _dev(Wv, "Wv"), B, n_q, n_k, d_model, h, d_k, d_v,
+                              _dtype_code(X_q), _dev(workspace, "workspace"),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("mha_project_in", st)
+
+
+def mha_attend(B, n_q, n_k, h, d_k, d_v, workspace, mask_kind=0, key_lengths=None,
+               dtype=torch.bfloat16, stream=None):
+    arr, kl = _key_lengths(mask_kind, key_lengths, B)
+    code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
+    st = lib().mha_attend(B, n_q, n_k, h, d_k, d_v, int(mask_kind), kl, code,
+                          _dev(workspace, "workspace"),
+                          workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("mha_attend", st)
+
+
+def mha_project_out(Wo, Y, B, n_q, n_k, h, d_k, d_v, workspace, stream=None):
+    d_model = Wo.shape[1]
+    st = lib().mha_project_out(_dev(Wo, "Wo"), _dev(Y, "Y"), B, n_q, n_k, d_model, h, d_k, d_v,
+                               _dtype_code(Y), _dev(workspace, "workspace"),
+                               workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("mha_project_out", st)
+
+
+def workspace_views(workspace, B, n_q, n_k, h, d_k, d_v):
+    """Views of the workspace's Q, K, V ([B][h][n][d]) and concatenated O
+    ([B][n_q][h*d_v]) as documented at mha_workspace_bytes (bf16)."""
+    def up(x):
+        return (x + 255) // 256 * 256
+    e = 2
+    sizes = [B * h * n_q * d_k, B * h * n_k * d_k, B * h * n_k * d_v, B * n_q * h * d_v]
+    offs = []
+    o = 0
+    for s in sizes:
+        offs.append(o)
+        o += up(e * s)
+    flat = workspace.view(torch.uint8)
+
+    def view(i, shape):
+        return flat[offs[i]:offs[i] + e * sizes[i]].view(torch.bfloat16).view(*shape)
+    return (view(0, (B, h, n_q, d_k)), view(1, (B, h, n_k, d_k)), view(2, (B, h, n_k, d_v)),
+            view(3, (B, n_q, h * d_v)))

@@ -1,0 +1,55 @@
+// Internal interface between the C-ABI layer (mha_api.hip) and the kernels.
+// Not installed; the public interface is include/mha.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/mha.h"
+
+namespace mha {
+
+// Strides are in elements; the innermost (feature) dimension is contiguous.
+struct AttnArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  void* O;
+  int64_t q_sb, q_sh, q_sr;   // batch, head, row strides of Q
+  int64_t k_sb, k_sh, k_sr;
+  int64_t v_sb, v_sh, v_sr;
+  int64_t o_sb, o_sh, o_sr;
+  int B, h, n_q, n_k;
+  float scale;        // multiplies q.k
+  int causal;         // key j hidden from query i when j > i
+  int padded;         // key j hidden in batch b when j >= key_len[b]
+  int32_t key_len[MHA_MAX_PADDED_BATCH];
+};
+
+// One column segment of a projection GEMM: columns [0, width) of weight W
+// (row stride = width) and the per-head scatter of the result:
+//   out element (row m, column c) -> dst[((b*heads + c/hd)*rows + pos)*hd + c%hd]
+// with b = m / rows, pos = m % rows, hd = head width.  A plain row-major
+// [M][width] output is heads = 1, hd = width, rows = M.
+struct GemmSeg {
+  const void* W;
+  void* dst;
+  int width;
+  int hd;
+  int heads;
+  int rows;
+};
+
+struct GemmArgs {
+  const void* A;      // [M][K] row-major
+  int M, K;
+  int nseg;
+  GemmSeg seg[3];
+  int col_start[4];   // prefix sums of segment widths; col_start[nseg] = N
+};
+
+hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s);
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+
+}  // namespace mha

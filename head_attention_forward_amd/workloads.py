@@ -1,0 +1,141 @@
+"""Seeded synthetic workloads for multi-head attention.
+
+This module only draws inputs: shapes, distributions and random numbers.  It
+holds none of the attention arithmetic and is shared by the tests, the bench
+and the smoke check (the oracle never imports it; callers hand it arrays).
+
+The pages' workloads are WMT 2014 translation batches, which are not used;
+seeded Gaussian tensors of the pages' model shapes stand in for them:
+the base model (d_model = 512, h = 8, d_k = d_v = 64) and the big model
+(d_model = 1024, h = 16).  Base shapes follow hex4c59.cc "读懂 Attention Is All
+You Need" (section "多头注意力让一次读取有多组投影") and research-heat.pages.dev
+"做法" (section "一次平均不够，因而切开多头"); batch 32 x length 100 matches
+the worked shapes of devpress.csdn.net "【深度学习】Transformer", section 2.2.
+
+Recipe (every workload): one ``torch.Generator('cpu')`` seeded with ``seed``;
+fp32 standard-normal draws scaled by the stated standard deviation, in the
+fixed order X_q, X_kv (cross-attention only), Wq, Wk, Wv, Wo, key_lengths for
+the multi-head block and Q, K, V for bare attention; then a round-to-nearest-
+even cast to bf16 (fp32 workloads stay fp32).  Projection weights have
+variance 1/d_model.  Key lengths are integers drawn uniformly from
+[lo, hi] inclusive.
+"""
+
+import dataclasses
+import math
+from typing import Optional, Tuple
+
+import torch
+
+MASK_NONE = 0
+MASK_CAUSAL = 1
+MASK_KEY_PADDING = 2
+MASK_CAUSAL_KEY_PADDING = 3
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str            # "sdpa" (bare attention) or "mha" (full block)
+    dtype: str           # "bf16" or "f32"
+    B: int
+    n_q: int
+    n_k: int
+    h: int
+    d_k: int
+    d_v: int
+    mask: int
+    d_model: int = 0
+    self_attn: bool = False
+    key_len_range: Optional[Tuple[int, int]] = None
+    description: str = ""
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def nominal_attention_flops(self):
+        """4 * B * h * n_q * n_k * d_k (QK^T and PV, dense)."""
+        return 4.0 * self.B * self.h * self.n_q * self.n_k * self.d_k
+
+    def replace(self, **kw):
+        return dataclasses.replace(self, **kw)
+
+
+WORKLOADS = {
+    "sdpa_f32_tiny": Workload(
+        "sdpa_f32_tiny", "sdpa", "f32", B=1, n_q=64, n_k=64, h=1, d_k=64, d_v=64,
+        mask=MASK_NONE,
+        description="bare attention, fp32, B=1 h=1 n=64 d=64, unmasked"),
+    "encoder_self_base": Workload(
+        "encoder_self_base", "mha", "bf16", B=32, n_q=100, n_k=100, h=8, d_k=64, d_v=64,
+        mask=MASK_NONE, d_model=512, self_attn=True,
+        description="encoder self-attention block, bf16, B=32 n=100 d_model=512 h=8 d=64"),
+    "decoder_causal_base": Workload(
+        "decoder_causal_base", "mha", "bf16", B=16, n_q=512, n_k=512, h=8, d_k=64, d_v=64,
+        mask=MASK_CAUSAL, d_model=512, self_attn=True,
+        description="decoder causal self-attention block, bf16, B=16 n=512 d_model=512 h=8"),
+    "cross_padded_big": Workload(
+        "cross_padded_big", "mha", "bf16", B=32, n_q=96, n_k=128, h=16, d_k=64, d_v=64,
+        mask=MASK_KEY_PADDING, d_model=1024, self_attn=False, key_len_range=(64, 128),
+        description="cross-attention block, bf16, B=32 n_q=96 n_k=128 d_model=1024 h=16, "
+                    "key padding with lengths in [64,128]"),
+    "long_causal_sdpa": Workload(
+        "long_causal_sdpa", "sdpa", "bf16", B=4, n_q=4096, n_k=4096, h=16, d_k=64, d_v=64,
+        mask=MASK_CAUSAL,
+        description="bare causal attention, bf16, B=4 h=16 n=4096 d=64"),
+}
+
+ORDER = ["sdpa_f32_tiny", "encoder_self_base", "decoder_causal_base", "cross_padded_big",
+         "long_causal_sdpa"]
+
+
+def _normal(g, shape, std, dtype):
+    x = torch.randn(shape, generator=g, dtype=torch.float32)
+    if std != 1.0:
+        x = x * std
+    return x.to(dtype)
+
+
+def generate(w: Workload, seed: int = 0):
+    """Draw the inputs of ``w`` on the CPU.  Returns a dict of tensors.
+
+    sdpa: Q [B][h][n_q][d_k], K [B][h][n_k][d_k], V [B][h][n_k][d_v], scale,
+          key_lengths (int32 [B] or None).
+    mha:  X_q [B][n_q][d_model], X_kv (the same tensor object for
+          self-attention), Wq/Wk [d_model][h*d_k], Wv [d_model][h*d_v],
+          Wo [h*d_v][d_model], key_lengths.
+    """
+    g = torch.Generator("cpu")
+    g.manual_seed(seed)
+    dt = w.torch_dtype
+    out = {}
+    if w.kind == "sdpa":
+        out["Q"] = _normal(g, (w.B, w.h, w.n_q, w.d_k), 1.0, dt)
+        out["K"] = _normal(g, (w.B, w.h, w.n_k, w.d_k), 1.0, dt)
+        out["V"] = _normal(g, (w.B, w.h, w.n_k, w.d_v), 1.0, dt)
+        out["scale"] = 1.0 / math.sqrt(w.d_k)
+    else:
+        std = 1.0 / math.sqrt(w.d_model)
+        out["X_q"] = _normal(g, (w.B, w.n_q, w.d_model), 1.0, dt)
+        if w.self_attn:
+            if w.n_q != w.n_k:
+                raise ValueError("self-attention needs n_q == n_k")
+            out["X_kv"] = out["X_q"]
+        else:
+            out["X_kv"] = _normal(g, (w.B, w.n_k, w.d_model), 1.0, dt)
+        out["Wq"] = _normal(g, (w.d_model, w.h * w.d_k), std, dt)
+        out["Wk"] = _normal(g, (w.d_model, w.h * w.d_k), std, dt)
+        out["Wv"] = _normal(g, (w.d_model, w.h * w.d_v), std, dt)
+        out["Wo"] = _normal(g, (w.h * w.d_v, w.d_model), std, dt)
+    if w.mask & MASK_KEY_PADDING:
+        lo, hi = w.key_len_range if w.key_len_range else (1, w.n_k)
+        out["key_lengths"] = torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int32)
+    else:
+        out["key_lengths"] = None
+    return out
+
+
+def to_f64(t):
+    """Exact upcast of a CPU tensor (bf16 or fp32) to a float64 numpy array."""
+    return t.detach().to("cpu").to(torch.float64).numpy()

@@ -1,0 +1,181 @@
+/*
+ * mha.h -- C ABI of libmha: multi-head scaled dot-product attention, forward,
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are web pages on the 2017 paper "Attention Is
+ * All You Need"; each entry point cites the passage that defines it):
+ *
+ *   Attention(Q, K, V) = softmax(Q K^T / sqrt(d_k) + M) V           per head
+ *   head_i   = Attention(X_q W_i^Q, X_kv W_i^K, X_kv W_i^V)
+ *   MultiHead = Concat(head_1, ..., head_h) W^O
+ *
+ * with M an additive 0 / -inf mask applied before the row softmax.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor arguments are DEVICE pointers to caller-owned, row-major,
+ *   densely packed memory, in the dtype given by `dtype`, except
+ *   `key_lengths`, which is a HOST pointer (read during the call only).
+ * - Math orientation is X.W as on the pages: W^Q, W^K are d_model x (h*d_k),
+ *   W^V is d_model x (h*d_v), W^O is (h*d_v) x d_model.  Holders of weights in
+ *   [out][in] layout pass the transpose.  There are no biases.
+ * - Head i owns the contiguous column block [i*d, (i+1)*d) of a stacked
+ *   projection and the row block [i*d_v, (i+1)*d_v) of W^O.
+ * - Accumulation is always fp32.  bf16 intermediates (Q, K, V, softmax
+ *   weights fed to the second product, the concatenated heads) are rounded
+ *   to nearest even.
+ * - Work is enqueued on `stream` and the call returns before it completes.
+ *   The library allocates nothing, keeps no pointer after returning and
+ *   holds no global state; calls on different streams may run concurrently
+ *   as long as their output buffers do not overlap.
+ * - Every argument check runs on the host before any HIP call; a failed
+ *   check returns a negative status and enqueues nothing.  MHA_ERR_HIP
+ *   reports a launch failure (hipGetLastError after the launches).  No C++
+ *   exception crosses this interface.
+ *
+ * Supported on the GPU in this version: d_k = d_v = 64 for attention;
+ * bf16 for every entry point; fp32 for sdpa_forward.  Other combinations
+ * return MHA_ERR_UNSUPPORTED.
+ */
+#ifndef MHA_H
+#define MHA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define MHA_OK                 0
+#define MHA_ERR_NULL          -1  /* a required pointer is NULL                    */
+#define MHA_ERR_DIM           -2  /* a size is <= 0, or an index would overflow    */
+#define MHA_ERR_MASK          -3  /* unknown mask kind, or causal with n_q != n_k  */
+#define MHA_ERR_KEYLEN        -4  /* key_lengths missing, or a length outside [1, n_k] */
+#define MHA_ERR_UNSUPPORTED   -5  /* head size / dtype / batch limit not supported */
+#define MHA_ERR_WORKSPACE     -6  /* workspace missing or smaller than required    */
+#define MHA_ERR_HIP           -7  /* a HIP launch failed                           */
+#define MHA_ERR_SCALE         -8  /* scale not finite or not > 0                   */
+
+/* Mask kinds (bit 0: causal, bit 1: key padding). */
+#define MHA_MASK_NONE              0
+#define MHA_MASK_CAUSAL            1  /* key j hidden from query i when j > i      */
+#define MHA_MASK_KEY_PADDING       2  /* key j hidden in batch b when j >= L_b     */
+#define MHA_MASK_CAUSAL_KEY_PADDING 3
+
+/* Element types. */
+#define MHA_DTYPE_BF16  0
+#define MHA_DTYPE_F32   1
+
+/* Largest batch accepted together with key padding (lengths travel as kernel
+ * arguments). */
+#define MHA_MAX_PADDED_BATCH 256
+
+/*
+ * sdpa_forward -- bare scaled dot-product attention for every (batch, head).
+ *
+ * Defines: softmax(Q K^T * scale + M) V, rows = queries, columns = keys,
+ * softmax along each row.  Sources: hex4c59.cc "读懂 Attention Is All You
+ * Need", sections "六步算完一行注意力", "把所有位置合并，就是那条核心公式" and
+ * "为什么要按键的维度缩放？"; devpress.csdn.net "【深度学习】Transformer",
+ * section 2.1, equation (2.4).  The mask is added before the softmax
+ * (hex4c59.cc, section "掩码必须在 softmax 之前生效"; devpress.csdn.net
+ * section 3.1 prints the causal pattern).
+ *
+ *   Q [B][h][n_q][d_k], K [B][h][n_k][d_k], V [B][h][n_k][d_v]  (inputs)
+ *   O [B][h][n_q][d_v]                                           (output)
+ *   scale       finite and > 0 (the method uses 1/sqrt(d_k))
+ *   mask_kind   MHA_MASK_*; causal needs n_q == n_k
+ *   key_lengths host int32[B], each in [1, n_k]; required iff the padding bit
+ *               is set (B <= MHA_MAX_PADDED_BATCH), ignored otherwise
+ *   dtype       MHA_DTYPE_BF16 or MHA_DTYPE_F32 (Q, K, V, O all of it)
+ *
+ * The n_q x n_k score matrix is never stored: one fused kernel streams K/V
+ * tiles and keeps a running row maximum and row sum (an exact reformulation
+ * of the row softmax).  O must not overlap Q, K or V.
+ */
+int sdpa_forward(const void* Q, const void* K, const void* V, void* O,
+                 int B, int h, int n_q, int n_k, int d_k, int d_v,
+                 float scale, int mask_kind, const int32_t* key_lengths,
+                 int dtype, hipStream_t stream);
+
+/*
+ * mha_workspace_bytes -- device scratch that mha_forward and the stage calls
+ * need for the projected heads and the concatenated attention output:
+ *   Q [B][h][n_q][d_k], K [B][h][n_k][d_k], V [B][h][n_k][d_v],
+ *   O concat [B][n_q][h*d_v], each 256-byte aligned, in the element type.
+ * Returns 0 for invalid sizes.
+ */
+size_t mha_workspace_bytes(int B, int n_q, int n_k, int h, int d_k, int d_v, int dtype);
+
+/*
+ * mha_forward -- the multi-head attention block, Concat(head_1..head_h) W^O.
+ *
+ * Sources: devpress.csdn.net "【深度学习】Transformer", section 2.2 (MultiHead
+ * formula and the shapes W_i^Q, W_i^K in R^{d x d_k}, W_i^V in R^{d x d_v},
+ * W^O in R^{h d_v x d}); hex4c59.cc, sections "Q、K、V 是三种计算角色" and
+ * "多头注意力让一次读取有多组投影".  The three uses of the block
+ * (hex4c59.cc, section "解码器有两种读取：看前缀，以及看源句"; wiki.hugogu.cn
+ * table of attention uses; devpress.csdn.net section 3.2):
+ *   encoder self-attention     X_kv == X_q, mask NONE
+ *   decoder masked self-attn   X_kv == X_q, mask CAUSAL
+ *   encoder-decoder (cross)    X_q from the decoder, X_kv from the encoder,
+ *                              n_q may differ from n_k, optional key padding
+ *
+ *   X_q [B][n_q][d_model], X_kv [B][n_k][d_model]  (X_kv may equal X_q)
+ *   Wq, Wk [d_model][h*d_k], Wv [d_model][h*d_v], Wo [h*d_v][d_model]
+ *   Y [B][n_q][d_model]                            (output)
+ *   scale is fixed at 1/sqrt(d_k).
+ *   workspace   device buffer of at least mha_workspace_bytes(...) bytes,
+ *               owned by the caller, not read before it is written.
+ *   dtype       MHA_DTYPE_BF16.
+ *
+ * When X_kv == X_q (same pointer) and n_q == n_k, the three input
+ * projections run as one GEMM over the stacked weights.  Y must not overlap
+ * any input or the workspace.
+ */
+int mha_forward(const void* X_q, const void* X_kv,
+                const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                void* Y,
+                int B, int n_q, int n_k, int d_model, int h, int d_k, int d_v,
+                int mask_kind, const int32_t* key_lengths, int dtype,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The three stages of mha_forward, callable on their own with the same
+ * arguments (each ignores what it does not use).  mha_forward is exactly
+ * mha_project_in; mha_attend; mha_project_out on one stream.  They share
+ * the workspace layout documented at mha_workspace_bytes.
+ *
+ * mha_project_in  -- Q = X_q W^Q, K = X_kv W^K, V = X_kv W^V, written per head
+ *                    into the workspace (devpress.csdn.net section 2.1,
+ *                    equations (2.1)-(2.3); hex4c59.cc section
+ *                    "Q、K、V 是三种计算角色").
+ * mha_attend      -- per-head attention of the workspace Q, K, V, written in
+ *                    concatenated layout [B][n_q][h*d_v] (the Concat of the
+ *                    MultiHead formula).
+ * mha_project_out -- Y = Concat . W^O.
+ */
+int mha_project_in(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
+                   const void* Wv,
+                   int B, int n_q, int n_k, int d_model, int h, int d_k, int d_v,
+                   int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int mha_attend(int B, int n_q, int n_k, int h, int d_k, int d_v,
+               int mask_kind, const int32_t* key_lengths, int dtype,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+int mha_project_out(const void* Wo, void* Y,
+                    int B, int n_q, int n_k, int d_model, int h, int d_k, int d_v,
+                    int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Text of a status code (static storage; never NULL). */
+const char* mha_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MHA_H */

@@ -1,0 +1,175 @@
+"""The C ABI on the CPU: libmha.so loads without a GPU, exports every symbol
+include/*.h declares, and rejects every invalid-argument class with its
+status code before any HIP call (the argument checks are host-only, so no
+call below reaches a kernel launch)."""
+
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import head_attention_forward_amd as hafa
+from head_attention_forward_amd import _binding as bnd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+OK, NULL, DIM, MASK, KEYLEN, UNSUP, WS, HIP, SCALE = 0, -1, -2, -3, -4, -5, -6, -7, -8
+BF16, F32 = 0, 1
+
+# Non-null, 256-byte aligned stand-ins; never dereferenced because every call
+# below fails a host-side check first.
+FAKE = ctypes.c_void_p(0x10000)
+FAKE2 = ctypes.c_void_p(0x20000)
+MISALIGNED = ctypes.c_void_p(0x10008)
+
+
+def declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        for m in re.finditer(r"^\s*(?:int|size_t|const char\s*\*)\s+(\w+)\s*\(", text, re.M):
+            names.add(m.group(1))
+    return names
+
+
+@pytest.fixture(scope="module")
+def L():
+    return bnd.lib()
+
+
+def test_library_exports_every_declared_symbol(L):
+    names = declared_symbols()
+    assert names >= {"sdpa_forward", "mha_forward", "mha_workspace_bytes", "mha_status_str",
+                     "mha_project_in", "mha_attend", "mha_project_out"}
+    for n in names:
+        assert hasattr(L, n), f"libmha.so does not export {n}"
+        assert n in bnd._SIG, f"binding has no signature for {n}"
+
+
+def test_status_strings(L):
+    for code in (OK, NULL, DIM, MASK, KEYLEN, UNSUP, WS, HIP, SCALE):
+        s = L.mha_status_str(code)
+        assert s and s != b"unknown status"
+    assert L.mha_status_str(12345) == b"unknown status"
+
+
+def test_workspace_bytes(L):
+    def up(x):
+        return (x + 255) // 256 * 256
+    B, n_q, n_k, h, d = 32, 96, 128, 16, 64
+    want = up(2 * B * h * n_q * d) + 2 * up(2 * B * h * n_k * d) + up(2 * B * n_q * h * d)
+    assert L.mha_workspace_bytes(B, n_q, n_k, h, d, d, BF16) == want
+    assert L.mha_workspace_bytes(0, n_q, n_k, h, d, d, BF16) == 0
+    assert L.mha_workspace_bytes(B, n_q, n_k, h, d, d, 7) == 0
+
+
+def sdpa(L, Q=FAKE, K=FAKE, V=FAKE, O=FAKE2, B=2, h=2, n_q=8, n_k=8, d_k=64, d_v=64, scale=0.125,
+         mask=0, kl=None, dtype=BF16):
+    return L.sdpa_forward(Q, K, V, O, B, h, n_q, n_k, d_k, d_v, scale, mask, kl, dtype, None)
+
+
+def keylens(*v):
+    arr = (ctypes.c_int32 * len(v))(*v)
+    return ctypes.cast(arr, ctypes.c_void_p), arr
+
+
+def test_sdpa_rejections(L):
+    assert sdpa(L, Q=None) == NULL
+    assert sdpa(L, O=None) == NULL
+    assert sdpa(L, B=0) == DIM
+    assert sdpa(L, n_k=-1) == DIM
+    assert sdpa(L, h=1 << 20, B=1 << 12) == DIM
+    assert sdpa(L, d_k=32) == UNSUP
+    assert sdpa(L, d_v=128) == UNSUP
+    assert sdpa(L, scale=0.0) == SCALE
+    assert sdpa(L, scale=float("nan")) == SCALE
+    assert sdpa(L, scale=float("inf")) == SCALE
+    assert sdpa(L, mask=4) == MASK
+    assert sdpa(L, mask=-1) == MASK
+    assert sdpa(L, mask=1, n_q=8, n_k=9) == MASK      # causal needs n_q == n_k
+    assert sdpa(L, mask=2) == KEYLEN                   # lengths missing
+    p, keep = keylens(8, 0)
+    assert sdpa(L, mask=2, kl=p) == KEYLEN             # length 0
+    p, keep = keylens(9, 3)
+    assert sdpa(L, mask=2, kl=p) == KEYLEN             # length > n_k
+    p, keep = keylens(*([4] * 300))
+    assert sdpa(L, mask=2, kl=p, B=300, h=1) == UNSUP  # batch above the padded limit
+    assert sdpa(L, dtype=5) == UNSUP
+    assert sdpa(L, Q=MISALIGNED) == UNSUP
+
+
+def mha(L, X_q=FAKE, X_kv=FAKE, W=FAKE, Y=FAKE2, B=2, n_q=8, n_k=8, d_model=64, h=2, d_k=64,
+        d_v=64, mask=0, kl=None, dtype=BF16, ws=FAKE, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.mha_workspace_bytes(B, n_q, n_k, h, d_k, d_v, BF16) if B > 0 else 0
+    return L.mha_forward(X_q, X_kv, W, W, W, W, Y, B, n_q, n_k, d_model, h, d_k, d_v, mask, kl,
+                         dtype, ws, ws_bytes, None)
+
+
+def test_mha_rejections(L):
+    assert mha(L, X_q=None) == NULL
+    assert mha(L, Y=None) == NULL
+    assert mha(L, W=None) == NULL
+    assert mha(L, B=0) == DIM
+    assert mha(L, d_model=0) == DIM
+    assert mha(L, d_k=16) == UNSUP
+    assert mha(L, dtype=F32) == UNSUP
+    assert mha(L, d_model=60) == UNSUP                  # rows not 16-byte multiples
+    assert mha(L, ws=None) == WS
+    assert mha(L, ws=ctypes.c_void_p(0x10010)) == WS   # workspace not 256-byte aligned
+    assert mha(L, ws_bytes=1024) == WS
+    assert mha(L, mask=1, n_q=8, n_k=12) == MASK
+    assert mha(L, mask=7) == MASK
+    assert mha(L, mask=2) == KEYLEN
+    p, keep = keylens(3, 13)
+    assert mha(L, mask=2, n_k=12, kl=p) == KEYLEN
+    assert mha(L, Y=MISALIGNED) == UNSUP
+
+
+def test_stage_rejections(L):
+    ws = L.mha_workspace_bytes(2, 8, 8, 2, 64, 64, BF16)
+    assert L.mha_project_in(None, FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 64, 2, 64, 64, BF16, FAKE, ws,
+                            None) == NULL
+    assert L.mha_project_in(FAKE, FAKE, FAKE, FAKE, FAKE, 2, 8, 8, 64, 2, 64, 64, BF16, FAKE, 10,
+                            None) == WS
+    assert L.mha_attend(2, 8, 8, 2, 64, 64, 3, None, BF16, FAKE, ws, None) == KEYLEN
+    ws9 = L.mha_workspace_bytes(2, 8, 9, 2, 64, 64, BF16)
+    assert L.mha_attend(2, 8, 9, 2, 64, 64, 1, None, BF16, FAKE, ws9, None) == MASK
+    assert L.mha_project_out(FAKE, None, 2, 8, 8, 64, 2, 64, 64, BF16, FAKE, ws, None) == NULL
+    assert L.mha_project_out(FAKE, FAKE2, 2, 8, 8, 64, 2, 64, 64, F32, FAKE, ws, None) == UNSUP
+
+
+def test_binding_refuses_host_tensors():
+    import torch
+    x = torch.zeros(1, 1, 4, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU memory"):
+        hafa.sdpa_forward(x, x, x)
+
+
+def test_workloads_match_the_stated_shapes():
+    W = hafa.WORKLOADS
+    assert (W["sdpa_f32_tiny"].B, W["sdpa_f32_tiny"].n_q, W["sdpa_f32_tiny"].dtype) == (1, 64, "f32")
+    w = W["encoder_self_base"]
+    assert (w.B, w.n_q, w.d_model, w.h, w.d_k, w.mask) == (32, 100, 512, 8, 64, 0)
+    w = W["decoder_causal_base"]
+    assert (w.B, w.n_q, w.d_model, w.h, w.mask) == (16, 512, 512, 8, 1)
+    w = W["cross_padded_big"]
+    assert (w.B, w.n_q, w.n_k, w.d_model, w.h, w.mask, w.key_len_range) == \
+        (32, 96, 128, 1024, 16, 2, (64, 128))
+    w = W["long_causal_sdpa"]
+    assert (w.B, w.h, w.n_q, w.d_k, w.mask, w.dtype) == (4, 16, 4096, 64, 1, "bf16")
+
+
+def test_generator_is_seeded_and_ordered():
+    w = hafa.WORKLOADS["cross_padded_big"].replace(B=3, n_q=5, n_k=7, d_model=16, h=2,
+                                                    key_len_range=(2, 7))
+    a = hafa.generate(w, seed=0)
+    b = hafa.generate(w, seed=0)
+    for k in ("X_q", "X_kv", "Wq", "Wk", "Wv", "Wo", "key_lengths"):
+        assert a[k].equal(b[k])
+    assert a["X_q"].dtype.is_floating_point and str(a["X_q"].dtype) == "torch.bfloat16"
+    assert int(a["key_lengths"].min()) >= 2 and int(a["key_lengths"].max()) <= 7
+    s = hafa.generate(hafa.WORKLOADS["encoder_self_base"].replace(B=2, n_q=3, n_k=3), seed=0)
+    assert s["X_kv"] is s["X_q"]

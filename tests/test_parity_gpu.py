@@ -1,0 +1,277 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances: fp32 inputs max-abs <= 1e-5; bf16 inputs (fp32 accumulation)
+max-abs <= 2e-2 and relative L2 <= 5e-3, with identical masking patterns
+(masked keys get weight exactly 0 on both sides; checked directly by the
+perturbation tests, which must be bit-exact).
+
+Each GPU step prints the case it runs (flushed) before launching it."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import head_attention_forward_amd as hafa
+from head_attention_forward_amd.workloads import WORKLOADS, generate, to_f64
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS = 2e-2
+BF16_REL_L2 = 5e-3
+F32_MAX_ABS = 1e-5
+
+
+def announce(*what):
+    print("[gpu case]", *what, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a ROCm GPU")
+    return torch.device("cuda")
+
+
+def assert_bf16_close(got, want, what=""):
+    g = to_f64(got)
+    assert g.shape == want.shape, (g.shape, want.shape)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite output"
+    err = g - want
+    max_abs = float(np.abs(err).max())
+    rel = float(np.linalg.norm(err) / max(np.linalg.norm(want), 1e-300))
+    print(f"  {what}: max_abs={max_abs:.3e} rel_l2={rel:.3e}", flush=True)
+    assert max_abs <= BF16_MAX_ABS, f"{what}: max-abs {max_abs}"
+    assert rel <= BF16_REL_L2, f"{what}: rel-L2 {rel}"
+
+
+def assert_f32_close(got, want, what=""):
+    g = to_f64(got)
+    assert np.all(np.isfinite(g))
+    max_abs = float(np.abs(g - want).max())
+    print(f"  {what}: max_abs={max_abs:.3e}", flush=True)
+    assert max_abs <= F32_MAX_ABS, f"{what}: max-abs {max_abs}"
+
+
+def sdpa_inputs(B, h, n_q, n_k, dtype, seed, q_scale=1.0):
+    g = torch.Generator("cpu")
+    g.manual_seed(seed)
+    Q = (torch.randn((B, h, n_q, 64), generator=g) * q_scale).to(dtype)
+    K = torch.randn((B, h, n_k, 64), generator=g).to(dtype)
+    V = torch.randn((B, h, n_k, 64), generator=g).to(dtype)
+    return Q, K, V
+
+
+def run_sdpa(dev, Q, K, V, scale, mask, kl):
+    return hafa.sdpa_forward(Q.to(dev), K.to(dev), V.to(dev), scale, mask, kl)
+
+
+def ref_sdpa(Q, K, V, scale, mask, kl):
+    return oracle.sdpa_ref(to_f64(Q), to_f64(K), to_f64(V), scale, mask,
+                           None if kl is None else np.asarray(kl))
+
+
+# ------------------------------------------------------------------ the five workloads
+
+def test_sdpa_f32_tiny(dev):
+    w = WORKLOADS["sdpa_f32_tiny"]
+    x = generate(w, seed=0)
+    announce("sdpa_forward f32", w.description)
+    O = run_sdpa(dev, x["Q"], x["K"], x["V"], x["scale"], w.mask, None)
+    torch.cuda.synchronize()
+    assert_f32_close(O, ref_sdpa(x["Q"], x["K"], x["V"], x["scale"], w.mask, None), w.name)
+
+
+def _mha_case(dev, w, seed=0):
+    x = generate(w, seed=seed)
+    Xq = x["X_q"].to(dev)
+    Xkv = Xq if w.self_attn else x["X_kv"].to(dev)
+    Ws = [x[k].to(dev) for k in ("Wq", "Wk", "Wv", "Wo")]
+    kl = x["key_lengths"]
+    announce("mha_forward bf16", w.description, "seed", seed)
+    Y = hafa.mha_forward(Xq, Xkv, *Ws, w.h, w.mask, kl)
+    torch.cuda.synchronize()
+    want, inter = oracle.mha_ref(to_f64(x["X_q"]), to_f64(x["X_kv"]),
+                                 *[to_f64(x[k]) for k in ("Wq", "Wk", "Wv", "Wo")], w.h, w.mask,
+                                 None if kl is None else kl.numpy(), return_intermediates=True)
+    assert_bf16_close(Y, want, w.name)
+    return x, Xq, Xkv, Ws, kl, Y, inter
+
+
+@pytest.mark.parametrize("name", ["encoder_self_base", "decoder_causal_base", "cross_padded_big"])
+def test_mha_workloads(dev, name):
+    _mha_case(dev, WORKLOADS[name])
+
+
+def test_mha_stages_equal_forward_and_intermediates(dev):
+    """The three stage calls reproduce mha_forward bit for bit, and the
+    workspace intermediates match the oracle's projections and concat."""
+    w = WORKLOADS["cross_padded_big"]
+    x, Xq, Xkv, Ws, kl, Y, inter = _mha_case(dev, w)
+    ws = hafa.alloc_workspace(w.B, w.n_q, w.n_k, w.h, w.d_k, w.d_v, dev)
+    announce("mha stages", w.name)
+    hafa.mha_project_in(Xq, Xkv, Ws[0], Ws[1], Ws[2], w.h, ws)
+    hafa.mha_attend(w.B, w.n_q, w.n_k, w.h, w.d_k, w.d_v, ws, w.mask, kl)
+    Y2 = torch.empty_like(Y)
+    hafa.mha_project_out(Ws[3], Y2, w.B, w.n_q, w.n_k, w.h, w.d_k, w.d_v, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+    q, k, v, o = hafa.workspace_views(ws, w.B, w.n_q, w.n_k, w.h, w.d_k, w.d_v)
+    assert_bf16_close(q, inter["Q"], "Q projection")
+    assert_bf16_close(k, inter["K"], "K projection")
+    assert_bf16_close(v, inter["V"], "V projection")
+    assert_bf16_close(o, inter["concat"], "concatenated heads")
+
+
+def test_sdpa_long_causal_sampled(dev):
+    """Full size, in the launch configuration the bench times; the oracle
+    evaluates sampled rows one by one (every boundary row included)."""
+    w = WORKLOADS["long_causal_sdpa"]
+    x = generate(w, seed=0)
+    announce("sdpa_forward bf16", w.description)
+    O = run_sdpa(dev, x["Q"], x["K"], x["V"], x["scale"], w.mask, None)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    special = [0, 1, 31, 32, 63, 64, 127, 128, 129, 255, 256, 2047, 2048, 4094, 4095]
+    idx = [(b, hh, q) for b in range(w.B) for hh in (0, w.h - 1) for q in special]
+    idx += [(int(rng.integers(w.B)), int(rng.integers(w.h)), int(rng.integers(w.n_q)))
+            for _ in range(400)]
+    idx = np.array(idx)
+    want = oracle.sdpa_ref_rows(to_f64(x["Q"]), to_f64(x["K"]), to_f64(x["V"]), x["scale"],
+                                w.mask, None, idx)
+    got = O[idx[:, 0], idx[:, 1], idx[:, 2]]
+    assert_bf16_close(got, want, w.name + " sampled rows")
+    # Causal row 0 sees only key 0: exactly value row 0.
+    assert torch.equal(O[:, :, 0].cpu(), x["V"][:, :, 0])
+    # Every output row is a convex combination of V rows: coordinates within the
+    # per-(batch, head) range of V (checked on the whole output).
+    Vd = x["V"].to(dev).float()
+    lo = Vd.amin(dim=2, keepdim=True)
+    hi = Vd.amax(dim=2, keepdim=True)
+    Of = O.float()
+    assert bool(((Of >= lo - 1e-2) & (Of <= hi + 1e-2)).all())
+
+
+# ------------------------------------------------------------------ edge shapes
+
+EDGE = [
+    # (B, h, n_q, n_k, mask, key_lengths)
+    (1, 1, 1, 1, 0, None),
+    (1, 1, 1, 300, 0, None),          # single query, many keys
+    (2, 3, 63, 63, 1, None),
+    (1, 2, 64, 64, 1, None),
+    (2, 1, 65, 65, 1, None),
+    (3, 2, 100, 100, 0, None),
+    (1, 1, 127, 127, 1, None),
+    (2, 2, 128, 128, 0, None),
+    (1, 3, 129, 129, 1, None),
+    (2, 2, 200, 77, 0, None),         # n_q != n_k, ragged keys
+    (2, 2, 33, 250, 0, None),
+    (4, 2, 96, 128, 2, [1, 64, 127, 128]),
+    (3, 1, 130, 130, 3, [1, 65, 130]),
+    (2, 2, 257, 257, 3, [200, 257]),
+]
+
+
+@pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", EDGE)
+def test_sdpa_bf16_edges(dev, B, h, n_q, n_k, mask, kl):
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.bfloat16, seed=n_q * 1000 + n_k)
+    announce("sdpa_forward bf16 edge", dict(B=B, h=h, n_q=n_q, n_k=n_k, mask=mask, kl=kl))
+    O = run_sdpa(dev, Q, K, V, 0.125, mask, kl)
+    torch.cuda.synchronize()
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"edge {B}x{h}x{n_q}x{n_k} m{mask}")
+
+
+@pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", [(1, 1, 1, 1, 0, None), (2, 2, 100, 100, 1, None),
+                                                 (2, 1, 70, 129, 2, [5, 129]),
+                                                 (1, 2, 200, 200, 3, [150])])
+def test_sdpa_f32_edges(dev, B, h, n_q, n_k, mask, kl):
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.float32, seed=7 + n_q)
+    announce("sdpa_forward f32 edge", dict(B=B, h=h, n_q=n_q, n_k=n_k, mask=mask, kl=kl))
+    O = run_sdpa(dev, Q, K, V, 0.125, mask, kl)
+    torch.cuda.synchronize()
+    assert_f32_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"f32 edge {n_q}x{n_k} m{mask}")
+
+
+def test_saturated_and_uniform(dev):
+    """Large-magnitude scores (softmax saturation) stay finite and accurate;
+    Q = 0 gives uniform weights: outputs are means of the visible V rows."""
+    Q, K, V = sdpa_inputs(2, 2, 150, 150, torch.bfloat16, seed=3, q_scale=30.0)
+    announce("sdpa saturated")
+    O = run_sdpa(dev, Q, K, V, 0.125, 1, None)
+    torch.cuda.synchronize()
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, 1, None), "saturated causal")
+    Z = torch.zeros_like(Q)
+    announce("sdpa zero queries")
+    for mask, kl in ((0, None), (1, None), (2, [7, 150])):
+        O = run_sdpa(dev, Z, K, V, 0.125, mask, kl)
+        torch.cuda.synchronize()
+        Vd = to_f64(V)
+        want = np.empty(O.shape)
+        for b in range(2):
+            for q in range(150):
+                n_vis = q + 1 if mask == 1 else (kl[b] if mask == 2 else 150)
+                want[b, :, q] = Vd[b, :, :n_vis].mean(axis=1)
+        assert_bf16_close(O, want, f"zero Q mask {mask}")
+
+
+def test_masked_keys_have_exactly_zero_weight(dev):
+    """Changing keys/values a query may not see leaves its output bit-exact:
+    future rows under the causal mask, padded rows under key padding."""
+    B, h, n = 2, 2, 200
+    Q, K, V = sdpa_inputs(B, h, n, n, torch.bfloat16, seed=11)
+    announce("causal perturbation")
+    O = run_sdpa(dev, Q, K, V, 0.125, 1, None).cpu()
+    for i in (0, 63, 64, 130, 198):
+        K2, V2 = K.clone(), V.clone()
+        K2[:, :, i + 1:] = K2[:, :, i + 1:] * -7
+        V2[:, :, i + 1:] = V2[:, :, i + 1:] * 5 + 3
+        O2 = run_sdpa(dev, Q, K2, V2, 0.125, 1, None).cpu()
+        assert torch.equal(O2[:, :, : i + 1], O[:, :, : i + 1]), i
+    announce("padding perturbation")
+    kl = [37, 129]
+    O = run_sdpa(dev, Q, K, V, 0.125, 2, kl).cpu()
+    K2, V2 = K.clone(), V.clone()
+    for b, L in enumerate(kl):
+        K2[b, :, L:] = 50.0
+        V2[b, :, L:] = -80.0
+    O2 = run_sdpa(dev, Q, K2, V2, 0.125, 2, kl).cpu()
+    assert torch.equal(O, O2)
+
+
+def test_deterministic_and_in_bounds(dev):
+    """Two runs agree bit for bit, and nothing is written past the output
+    (canary bytes around the output stay intact)."""
+    B, h, n_q, n_k = 3, 2, 131, 131
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.bfloat16, seed=5)
+    Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
+    numel = B * h * n_q * 64
+    pad = 4096
+    buf = torch.full((numel + 2 * pad,), -12345.0, dtype=torch.bfloat16, device=dev)
+    out = buf[pad:pad + numel].view(B, h, n_q, 64)
+    announce("determinism + canary")
+    hafa.sdpa_forward(Qd, Kd, Vd, 0.125, 3, [131, 17, 64], out=out)
+    first = out.clone()
+    hafa.sdpa_forward(Qd, Kd, Vd, 0.125, 3, [131, 17, 64], out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out)
+    assert bool((buf[:pad] == -12345.0).all()) and bool((buf[pad + numel:] == -12345.0).all())
+
+
+def test_mha_small_shapes(dev):
+    """The whole block on small odd shapes: h = 1, odd batch, ragged rows,
+    cross-attention without padding, padding with causal self-attention."""
+    cases = [
+        dict(B=1, n_q=1, n_k=1, d_model=64, h=1, mask=0, self_attn=True),
+        dict(B=3, n_q=37, n_k=37, d_model=128, h=2, mask=1, self_attn=True),
+        dict(B=2, n_q=50, n_k=130, d_model=192, h=3, mask=0, self_attn=False),
+        dict(B=2, n_q=70, n_k=70, d_model=256, h=4, mask=3, self_attn=True, key_len_range=(1, 70)),
+    ]
+    for c in cases:
+        w = WORKLOADS["cross_padded_big"].replace(
+            name="small", B=c["B"], n_q=c["n_q"], n_k=c["n_k"], d_model=c["d_model"], h=c["h"],
+            mask=c["mask"], self_attn=c["self_attn"], key_len_range=c.get("key_len_range"),
+            description=str(c))
+        _mha_case(dev, w, seed=1)
