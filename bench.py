@@ -1,0 +1,479 @@
+"""Benchmark of the multi-head attention forward hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one pass of the whole path over one batch: for a multi-head block
+the input projection(s), the fused attention and the output projection; for
+bare attention the fused attention kernel.  Inputs are seeded synthetic
+tensors of the workload's shapes, resident in GPU memory before timing, and
+rotated through enough buffer sets that every step reads memory no earlier
+step left in the 256 MB Infinity Cache.
+
+Prints one JSON line: the metric (attention forward TFLOP/s counted as
+4*B*h*n_q*n_k*d_k per step, and its fraction of the bf16 MFMA peak), the
+per-kernel durations (HIP launch events recorded by the library around each
+kernel of each timed step), the roofline of the dominant kernel, and the
+fp64 CPU oracle timed on a bounded sample of the same workload on the host.
+"""
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (4·B·h·n_q·n_k·d_k) + % of bf16 MFMA peak"
+PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk (dense bf16 MFMA)
+PEAK_FP32_TFLOPS = 157.3       # fp32 vector
+PEAK_HBM_GBS = 8000.0          # HBM3E
+MALL_BYTES = 256 << 20
+DEFAULT_WORKLOAD = "encoder_self_base"
+
+
+def parse_args():
+    p = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--sets", type=int, default=0, help="buffer sets to rotate (0 = auto)")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target length of the CPU oracle sample")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-parity", action="store_true")
+    p.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    p.add_argument("--copy-calibration-mib", type=int, default=0,
+                   help="also run a plain device copy of this many MiB (counter calibration)")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------------------- accounting
+
+def kernel_plan(w):
+    """Launch order of one step with each kernel's algorithmic flops and bytes
+    (bytes: every input element read once, every output written once)."""
+    e = 2 if w.dtype == "bf16" else 4
+    B, h, nq, nk, dk, dv = w.B, w.h, w.n_q, w.n_k, w.d_k, w.d_v
+    # visible (query, key) pairs per (batch, head)
+    if w.mask & 1:
+        pairs_bh = [nq * (nq + 1) / 2.0] * B
+    elif w.mask & 2:
+        pairs_bh = None
+    else:
+        pairs_bh = [float(nq * nk)] * B
+    plan = []
+
+    def gemm(name, M, K, N):
+        plan.append(dict(name=name, flops=2.0 * M * K * N, bytes=float(e * (M * K + K * N + M * N)),
+                         peak_kind="mfma"))
+
+    if w.kind == "mha":
+        if w.self_attn:
+            gemm("qkv_projection_gemm", B * nq, w.d_model, h * (2 * dk + dv))
+        else:
+            gemm("q_projection_gemm", B * nq, w.d_model, h * dk)
+            gemm("kv_projection_gemm", B * nk, w.d_model, h * (dk + dv))
+    plan.append(dict(name="attention", flops=None, bytes=None,
+                     peak_kind="mfma" if w.dtype == "bf16" else "fp32"))
+    if w.kind == "mha":
+        gemm("output_projection_gemm", B * nq, h * dv, w.d_model)
+    return plan, pairs_bh
+
+
+def attention_accounting(w, key_lengths):
+    """Algorithmic flops (visible pairs x 2(d_k + d_v)) and bytes (read Q,
+    the K/V rows some query can see, write O) of one attention launch."""
+    e = 2 if w.dtype == "bf16" else 4
+    B, h, nq, nk, dk, dv = w.B, w.h, w.n_q, w.n_k, w.d_k, w.d_v
+    if w.mask & 2:
+        L = [int(x) for x in key_lengths]
+    else:
+        L = [nk] * B
+    pairs = 0.0
+    kv_rows = 0
+    for b in range(B):
+        if w.mask & 1:
+            Lb = L[b]
+            # query i sees min(i + 1, L_b) keys
+            full = min(Lb, nq)
+            pairs += full * (full + 1) / 2.0 + max(0, nq - full) * Lb
+        else:
+            pairs += nq * L[b]
+        kv_rows += L[b]
+    flops = 2.0 * pairs * (dk + dv) * h
+    bytes_ = e * h * (B * nq * dk + kv_rows * (dk + dv) + B * nq * dv)
+    return flops, float(bytes_)
+
+
+# ----------------------------------------------------------------------------- steps
+
+class Step:
+    """Pre-marshalled launches of one workload over rotating buffer sets."""
+
+    def __init__(self, w, x, dev, sets):
+        import torch
+        from head_attention_forward_amd import _binding as bnd
+        self.w = w
+        self.lib = bnd.lib()
+        self.sets = []
+        self.keep = []
+        kl = x["key_lengths"]
+        if kl is not None:
+            self.kl_arr = (ctypes.c_int32 * w.B)(*[int(v) for v in kl])
+            self.kl = ctypes.cast(self.kl_arr, ctypes.c_void_p)
+        else:
+            self.kl = None
+        P = ctypes.c_void_p
+        for _ in range(sets):
+            if w.kind == "sdpa":
+                Q, K, V = (x[k].to(dev) for k in ("Q", "K", "V"))
+                O = torch.empty((w.B, w.h, w.n_q, w.d_v), dtype=Q.dtype, device=dev)
+                self.keep.append((Q, K, V, O))
+                code = bnd.DTYPE_BF16 if w.dtype == "bf16" else bnd.DTYPE_F32
+                self.sets.append((P(Q.data_ptr()), P(K.data_ptr()), P(V.data_ptr()), P(O.data_ptr()),
+                                  w.B, w.h, w.n_q, w.n_k, w.d_k, w.d_v, float(x["scale"]), w.mask,
+                                  self.kl, code))
+            else:
+                Xq = x["X_q"].to(dev)
+                Xkv = Xq if w.self_attn else x["X_kv"].to(dev)
+                Ws = [x[k].to(dev) for k in ("Wq", "Wk", "Wv", "Wo")]
+                Y = torch.empty((w.B, w.n_q, w.d_model), dtype=Xq.dtype, device=dev)
+                ws = bnd.alloc_workspace(w.B, w.n_q, w.n_k, w.h, w.d_k, w.d_v, dev)
+                self.keep.append((Xq, Xkv, Ws, Y, ws))
+                self.sets.append((P(Xq.data_ptr()), P(Xkv.data_ptr()),
+                                  *[P(t.data_ptr()) for t in Ws], P(Y.data_ptr()),
+                                  w.B, w.n_q, w.n_k, w.d_model, w.h, w.d_k, w.d_v, w.mask, self.kl,
+                                  bnd.DTYPE_BF16, P(ws.data_ptr()), ws.numel()))
+        self.n_launches = 1 if w.kind == "sdpa" else (3 if w.self_attn else 4)
+
+    def output(self, i):
+        return self.keep[i][3]
+
+    def run(self, i, stream):
+        f = self.lib.sdpa_forward if self.w.kind == "sdpa" else self.lib.mha_forward
+        st = f(*self.sets[i], stream)
+        if st != 0:
+            raise RuntimeError(f"launch failed with status {st}")
+
+    def run_timed(self, i, stream, events_ptr, cap):
+        f = self.lib.sdpa_forward_timed if self.w.kind == "sdpa" else self.lib.mha_forward_timed
+        n = ctypes.c_int()
+        st = f(*self.sets[i], stream, events_ptr, cap, ctypes.byref(n))
+        if st != 0 or n.value != self.n_launches:
+            raise RuntimeError(f"timed launch failed with status {st} ({n.value} launches)")
+
+
+def set_bytes(w):
+    e = 2 if w.dtype == "bf16" else 4
+    if w.kind == "sdpa":
+        return e * w.B * w.h * (w.n_q * (w.d_k + w.d_v) + w.n_k * (w.d_k + w.d_v))
+    xs = w.B * w.n_q * w.d_model * (1 if w.self_attn else 1) + (0 if w.self_attn else w.B * w.n_k * w.d_model)
+    ws = w.B * w.h * (w.n_q * w.d_k + w.n_k * (w.d_k + w.d_v) + w.n_q * w.d_v)
+    weights = w.d_model * w.h * (2 * w.d_k + w.d_v) + w.h * w.d_v * w.d_model
+    return e * (xs + ws + weights + w.B * w.n_q * w.d_model)
+
+
+# ----------------------------------------------------------------------------- parity
+
+def parity_check(w, x, out):
+    """One step's output against the fp64 oracle (sampled rows for shapes too
+    large to evaluate whole)."""
+    import numpy as np
+    import oracle
+    from head_attention_forward_amd.workloads import to_f64
+    kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
+    rows = "all"
+    if w.kind == "mha":
+        want = oracle.mha_ref(to_f64(x["X_q"]), to_f64(x["X_kv"]),
+                              *[to_f64(x[k]) for k in ("Wq", "Wk", "Wv", "Wo")], w.h, w.mask, kl)
+        got = to_f64(out)
+    elif w.B * w.h * w.n_q * w.n_k <= (1 << 24):
+        want = oracle.sdpa_ref(to_f64(x["Q"]), to_f64(x["K"]), to_f64(x["V"]), x["scale"], w.mask, kl)
+        got = to_f64(out)
+    else:
+        rng = np.random.default_rng(1)
+        idx = np.stack([rng.integers(0, w.B, 256), rng.integers(0, w.h, 256),
+                        rng.integers(0, w.n_q, 256)], axis=1)
+        idx[0] = (0, 0, w.n_q - 1)
+        rows = "256 sampled"
+        want = oracle.sdpa_ref_rows(to_f64(x["Q"]), to_f64(x["K"]), to_f64(x["V"]), x["scale"],
+                                    w.mask, kl, idx)
+        got = to_f64(out[idx[:, 0], idx[:, 1], idx[:, 2]])
+    err = got - want
+    max_abs = float(np.abs(err).max())
+    rel = float(np.linalg.norm(err) / np.linalg.norm(want))
+    if w.dtype == "bf16":
+        ok = max_abs <= 2e-2 and rel <= 5e-3
+    else:
+        ok = max_abs <= 1e-5
+    return dict(max_abs=max_abs, rel_l2=rel, ok=bool(ok), rows=rows)
+
+
+# ----------------------------------------------------------------------------- cpu baseline
+
+def cpu_baseline(w, x, target_s):
+    """The oracle, as it is, on a bounded sample of the workload: the first
+    b batches (multi-head block) or the first heads of batch 0 (bare
+    attention), sized to roughly target_s seconds."""
+    import numpy as np
+    import oracle
+    from head_attention_forward_amd.workloads import to_f64
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
+
+    if w.kind == "mha":
+        Xq, Xkv = to_f64(x["X_q"]), to_f64(x["X_kv"])
+        Ws = [to_f64(x[k]) for k in ("Wq", "Wk", "Wv", "Wo")]
+
+        def run(b):
+            t0 = time.perf_counter()
+            oracle.mha_ref(Xq[:b], Xkv[:b], *Ws, w.h, w.mask, None if kl is None else kl[:b])
+            return time.perf_counter() - t0
+        t1 = run(1)
+        b = int(max(1, min(w.B, target_s / max(t1, 1e-6))))
+        t = run(b)
+        flops = 4.0 * b * w.h * w.n_q * w.n_k * w.d_k
+        sample = f"multi-head block on the first {b} of {w.B} sequences"
+    else:
+        Q, K, V = to_f64(x["Q"][:1]), to_f64(x["K"][:1]), to_f64(x["V"][:1])
+
+        def run(nh):
+            t0 = time.perf_counter()
+            oracle.sdpa_ref(Q[:, :nh], K[:, :nh], V[:, :nh], x["scale"], w.mask,
+                            None if kl is None else kl[:1])
+            return time.perf_counter() - t0
+        t1 = run(1)
+        nh = int(max(1, min(w.h, target_s / max(t1, 1e-6))))
+        t = run(nh)
+        flops = 4.0 * nh * w.n_q * w.n_k * w.d_k
+        sample = f"{nh} of {w.B * w.h} (batch, head) pairs"
+    return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=sample + f"; {t:.2f} s, numpy float64", seconds=round(t, 3))
+
+
+# ----------------------------------------------------------------------------- traffic
+
+def kernel_source_sha():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "head_attention_forward_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload, kernel):
+    """HBM bytes per launch from the committed counter summary, if it was
+    taken on the current kernel sources; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except Exception:
+        return None
+    if rec.get("kernel_source_sha") != kernel_source_sha():
+        return None
+    ent = rec.get("entries", {}).get(f"{workload}/{kernel}")
+    return None if ent is None else float(ent["bytes_per_launch"])
+
+
+# ----------------------------------------------------------------------------- main
+
+def main():
+    args = parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by (batch, head) with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from head_attention_forward_amd import _hip
+    from head_attention_forward_amd.workloads import WORKLOADS, generate
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.workload not in WORKLOADS:
+        print(f"unknown workload {args.workload}; choose from {sorted(WORKLOADS)}", file=sys.stderr)
+        sys.exit(2)
+    w = WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    log = lambda *a: print("[bench]", *a, file=sys.stderr, flush=True)  # noqa: E731
+
+    x = generate(w, seed=args.seed)
+    sets = args.sets or max(2, min(64, math.ceil(2 * MALL_BYTES / set_bytes(w))))
+    log(f"workload {w.name}: {w.description}; {sets} buffer sets of {set_bytes(w) / 2**20:.1f} MiB")
+    step = Step(w, x, dev, sets)
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    parity = None
+    if not args.no_parity:
+        step.run(0, sp)
+        torch.cuda.synchronize()
+        parity = parity_check(w, x, step.output(0))
+        log(f"parity vs oracle: {parity}")
+        if not parity["ok"]:
+            print(json.dumps(dict(metric=METRIC, value=None, error="parity failed", parity=parity)))
+            sys.exit(1)
+
+    for i in range(args.warmup):
+        step.run(i % sets, sp)
+    torch.cuda.synchronize()
+    K = args.steps
+
+    # Timed region for the metric: K steps of plain launches, replayed from a
+    # captured HIP graph when capture works (launch overhead off the host),
+    # otherwise issued eagerly.
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record(stream)
+    for k in range(K):
+        step.run(k % sets, sp)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_eager = t_start.elapsed_time(t_end) / K
+    ref_out = step.output(0).clone()
+
+    ms_graph = None
+    graph_note = None
+    if not args.no_graph:
+        try:
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                cs = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+                for k in range(K):
+                    step.run(k % sets, cs)
+            for rep in range(3):
+                step.output(0).zero_()
+                torch.cuda.synchronize()
+                graph.replay()
+                torch.cuda.synchronize()
+                if not torch.equal(step.output(0), ref_out):
+                    raise RuntimeError(f"graph replay {rep} differs from the eager result")
+            t_start.record(stream)
+            graph.replay()
+            t_end.record(stream)
+            torch.cuda.synchronize()
+            ms_graph = t_start.elapsed_time(t_end) / K
+            del graph
+        except Exception as ex:  # capture unsupported: keep the eager figure
+            graph_note = f"graph capture not used: {ex}"
+            log(graph_note)
+    ms_step = ms_graph if ms_graph is not None else ms_eager
+
+    # Per-kernel durations: K more steps through the instrumented entry point,
+    # whose launch events bracket each kernel's own execution.
+    nl = step.n_launches
+    pool = _hip.EventPool(2 * nl * K)
+    for k in range(K):
+        step.run_timed(k % sets, sp, pool.ptr(2 * nl * k), 2 * nl)
+    torch.cuda.synchronize()
+
+    plan, _ = kernel_plan(w)
+    a_flops, a_bytes = attention_accounting(w, x["key_lengths"])
+    kernels = []
+    for j, kp in enumerate(plan):
+        durs = [pool.elapsed_ms(2 * (nl * k + j), 2 * (nl * k + j) + 1) for k in range(K)]
+        avg_us = 1e3 * float(np.mean(durs))
+        flops = a_flops if kp["name"] == "attention" else kp["flops"]
+        byts = a_bytes if kp["name"] == "attention" else kp["bytes"]
+        kernels.append(dict(name=kp["name"], avg_us=round(avg_us, 3),
+                            min_us=round(1e3 * float(np.min(durs)), 3),
+                            tflops=round(flops / (avg_us * 1e-6) / 1e12, 2),
+                            gbs=round(byts / (avg_us * 1e-6) / 1e9, 1),
+                            flops=flops, bytes=byts, peak_kind=kp["peak_kind"]))
+    pool.close()
+    log("kernels: " + ", ".join(f"{k['name']} {k['avg_us']:.2f} us" for k in kernels))
+
+    dom = max(kernels, key=lambda k: k["avg_us"])
+    peak_flops = PEAK_BF16_TFLOPS if dom["peak_kind"] == "mfma" else PEAK_FP32_TFLOPS
+    ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
+    ai = dom["flops"] / dom["bytes"]
+    traffic = recorded_traffic(w.name, dom["name"])
+    if ai < ridge:
+        roof = dict(bound="hbm", achieved=dom["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=round(dom["gbs"] / PEAK_HBM_GBS, 4))
+    else:
+        roof = dict(bound="mfma" if dom["peak_kind"] == "mfma" else "alu", achieved=dom["tflops"],
+                    peak=peak_flops, unit="TFLOP/s", frac=round(dom["tflops"] / peak_flops, 4))
+    roof.update(traffic=traffic, kernel=dom["name"], avg_us=dom["avg_us"],
+                algorithmic_flops=dom["flops"], algorithmic_bytes=dom["bytes"])
+
+    nominal = w.nominal_attention_flops()
+    value = nominal / (ms_step * 1e-3) / 1e12
+    att = next(k for k in kernels if k["name"] == "attention")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample ...")
+        cpu = cpu_baseline(w, x, args.cpu_seconds)
+        log(f"cpu baseline: {cpu}")
+
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy calibration: {n} bytes read, {n} bytes written")
+
+    cfg = dict(workload=w.name, B=w.B, n_q=w.n_q, n_k=w.n_k, h=w.h, d_k=w.d_k, d_v=w.d_v,
+               mask={0: "none", 1: "causal", 2: "key_padding", 3: "causal+key_padding"}[w.mask],
+               kind="multi-head block (projections + attention + output projection)"
+               if w.kind == "mha" else "bare attention", buffer_sets=sets)
+    if w.kind == "mha":
+        cfg.update(d_model=w.d_model, self_attention=w.self_attn)
+    if x["key_lengths"] is not None:
+        cfg["key_lengths_mean"] = float(x["key_lengths"].float().mean())
+    out = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "timing": dict(launch="hip graph" if ms_graph is not None else "eager",
+                       ms_per_step_graph=None if ms_graph is None else round(ms_graph, 5),
+                       ms_per_step_eager=round(ms_eager, 5),
+                       kernel_sum_ms=round(sum(k["avg_us"] for k in kernels) / 1e3, 5),
+                       note=graph_note),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/d_model) weights)",
+        "config": cfg,
+        "attention_kernel": dict(avg_us=att["avg_us"], nominal_tflops=round(nominal / (att["avg_us"] * 1e-6) / 1e12, 2),
+                                 algorithmic_tflops=att["tflops"], gbs=att["gbs"]),
+        "kernels": [{k: v for k, v in kk.items() if k not in ("peak_kind",)} for kk in kernels],
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "kernel_source_sha": kernel_source_sha(),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -24,6 +24,7 @@ MAX_PADDED_BATCH = 256
 STATUS = {
     0: "MHA_OK", -1: "MHA_ERR_NULL", -2: "MHA_ERR_DIM", -3: "MHA_ERR_MASK", -4: "MHA_ERR_KEYLEN",
     -5: "MHA_ERR_UNSUPPORTED", -6: "MHA_ERR_WORKSPACE", -7: "MHA_ERR_HIP", -8: "MHA_ERR_SCALE",
+    -9: "MHA_ERR_EVENTS",
 }
 
 # Every symbol include/mha.h declares, with its ctypes signature.
@@ -39,6 +40,10 @@ _SIG = {
     "mha_attend": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _I, _P, ctypes.c_size_t, _P]),
     "mha_project_out": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
     "mha_status_str": (ctypes.c_char_p, [_I]),
+    "sdpa_forward_timed": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _I,
+                                _P, _P, _I, _P]),
+    "mha_forward_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _I,
+                               _P, ctypes.c_size_t, _P, _P, _I, _P]),
 }
 
 _lib = None

@@ -114,11 +114,12 @@ __global__ __launch_bounds__(QB) void attn_fwd_f32_d64_kernel(const AttnArgs a) 
 
 }  // namespace
 
-hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s) {
+hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev) {
   const int nqt = (a.n_q + QB - 1) / QB;
   dim3 grid(a.B * a.h, nqt);
   void* args[] = {(void*)&a};
-  return hipLaunchKernel((const void*)attn_fwd_f32_d64_kernel, grid, dim3(QB), args, 0, s);
+  return hipExtLaunchKernel((const void*)attn_fwd_f32_d64_kernel, grid, dim3(QB), args, 0, s, ev.start,
+                            ev.stop, 0);
 }
 
 }  // namespace mha

@@ -13,39 +13,55 @@
 // so the projection writes Q, K, V directly in the [B][h][n][d] layout the
 // attention kernel streams, and the output projection writes Y row-major.
 //
-// Tiling: 256 threads = 2 x 2 waves, each wave owns a (BM/2) x (BN/2) block of
-// 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16).  K advances 32 at a time;
-// the A tile is staged in LDS as [m][k] and the weight tile transposed to
-// [n][k], so both MFMA operands are single 16-byte LDS reads (the operands
-// want 8 consecutive k per lane).  The next K tile is prefetched into
-// registers while the current one is multiplied.
+// Tiling: 256 threads = 2 x 2 waves; a BM x 128 output tile, each wave a
+// (BM/2) x 64 block of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16).  K
+// advances 64 per step through two LDS buffers (one barrier per step); the
+// global loads of step t+2 are in flight while step t is multiplied.  Both
+// tiles stay in their global row-major layout in LDS: the A operand (8
+// consecutive k of one row per lane) is one 16-byte read, the weight operand
+// (8 consecutive k of one column) is two transposing reads
+// (ds_read_b64_tr_b16).  Rows are XOR-swizzled in 16-byte chunks so that
+// both read patterns are free of bank conflicts.
 #include "kernels.h"
 
 namespace mha {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int BK = 32;
-constexpr int LDK = BK + 8;  // LDS row stride (elements) of both tiles: 80 bytes
+constexpr int BK = 64;
+constexpr int BN = 128;
 
-template <int BM, int BN>
+// A tile [BM][BK]: 128-byte rows; chunk c of row m sits at chunk c ^ ((m >> 1) & 7).
+__device__ __forceinline__ int a_off(int m, int chunk) {
+  return m * BK + ((chunk ^ ((m >> 1) & 7)) << 3);
+}
+// W tile [BK][BN]: 256-byte rows; chunk c of row k sits at chunk c ^ ((k & 3) << 2).
+__device__ __forceinline__ int b_off(int k, int chunk) {
+  return k * BN + ((chunk ^ ((k & 3) << 2)) << 3);
+}
+
+__device__ __forceinline__ i16x4 tr_read(const __bf16* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+}
+
+template <int BM>
 __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
-  constexpr int MB = BM / 64;                 // 32x32 tiles per wave along m
-  constexpr int NB = BN / 64;                 // ... along n
-  constexpr int ACH = BM * BK / 8 / 256;      // 16-byte A chunks per thread
-  constexpr int BTOT = (BK / 2) * (BN / 8);   // (2 rows x 16 bytes) W chunks per tile
-  constexpr int BCH = (BTOT + 255) / 256;      // ... per thread
-  static_assert(ACH >= 1 && ACH * 256 == BM * BK / 8, "A tile must split evenly over 256 threads");
+  constexpr int MB = BM / 64;                  // 32-row MFMA tiles per wave
+  constexpr int NB = 2;                        // 32-column MFMA tiles per wave
+  constexpr int ACH = BM * BK / 8 / 256;       // 16-byte A chunks per thread per step
+  constexpr int BCH = BK * BN / 8 / 256;       // 16-byte W chunks per thread per step
 
-  __shared__ __attribute__((aligned(16))) __bf16 As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) __bf16 Bt[BN * LDK];
+  __shared__ __attribute__((aligned(16))) __bf16 As[2][BM * BK];
+  __shared__ __attribute__((aligned(16))) __bf16 Bs[2][BK * BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int col = lane & 31;
   const int grp = lane >> 5;
   const int wm = wave >> 1;
@@ -56,62 +72,57 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   const int N = g.col_start[g.nseg];
   const __bf16* A = (const __bf16*)g.A;
 
-  u32x4 areg[ACH];
-  u32x4 breg[BCH][2];
-
-  // Weight chunk (k row pair kp, column chunk nc): the segment holding
-  // column n0 + 8nc.  Widths are multiples of 8, so a chunk never straddles.
-  auto w_ptr = [&](int n, int k) -> const __bf16* {
+  // Per-thread source rows/columns, fixed across K steps.  Loads are
+  // unconditional (straight-line code keeps two steps of loads in flight):
+  // rows past M and columns past N are clamped to the last one (their
+  // results are never stored); k past K is zeroed when the chunk is stored.
+  const __bf16* a_src[ACH];
+  int a_row[ACH], a_chunk[ACH];
+#pragma unroll
+  for (int r = 0; r < ACH; ++r) {
+    const int c = tid + r * 256;
+    a_row[r] = c >> 3;
+    a_chunk[r] = c & 7;
+    const int m = min(m0 + a_row[r], g.M - 1);
+    a_src[r] = A + (int64_t)m * g.K + a_chunk[r] * 8;
+  }
+  const __bf16* b_src[BCH];
+  int b_stride[BCH], b_row[BCH], b_chunk[BCH];
+#pragma unroll
+  for (int r = 0; r < BCH; ++r) {
+    const int c = tid + r * 256;
+    b_row[r] = c >> 4;      // k within the step
+    b_chunk[r] = c & 15;    // 8-column chunk within the tile
+    const int n = min(n0 + b_chunk[r] * 8, N - 8);
     int s = 0;
     while (s + 1 < g.nseg && n >= g.col_start[s + 1]) ++s;
-    const GemmSeg& sg = g.seg[s];
-    return (const __bf16*)sg.W + (int64_t)k * sg.width + (n - g.col_start[s]);
-  };
+    b_src[r] = (const __bf16*)g.seg[s].W + (n - g.col_start[s]);
+    b_stride[r] = g.seg[s].width;
+  }
 
-  auto load_tile = [&](int k0) {
+  u32x4 areg[ACH], breg[BCH];
+  auto load_step = [&](int k0) {
 #pragma unroll
     for (int r = 0; r < ACH; ++r) {
-      const int c = tid + r * 256;
-      const int row = m0 + c / (BK / 8);
-      const int k = k0 + (c % (BK / 8)) * 8;
-      areg[r] = (row < g.M && k < g.K) ? *(const u32x4*)(A + (int64_t)row * g.K + k) : u32x4{0, 0, 0, 0};
+      const int k = min(k0 + a_chunk[r] * 8, g.K - 8) - a_chunk[r] * 8;
+      areg[r] = *(const u32x4*)(a_src[r] + k);
     }
 #pragma unroll
     for (int r = 0; r < BCH; ++r) {
-      const int p = tid + r * 256;
-      const int kp = p % (BK / 2);
-      const int nc = p / (BK / 2);
-      const int n = n0 + nc * 8;
-      const int k = k0 + 2 * kp;
-      if (p < BTOT && n < N) {
-        breg[r][0] = k < g.K ? *(const u32x4*)w_ptr(n, k) : u32x4{0, 0, 0, 0};
-        breg[r][1] = k + 1 < g.K ? *(const u32x4*)w_ptr(n, k + 1) : u32x4{0, 0, 0, 0};
-      } else {
-        breg[r][0] = u32x4{0, 0, 0, 0};
-        breg[r][1] = u32x4{0, 0, 0, 0};
-      }
+      const int k = min(k0 + b_row[r], g.K - 1);
+      breg[r] = *(const u32x4*)(b_src[r] + (int64_t)k * b_stride[r]);
     }
   };
-
-  auto store_tile = [&]() {
+  auto store_step = [&](int buf, int k0) {
 #pragma unroll
     for (int r = 0; r < ACH; ++r) {
-      const int c = tid + r * 256;
-      *(u32x4*)&As[(c / (BK / 8)) * LDK + (c % (BK / 8)) * 8] = areg[r];
+      const bool ok = k0 + a_chunk[r] * 8 < g.K;
+      *(u32x4*)&As[buf][a_off(a_row[r], a_chunk[r])] = ok ? areg[r] : u32x4{0, 0, 0, 0};
     }
 #pragma unroll
     for (int r = 0; r < BCH; ++r) {
-      const int p = tid + r * 256;
-      const int kp = p % (BK / 2);
-      const int nc = p / (BK / 2);
-      if (p >= BTOT) continue;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const unsigned x0 = breg[r][0][j];  // W[k][n+2j], W[k][n+2j+1]
-        const unsigned x1 = breg[r][1][j];  // W[k+1][...]
-        *(unsigned*)&Bt[(8 * nc + 2 * j) * LDK + 2 * kp] = (x0 & 0xffffu) | (x1 << 16);
-        *(unsigned*)&Bt[(8 * nc + 2 * j + 1) * LDK + 2 * kp] = (x0 >> 16) | (x1 & 0xffff0000u);
-      }
+      const bool ok = k0 + b_row[r] < g.K;
+      *(u32x4*)&Bs[buf][b_off(b_row[r], b_chunk[r])] = ok ? breg[r] : u32x4{0, 0, 0, 0};
     }
   };
 
@@ -121,22 +132,39 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
-  const int ktiles = (g.K + BK - 1) / BK;
-  load_tile(0);
-  for (int t = 0; t < ktiles; ++t) {
+  // Weight-operand source lane pattern of the transposing read: within each
+  // 16-lane group, lane s addresses row (s / 4) and columns 4 (s % 4) .. +3.
+  const int tr_k = (lane & 15) >> 2;
+  const int tr_n = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  const int steps = (g.K + BK - 1) / BK;
+  load_step(0);
+  store_step(0, 0);
+  load_step(BK);
+  for (int t = 0; t < steps; ++t) {
+    const int buf = t & 1;
     __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (t + 1 < ktiles) load_tile((t + 1) * BK);
+    store_step(buf ^ 1, (t + 1) * BK);
+    load_step((t + 2) * BK);
+    // Keep the loads here: sinking them toward their use (next step) would
+    // leave no compute to hide their latency.
+    __builtin_amdgcn_sched_barrier(0);
+    const __bf16* as = As[buf];
+    const __bf16* bs = Bs[buf];
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       bf16x8 af[MB], bfr[NB];
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        af[i] = *(const bf16x8*)&As[(wm * (BM / 2) + 32 * i + col) * LDK + 16 * ks + 8 * grp];
+        af[i] = *(const bf16x8*)&as[a_off(wm * (BM / 2) + 32 * i + col, 2 * ks + grp)];
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        bfr[j] = *(const bf16x8*)&Bt[(wn * (BN / 2) + 32 * j + col) * LDK + 16 * ks + 8 * grp];
+      for (int j = 0; j < NB; ++j) {
+        const int k = 16 * ks + 8 * grp + tr_k;
+        const int n = wn * 64 + 32 * j + tr_n;
+        const i16x4 lo = tr_read(&bs[b_off(k, n >> 3) + (n & 7)]);
+        const i16x4 hi = tr_read(&bs[b_off(k + 4, n >> 3) + (n & 7)]);
+        bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -145,10 +173,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
     }
   }
 
-  // acc[i][j][e] = C[m0 + wm*BM/2 + 32i + 8(e/4) + 4grp + e%4][n0 + wn*BN/2 + 32j + col]
+  // acc[i][j][e] = C[m0 + wm*BM/2 + 32i + 8(e/4) + 4grp + e%4][n0 + wn*64 + 32j + col]
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int n = n0 + wn * (BN / 2) + 32 * j + col;
+    const int n = n0 + wn * 64 + 32 * j + col;
     if (n >= N) continue;
     int s = 0;
     while (s + 1 < g.nseg && n >= g.col_start[s + 1]) ++s;
@@ -156,39 +184,46 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
     const int c = n - g.col_start[s];
     const int head = c / sg.hd;
     const int dd = c - head * sg.hd;
-    __bf16* dst = (__bf16*)sg.dst;
+    __bf16* dst = (__bf16*)sg.dst + (int64_t)head * sg.rows * sg.hd + dd;
+    const int64_t batch_stride = (int64_t)sg.heads * sg.rows * sg.hd;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
+      // Rows of this lane: mb + {0,1,2,3, 8..11, 16..19, 24..27}, mb = first row.
+      const int mb = m0 + wm * (BM / 2) + 32 * i + 4 * grp;
+      int bb = mb / sg.rows;
+      int pos = mb - bb * sg.rows;
+      int m = mb;
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int m = m0 + wm * (BM / 2) + 32 * i + 8 * (e >> 2) + 4 * grp + (e & 3);
-        if (m >= g.M) continue;
-        const int bb = m / sg.rows;
-        const int pos = m - bb * sg.rows;
-        const int64_t off = ((int64_t)(bb * sg.heads + head) * sg.rows + pos) * sg.hd + dd;
-        dst[off] = (__bf16)acc[i][j][e];
+        const int next = mb + 8 * (e >> 2) + (e & 3);
+        while (m < next) {  // advance (bb, pos) to row `next`
+          ++m;
+          if (++pos == sg.rows) { pos = 0; ++bb; }
+        }
+        if (m < g.M) dst[bb * batch_stride + (int64_t)pos * sg.hd] = (__bf16)acc[i][j][e];
       }
     }
   }
 }
 
-template <int BM, int BN>
-hipError_t launch_tile(const GemmArgs& g, hipStream_t s) {
+template <int BM>
+hipError_t launch_tile(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
   const int N = g.col_start[g.nseg];
   dim3 grid((N + BN - 1) / BN, (g.M + BM - 1) / BM);
   void* args[] = {(void*)&g};
-  return hipLaunchKernel((const void*)gemm_bf16_kernel<BM, BN>, grid, dim3(256), args, 0, s);
+  return hipExtLaunchKernel((const void*)gemm_bf16_kernel<BM>, grid, dim3(256), args, 0, s,
+                            ev.start, ev.stop, 0);
 }
 
 }  // namespace
 
-hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s) {
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
   const int N = g.col_start[g.nseg];
-  // Prefer big tiles; fall back to 64x64 when big tiles would leave most of
-  // the 256 compute units idle.
-  const long big = (long)((N + 127) / 128) * ((g.M + 127) / 128);
-  if (big >= 256) return launch_tile<128, 128>(g, s);
-  return launch_tile<64, 64>(g, s);
+  // 128-row tiles when they still give every compute unit two workgroups,
+  // otherwise 64-row tiles for more parallelism.
+  const long big = (long)((N + BN - 1) / BN) * ((g.M + 127) / 128);
+  if (big >= 512) return launch_tile<128>(g, s, ev);
+  return launch_tile<64>(g, s, ev);
 }
 
 }  // namespace mha

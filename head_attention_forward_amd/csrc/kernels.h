@@ -2,6 +2,7 @@
 // Not installed; the public interface is include/mha.h.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -48,8 +49,15 @@ struct GemmArgs {
   int col_start[4];   // prefix sums of segment widths; col_start[nseg] = N
 };
 
-hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s);
-hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s);
-hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s);
+// Launch-time events: when `start`/`stop` are non-null they are recorded at
+// the start and at the end of this kernel's execution (hipExtLaunchKernel).
+struct LaunchEvents {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+
+hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev = {});
 
 }  // namespace mha

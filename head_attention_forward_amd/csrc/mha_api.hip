@@ -91,6 +91,31 @@ int check_mha(const void* ws, size_t ws_bytes, int B, int n_q, int n_k, int d_mo
 
 int launch_status(hipError_t e) { return e == hipSuccess ? MHA_OK : MHA_ERR_HIP; }
 
+// Hands out (start, stop) event pairs to successive launches of a timed call;
+// a null timer hands out none.
+struct Timer {
+  hipEvent_t* ev = nullptr;
+  int cap = 0;
+  int used = 0;  // launches so far
+  LaunchEvents next() {
+    LaunchEvents le;
+    if (ev != nullptr && 2 * used + 1 < cap) {
+      le.start = ev[2 * used];
+      le.stop = ev[2 * used + 1];
+    }
+    ++used;
+    return le;
+  }
+};
+
+LaunchEvents next_events(Timer* t) { return t ? t->next() : LaunchEvents{}; }
+
+// Launches an mha_forward call makes: one fused projection for
+// self-attention, two otherwise, then attention and the output projection.
+int mha_launch_count(const void* X_q, const void* X_kv, int n_q, int n_k) {
+  return (X_q == X_kv && n_q == n_k) ? 3 : 4;
+}
+
 // Head-major layout [B][h][n][d] of the workspace Q, K, V.
 void set_head_major(int64_t& sb, int64_t& sh, int64_t& sr, int h, int n, int d) {
   sr = d;
@@ -100,7 +125,7 @@ void set_head_major(int64_t& sb, int64_t& sh, int64_t& sr, int h, int n, int d) 
 
 int do_project_in(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
                   const void* Wv, int B, int n_q, int n_k, int d_model, int h, int d_k, int d_v,
-                  const Workspace& w, hipStream_t stream) {
+                  const Workspace& w, hipStream_t stream, Timer* tm) {
   const GemmSeg sq{Wq, w.Q, h * d_k, d_k, h, n_q};
   const GemmSeg sk{Wk, w.K, h * d_k, d_k, h, n_k};
   const GemmSeg sv{Wv, w.V, h * d_v, d_v, h, n_k};
@@ -118,7 +143,7 @@ int do_project_in(const void* X_q, const void* X_kv, const void* Wq, const void*
     g.col_start[1] = h * d_k;
     g.col_start[2] = 2 * h * d_k;
     g.col_start[3] = 2 * h * d_k + h * d_v;
-    return launch_status(launch_gemm_bf16(g, stream));
+    return launch_status(launch_gemm_bf16(g, stream, next_events(tm)));
   }
   GemmArgs gq{};
   gq.A = X_q;
@@ -128,7 +153,7 @@ int do_project_in(const void* X_q, const void* X_kv, const void* Wq, const void*
   gq.seg[0] = sq;
   gq.col_start[0] = 0;
   gq.col_start[1] = h * d_k;
-  int st = launch_status(launch_gemm_bf16(gq, stream));
+  int st = launch_status(launch_gemm_bf16(gq, stream, next_events(tm)));
   if (st != MHA_OK) return st;
   GemmArgs gkv{};
   gkv.A = X_kv;
@@ -140,11 +165,11 @@ int do_project_in(const void* X_q, const void* X_kv, const void* Wq, const void*
   gkv.col_start[0] = 0;
   gkv.col_start[1] = h * d_k;
   gkv.col_start[2] = h * d_k + h * d_v;
-  return launch_status(launch_gemm_bf16(gkv, stream));
+  return launch_status(launch_gemm_bf16(gkv, stream, next_events(tm)));
 }
 
 int do_attend(int B, int n_q, int n_k, int h, int d_k, int d_v, int mask_kind,
-              const int32_t* key_lengths, const Workspace& w, hipStream_t stream) {
+              const int32_t* key_lengths, const Workspace& w, hipStream_t stream, Timer* tm) {
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.Q = w.Q;
@@ -164,11 +189,11 @@ int do_attend(int B, int n_q, int n_k, int h, int d_k, int d_v, int mask_kind,
   a.n_k = n_k;
   a.scale = 1.0f / sqrtf((float)d_k);
   fill_mask(a, mask_kind, key_lengths);
-  return launch_status(launch_attn_bf16_d64(a, stream));
+  return launch_status(launch_attn_bf16_d64(a, stream, next_events(tm)));
 }
 
 int do_project_out(const void* Wo, void* Y, int B, int n_q, int d_model, int h, int d_v,
-                   const Workspace& w, hipStream_t stream) {
+                   const Workspace& w, hipStream_t stream, Timer* tm) {
   GemmArgs g{};
   g.A = w.O;
   g.M = B * n_q;
@@ -177,7 +202,7 @@ int do_project_out(const void* Wo, void* Y, int B, int n_q, int d_model, int h, 
   g.seg[0] = GemmSeg{Wo, Y, d_model, d_model, 1, B * n_q};
   g.col_start[0] = 0;
   g.col_start[1] = d_model;
-  return launch_status(launch_gemm_bf16(g, stream));
+  return launch_status(launch_gemm_bf16(g, stream, next_events(tm)));
 }
 
 }  // namespace
@@ -198,6 +223,7 @@ const char* mha_status_str(int status) {
     case MHA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case MHA_ERR_HIP: return "HIP launch failed";
     case MHA_ERR_SCALE: return "scale must be finite and > 0";
+    case MHA_ERR_EVENTS: return "timing events missing or fewer than two per launch";
     default: return "unknown status";
   }
 }
@@ -208,9 +234,9 @@ size_t mha_workspace_bytes(int B, int n_q, int n_k, int h, int d_k, int d_v, int
   return carve(nullptr, B, n_q, n_k, h, d_k, d_v, dtype).bytes;
 }
 
-int sdpa_forward(const void* Q, const void* K, const void* V, void* O, int B, int h, int n_q,
-                 int n_k, int d_k, int d_v, float scale, int mask_kind,
-                 const int32_t* key_lengths, int dtype, hipStream_t stream) {
+static int sdpa_impl(const void* Q, const void* K, const void* V, void* O, int B, int h, int n_q,
+                     int n_k, int d_k, int d_v, float scale, int mask_kind,
+                     const int32_t* key_lengths, int dtype, hipStream_t stream, Timer* tm) {
   if (!Q || !K || !V || !O) return MHA_ERR_NULL;
   int st = check_attn_dims(B, h, n_q, n_k, d_k, d_v);
   if (st != MHA_OK) return st;
@@ -235,9 +261,31 @@ int sdpa_forward(const void* Q, const void* K, const void* V, void* O, int B, in
   a.n_k = n_k;
   a.scale = scale;
   fill_mask(a, mask_kind, key_lengths);
-  const hipError_t e = dtype == MHA_DTYPE_BF16 ? launch_attn_bf16_d64(a, stream)
-                                               : launch_attn_f32_d64(a, stream);
+  const LaunchEvents le = next_events(tm);
+  const hipError_t e = dtype == MHA_DTYPE_BF16 ? launch_attn_bf16_d64(a, stream, le)
+                                               : launch_attn_f32_d64(a, stream, le);
   return launch_status(e);
+}
+
+int sdpa_forward(const void* Q, const void* K, const void* V, void* O, int B, int h, int n_q,
+                 int n_k, int d_k, int d_v, float scale, int mask_kind,
+                 const int32_t* key_lengths, int dtype, hipStream_t stream) {
+  return sdpa_impl(Q, K, V, O, B, h, n_q, n_k, d_k, d_v, scale, mask_kind, key_lengths, dtype,
+                   stream, nullptr);
+}
+
+int sdpa_forward_timed(const void* Q, const void* K, const void* V, void* O, int B, int h,
+                       int n_q, int n_k, int d_k, int d_v, float scale, int mask_kind,
+                       const int32_t* key_lengths, int dtype, hipStream_t stream,
+                       hipEvent_t* events, int capacity, int* n_launches) {
+  if (events == nullptr || capacity < 2) return MHA_ERR_EVENTS;
+  for (int i = 0; i < 2; ++i)
+    if (events[i] == nullptr) return MHA_ERR_EVENTS;
+  Timer tm{events, capacity, 0};
+  const int st = sdpa_impl(Q, K, V, O, B, h, n_q, n_k, d_k, d_v, scale, mask_kind, key_lengths,
+                           dtype, stream, &tm);
+  if (n_launches) *n_launches = tm.used;
+  return st;
 }
 
 int mha_project_in(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
@@ -249,7 +297,8 @@ int mha_project_in(const void* X_q, const void* X_kv, const void* Wq, const void
   if (!aligned16(X_q) || !aligned16(X_kv) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv))
     return MHA_ERR_UNSUPPORTED;
   const Workspace w = carve(workspace, B, n_q, n_k, h, d_k, d_v, dtype);
-  return do_project_in(X_q, X_kv, Wq, Wk, Wv, B, n_q, n_k, d_model, h, d_k, d_v, w, stream);
+  return do_project_in(X_q, X_kv, Wq, Wk, Wv, B, n_q, n_k, d_model, h, d_k, d_v, w, stream,
+                       nullptr);
 }
 
 int mha_attend(int B, int n_q, int n_k, int h, int d_k, int d_v, int mask_kind,
@@ -260,7 +309,7 @@ int mha_attend(int B, int n_q, int n_k, int h, int d_k, int d_v, int mask_kind,
   st = check_mask(mask_kind, B, n_q, n_k, key_lengths);
   if (st != MHA_OK) return st;
   const Workspace w = carve(workspace, B, n_q, n_k, h, d_k, d_v, dtype);
-  return do_attend(B, n_q, n_k, h, d_k, d_v, mask_kind, key_lengths, w, stream);
+  return do_attend(B, n_q, n_k, h, d_k, d_v, mask_kind, key_lengths, w, stream, nullptr);
 }
 
 int mha_project_out(const void* Wo, void* Y, int B, int n_q, int n_k, int d_model, int h,
@@ -271,13 +320,13 @@ int mha_project_out(const void* Wo, void* Y, int B, int n_q, int n_k, int d_mode
   if (st != MHA_OK) return st;
   if (!aligned16(Wo) || !aligned16(Y)) return MHA_ERR_UNSUPPORTED;
   const Workspace w = carve(workspace, B, n_q, n_k, h, d_k, d_v, dtype);
-  return do_project_out(Wo, Y, B, n_q, d_model, h, d_v, w, stream);
+  return do_project_out(Wo, Y, B, n_q, d_model, h, d_v, w, stream, nullptr);
 }
 
-int mha_forward(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
-                const void* Wv, const void* Wo, void* Y, int B, int n_q, int n_k, int d_model,
-                int h, int d_k, int d_v, int mask_kind, const int32_t* key_lengths, int dtype,
-                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static int mha_impl(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
+                    const void* Wv, const void* Wo, void* Y, int B, int n_q, int n_k, int d_model,
+                    int h, int d_k, int d_v, int mask_kind, const int32_t* key_lengths, int dtype,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream, Timer* tm) {
   if (!X_q || !X_kv || !Wq || !Wk || !Wv || !Wo || !Y) return MHA_ERR_NULL;
   int st = check_mha(workspace, workspace_bytes, B, n_q, n_k, d_model, h, d_k, d_v, dtype);
   if (st != MHA_OK) return st;
@@ -287,11 +336,36 @@ int mha_forward(const void* X_q, const void* X_kv, const void* Wq, const void* W
       !aligned16(Wv) || !aligned16(Wo) || !aligned16(Y))
     return MHA_ERR_UNSUPPORTED;
   const Workspace w = carve(workspace, B, n_q, n_k, h, d_k, d_v, dtype);
-  st = do_project_in(X_q, X_kv, Wq, Wk, Wv, B, n_q, n_k, d_model, h, d_k, d_v, w, stream);
+  st = do_project_in(X_q, X_kv, Wq, Wk, Wv, B, n_q, n_k, d_model, h, d_k, d_v, w, stream, tm);
   if (st != MHA_OK) return st;
-  st = do_attend(B, n_q, n_k, h, d_k, d_v, mask_kind, key_lengths, w, stream);
+  st = do_attend(B, n_q, n_k, h, d_k, d_v, mask_kind, key_lengths, w, stream, tm);
   if (st != MHA_OK) return st;
-  return do_project_out(Wo, Y, B, n_q, d_model, h, d_v, w, stream);
+  return do_project_out(Wo, Y, B, n_q, d_model, h, d_v, w, stream, tm);
+}
+
+int mha_forward(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
+                const void* Wv, const void* Wo, void* Y, int B, int n_q, int n_k, int d_model,
+                int h, int d_k, int d_v, int mask_kind, const int32_t* key_lengths, int dtype,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mha_impl(X_q, X_kv, Wq, Wk, Wv, Wo, Y, B, n_q, n_k, d_model, h, d_k, d_v, mask_kind,
+                  key_lengths, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int mha_forward_timed(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
+                      const void* Wv, const void* Wo, void* Y, int B, int n_q, int n_k,
+                      int d_model, int h, int d_k, int d_v, int mask_kind,
+                      const int32_t* key_lengths, int dtype, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                      int capacity, int* n_launches) {
+  const int need = 2 * mha_launch_count(X_q, X_kv, n_q, n_k);
+  if (events == nullptr || capacity < need) return MHA_ERR_EVENTS;
+  for (int i = 0; i < need; ++i)
+    if (events[i] == nullptr) return MHA_ERR_EVENTS;
+  Timer tm{events, capacity, 0};
+  const int st = mha_impl(X_q, X_kv, Wq, Wk, Wv, Wo, Y, B, n_q, n_k, d_model, h, d_k, d_v,
+                          mask_kind, key_lengths, dtype, workspace, workspace_bytes, stream, &tm);
+  if (n_launches) *n_launches = tm.used;
+  return st;
 }
 
 }  // extern "C"

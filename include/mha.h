@@ -58,6 +58,7 @@ extern "C" {
 #define MHA_ERR_WORKSPACE     -6  /* workspace missing or smaller than required    */
 #define MHA_ERR_HIP           -7  /* a HIP launch failed                           */
 #define MHA_ERR_SCALE         -8  /* scale not finite or not > 0                   */
+#define MHA_ERR_EVENTS        -9  /* timing events missing or too few              */
 
 /* Mask kinds (bit 0: causal, bit 1: key padding). */
 #define MHA_MASK_NONE              0
@@ -170,6 +171,33 @@ int mha_attend(int B, int n_q, int n_k, int h, int d_k, int d_v,
 int mha_project_out(const void* Wo, void* Y,
                     int B, int n_q, int n_k, int d_model, int h, int d_k, int d_v,
                     int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Instrumented variants of sdpa_forward and mha_forward, for benchmarks and
+ * profilers: the same checks, launches and results, and in addition kernel
+ * launch i (in launch order, i = 0, 1, ...) records events[2i] when the
+ * kernel starts and events[2i+1] when it ends (AMD hipExtLaunchKernel launch
+ * events; elapsed times between them are pure kernel execution).  The caller
+ * creates the events (default flags) and owns them.  Launch counts:
+ * sdpa_forward 1; mha_forward 3 when X_kv == X_q and n_q == n_k (fused input
+ * projection, attention, output projection), otherwise 4 (Q projection,
+ * K/V projection, attention, output projection).  `capacity` is the number of
+ * events passed; fewer than two per launch, or a NULL event among them, is
+ * MHA_ERR_EVENTS.  *n_launches (if not NULL) receives the launch count.
+ */
+int sdpa_forward_timed(const void* Q, const void* K, const void* V, void* O,
+                       int B, int h, int n_q, int n_k, int d_k, int d_v,
+                       float scale, int mask_kind, const int32_t* key_lengths,
+                       int dtype, hipStream_t stream,
+                       hipEvent_t* events, int capacity, int* n_launches);
+
+int mha_forward_timed(const void* X_q, const void* X_kv,
+                      const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                      void* Y,
+                      int B, int n_q, int n_k, int d_model, int h, int d_k, int d_v,
+                      int mask_kind, const int32_t* key_lengths, int dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      hipEvent_t* events, int capacity, int* n_launches);
 
 /* Text of a status code (static storage; never NULL). */
 const char* mha_status_str(int status);

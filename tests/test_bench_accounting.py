@@ -1,0 +1,67 @@
+"""The bench's algorithmic flop and byte counts against closed forms (CPU)."""
+
+import math
+
+import pytest
+import torch
+
+import bench
+from head_attention_forward_amd.workloads import WORKLOADS, generate
+
+
+def test_attention_counts_unmasked_self():
+    w = WORKLOADS["encoder_self_base"]
+    f, b = bench.attention_accounting(w, None)
+    assert f == 4 * 32 * 8 * 100 * 100 * 64            # dense = nominal when unmasked
+    assert b == 2 * 32 * 8 * 100 * 64 * 4                # Q, K, V read once, O written once
+    assert abs(b - 13.1e6) < 0.05e6
+
+
+def test_attention_counts_causal():
+    w = WORKLOADS["long_causal_sdpa"]
+    f, b = bench.attention_accounting(w, None)
+    n = 4096
+    assert f == 2 * (n * (n + 1) / 2) * 128 * 64        # i + 1 visible keys for query i
+    assert abs(f / 1e9 - 137.5) < 0.1
+    assert abs(w.nominal_attention_flops() / 1e9 - 274.9) < 0.1
+
+
+def test_attention_counts_padded():
+    w = WORKLOADS["cross_padded_big"]
+    kl = torch.tensor([64, 128] * 16, dtype=torch.int32)
+    f, b = bench.attention_accounting(w, kl)
+    assert f == 2 * 96 * (64 + 128) * 16 * 16 * 128
+    assert b == 2 * 16 * (32 * 96 * 64 + (64 + 128) * 16 * 128 + 32 * 96 * 64)
+
+
+def test_causal_with_padding_counts():
+    w = WORKLOADS["decoder_causal_base"].replace(kind="sdpa", mask=3, B=2, n_q=10, n_k=10, h=1)
+    f, _ = bench.attention_accounting(w, [4, 10])
+    # batch 0: queries 0..3 see 1..4 keys, queries 4..9 see 4; batch 1: 1..10
+    pairs = (1 + 2 + 3 + 4 + 6 * 4) + 55
+    assert f == 2 * pairs * 128
+
+
+def test_gemm_plan():
+    plan, _ = bench.kernel_plan(WORKLOADS["encoder_self_base"])
+    assert [p["name"] for p in plan] == ["qkv_projection_gemm", "attention", "output_projection_gemm"]
+    assert plan[0]["flops"] == 2 * 3200 * 512 * 1536
+    assert plan[2]["flops"] == 2 * 3200 * 512 * 512
+    plan, _ = bench.kernel_plan(WORKLOADS["cross_padded_big"])
+    assert [p["name"] for p in plan][:2] == ["q_projection_gemm", "kv_projection_gemm"]
+    assert abs((plan[0]["flops"] + plan[1]["flops"]) / 1e9 - 23.6) < 0.1
+
+
+def test_buffer_sets_exceed_infinity_cache():
+    for name, w in WORKLOADS.items():
+        sets = max(2, min(64, math.ceil(2 * bench.MALL_BYTES / bench.set_bytes(w))))
+        if w.B * w.n_q > 64:
+            assert sets * bench.set_bytes(w) >= 2 * bench.MALL_BYTES or sets == 64, name
+
+
+def test_gpus_above_one_is_refused(monkeypatch, capsys):
+    monkeypatch.setattr("sys.argv", ["bench.py", "--gpus", "2"])
+    with pytest.raises(SystemExit) as e:
+        bench.main()
+    assert e.value.code == 2
+    assert "one GPU" in capsys.readouterr().err

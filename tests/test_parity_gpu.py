@@ -184,6 +184,25 @@ def test_sdpa_bf16_edges(dev, B, h, n_q, n_k, mask, kl):
     assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"edge {B}x{h}x{n_q}x{n_k} m{mask}")
 
 
+@pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", [(2, 64, 1000, 1000, 3, [1000, 777]),
+                                                 (2, 64, 1000, 1300, 0, None),
+                                                 (1, 128, 777, 777, 1, None)])
+def test_sdpa_bf16_large_ragged_sampled(dev, B, h, n_q, n_k, mask, kl):
+    """Shapes large enough for the 256-query workgroup configuration, with
+    ragged query and key counts; sampled rows against the oracle."""
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.bfloat16, seed=n_q + n_k)
+    announce("sdpa_forward bf16 large", dict(B=B, h=h, n_q=n_q, n_k=n_k, mask=mask, kl=kl))
+    O = run_sdpa(dev, Q, K, V, 0.125, mask, kl)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(n_q)
+    idx = [(b, hh, q) for b in range(B) for hh in (0, h - 1) for q in (0, 255, 256, n_q - 1)]
+    idx += [(int(rng.integers(B)), int(rng.integers(h)), int(rng.integers(n_q))) for _ in range(300)]
+    idx = np.array(idx)
+    want = oracle.sdpa_ref_rows(to_f64(Q), to_f64(K), to_f64(V), 0.125, mask,
+                                None if kl is None else np.array(kl), idx)
+    assert_bf16_close(O[idx[:, 0], idx[:, 1], idx[:, 2]], want, f"large {B}x{h}x{n_q}x{n_k} m{mask}")
+
+
 @pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", [(1, 1, 1, 1, 0, None), (2, 2, 100, 100, 1, None),
                                                  (2, 1, 70, 129, 2, [5, 129]),
                                                  (1, 2, 200, 200, 3, [150])])
