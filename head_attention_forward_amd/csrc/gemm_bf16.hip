@@ -13,117 +13,223 @@
 // so the projection writes Q, K, V directly in the [B][h][n][d] layout the
 // attention kernel streams, and the output projection writes Y row-major.
 //
-// Tiling: 256 threads = 2 x 2 waves; a BM x 128 output tile, each wave a
-// (BM/2) x 64 block of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16).  K
-// advances 64 per step through two LDS buffers (one barrier per step); the
-// global loads of step t+2 are in flight while step t is multiplied.  Both
-// tiles stay in their global row-major layout in LDS: the A operand (8
-// consecutive k of one row per lane) is one 16-byte read, the weight operand
-// (8 consecutive k of one column) is two transposing reads
-// (ds_read_b64_tr_b16).  Rows are XOR-swizzled in 16-byte chunks so that
-// both read patterns are free of bank conflicts.
+// Tiling: 256 threads = 2 x 2 waves; a BM x BN output tile, each wave a
+// (BM/2) x (BN/2) block of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16).
+// K advances 64 per stage.  Stages go from global memory straight into LDS
+// (global_load_lds_dwordx4: no register staging) through a ring of NS
+// buffers, NS-1 stages ahead of the one being multiplied, one barrier per
+// stage.  Both tiles keep their global row-major layout in LDS, with 16-byte
+// chunks XOR-swizzled so that the operand reads are free of bank conflicts:
+// the activation operand (8 consecutive k of one row per lane) is one
+// 16-byte read, the weight operand (8 consecutive k of one column) two
+// transposing reads (ds_read_b64_tr_b16).
+//
+// The products are computed transposed, C^T = W^T A^T: the weight fragment
+// is the MFMA's first operand.  A lane then holds, for one output row, four
+// runs of 4 consecutive columns, which it stores as 8-byte vectors.
+//
+// Tile order: workgroups are dealt to the 8 XCDs round-robin; the linear
+// workgroup id is remapped so that each XCD owns a contiguous band of the
+// row-major tile order (whole rows of tiles), i.e. each XCD's L2 streams its
+// own band of activation rows and the (small) weight matrix, instead of
+// every XCD reading every activation row.
 #include "kernels.h"
 
 namespace mha {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int BK = 64;
-constexpr int BN = 128;
+constexpr int kXcds = 8;
 
-// A tile [BM][BK]: 128-byte rows; chunk c of row m sits at chunk c ^ ((m >> 1) & 7).
-__device__ __forceinline__ int a_off(int m, int chunk) {
-  return m * BK + ((chunk ^ ((m >> 1) & 7)) << 3);
-}
-// W tile [BK][BN]: 256-byte rows; chunk c of row k sits at chunk c ^ ((k & 3) << 2).
-__device__ __forceinline__ int b_off(int k, int chunk) {
-  return k * BN + ((chunk ^ ((k & 3) << 2)) << 3);
+// A tile [BM][64]: 128-byte rows; chunk c of row m sits at chunk c ^ ((m >> 1) & 7).
+__device__ __forceinline__ int a_pos(int m, int chunk) { return chunk ^ ((m >> 1) & 7); }
+// W tile [64][BN]: BN = 128 -> 256-byte rows, chunk c of row k at c ^ ((k & 3) << 2);
+// BN = 64 -> 128-byte rows, chunk c of row k at c ^ (((k >> 1) & 1) << 2).
+template <int BN>
+__device__ __forceinline__ int b_pos(int k, int chunk) {
+  if constexpr (BN == 128) return chunk ^ ((k & 3) << 2);
+  else return chunk ^ (((k >> 1) & 1) << 2);
 }
 
 __device__ __forceinline__ i16x4 tr_read(const __bf16* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
 }
 
-template <int BM>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
-  constexpr int MB = BM / 64;                  // 32-row MFMA tiles per wave
-  constexpr int NB = 2;                        // 32-column MFMA tiles per wave
-  constexpr int ACH = BM * BK / 8 / 256;       // 16-byte A chunks per thread per step
-  constexpr int BCH = BK * BN / 8 / 256;       // 16-byte W chunks per thread per step
+// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
 
-  __shared__ __attribute__((aligned(16))) __bf16 As[2][BM * BK];
-  __shared__ __attribute__((aligned(16))) __bf16 Bs[2][BK * BN];
+// Waits until at most `later` stages issued after the current one are still
+// in flight (LPS loads per stage and wave), i.e. the current stage landed.
+template <int LPS, int NS>
+__device__ __forceinline__ void wait_stage(int later) {
+  if constexpr (NS >= 4) {
+    if (later >= 2) { wait_vmcnt<2 * LPS>(); return; }
+  }
+  if constexpr (NS >= 3) {
+    if (later >= 1) { wait_vmcnt<LPS>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+// Segment of column n and its fields, selected without indexing the argument
+// array dynamically (which would spill it to memory).
+__device__ __forceinline__ int seg_of(const GemmArgs& g, int n) {
+  return (g.nseg > 1 && n >= g.col_start[1]) + (g.nseg > 2 && n >= g.col_start[2]);
+}
+template <typename T>
+__device__ __forceinline__ T seg_field(const GemmArgs& g, int s, T GemmSeg::*f) {
+  return s == 0 ? g.seg[0].*f : (s == 1 ? g.seg[1].*f : g.seg[2].*f);
+}
+__device__ __forceinline__ const void* seg_ptr(const GemmArgs& g, int s) {
+  return seg_field(g, s, &GemmSeg::W);
+}
+__device__ __forceinline__ int seg_start(const GemmArgs& g, int s) {
+  return s == 0 ? g.col_start[0] : (s == 1 ? g.col_start[1] : g.col_start[2]);
+}
+
+// 16-byte global -> LDS copy per lane from a wave-uniform 64-bit base plus a
+// per-lane 32-bit byte offset (the saddr form: no vector address arithmetic);
+// lane l writes LDS byte address lds + 16 l.  Inline assembly, so that the
+// compiler does not wait for it before every LDS read; the kernel waits for
+// it explicitly (vmcnt) before the barrier that publishes a stage.
+__device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsigned lds) {
+  // The base is wave-uniform; readfirstlane pins it to SGPRs for the saddr operand.
+  const unsigned long long p = (unsigned long long)(size_t)sbase;
+  // (readfirstlane returns int: widen through unsigned, never sign-extend.)
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)p);
+  const unsigned long long sp = ((unsigned long long)hi << 32) | (unsigned long long)lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"((const void*)(size_t)sp)
+               : "memory", "m0");
+}
+
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+  return __builtin_amdgcn_readfirstlane(
+      (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p);
+}
+
+template <int BM, int BN, int NS>
+__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
+  static_assert(BM == 64 || BM == 128, "tile rows");
+  static_assert(BN == 64 || BN == 128, "tile columns");
+  static_assert(NS >= 2 && NS <= 4, "ring depth");
+  constexpr int MB = BM / 64;          // 32-row MFMA tiles per wave
+  constexpr int NB = BN / 64;          // 32-column MFMA tiles per wave
+  constexpr int AL = BM * BK * 2 / 1024 / 4;   // 1 KB A loads per wave and stage
+  constexpr int BL = BK * BN * 2 / 1024 / 4;   // 1 KB W loads per wave and stage
+  constexpr int LPS = AL + BL;
+  constexpr int BROW = BN / 8;                 // 16-byte chunks per W row
+
+  __shared__ __attribute__((aligned(1024))) __bf16 As[NS][BM * BK];
+  __shared__ __attribute__((aligned(1024))) __bf16 Bs[NS][BK * BN];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int grp = lane >> 5;
   const int wm = wave >> 1;
   const int wn = wave & 1;
 
-  const int n0 = blockIdx.x * BN;
-  const int m0 = blockIdx.y * BM;
   const int N = g.col_start[g.nseg];
-  const __bf16* A = (const __bf16*)g.A;
-
-  // Per-thread source rows/columns, fixed across K steps.  Loads are
-  // unconditional (straight-line code keeps two steps of loads in flight):
-  // rows past M and columns past N are clamped to the last one (their
-  // results are never stored); k past K is zeroed when the chunk is stored.
-  const __bf16* a_src[ACH];
-  int a_row[ACH], a_chunk[ACH];
-#pragma unroll
-  for (int r = 0; r < ACH; ++r) {
-    const int c = tid + r * 256;
-    a_row[r] = c >> 3;
-    a_chunk[r] = c & 7;
-    const int m = min(m0 + a_row[r], g.M - 1);
-    a_src[r] = A + (int64_t)m * g.K + a_chunk[r] * 8;
+  const int MT = (g.M + BM - 1) / BM;
+  const int NT = (N + BN - 1) / BN;
+  // XCD-aware tile order (see the file comment).
+  int tile;
+  {
+    const int T = MT * NT;
+    const int bid = blockIdx.x;
+    const int x = bid % kXcds;
+    const int per = T / kXcds;
+    const int rem = T - per * kXcds;
+    tile = x * per + min(x, rem) + bid / kXcds;
   }
-  const __bf16* b_src[BCH];
-  int b_stride[BCH], b_row[BCH], b_chunk[BCH];
-#pragma unroll
-  for (int r = 0; r < BCH; ++r) {
-    const int c = tid + r * 256;
-    b_row[r] = c >> 4;      // k within the step
-    b_chunk[r] = c & 15;    // 8-column chunk within the tile
-    const int n = min(n0 + b_chunk[r] * 8, N - 8);
-    int s = 0;
-    while (s + 1 < g.nseg && n >= g.col_start[s + 1]) ++s;
-    b_src[r] = (const __bf16*)g.seg[s].W + (n - g.col_start[s]);
-    b_stride[r] = g.seg[s].width;
-  }
+  const int m0 = (tile / NT) * BM;
+  const int n0 = (tile % NT) * BN;
+  const int nsteps = (g.K + BK - 1) / BK;
+  const bool ktail = (g.K % BK) != 0;  // the last stage reaches past K
 
-  u32x4 areg[ACH], breg[BCH];
-  auto load_step = [&](int k0) {
+  // The tile's columns lie in one segment (segment starts are multiples of BN).
+  const int sg = seg_of(g, n0);
+  const int wstride = seg_field(g, sg, &GemmSeg::width);
+  const int ncol0 = n0 - seg_start(g, sg);  // first tile column within the segment
+  const char* a_tile = (const char*)g.A + (int64_t)m0 * g.K * 2;
+  const char* w_seg = (const char*)seg_ptr(g, sg);
+
+  // DMA sources.  A load r of this wave fills LDS block (wave*AL + r): rows
+  // 8 blk .. +7, lane l -> row 8 blk + l/8, stored chunk l%8, which holds the
+  // source chunk the swizzle maps there.  Rows past M read the last row
+  // (never stored).  W load r fills LDS block (wave*BL + r): 1024 / (2 BN)
+  // rows of BN columns; columns past the segment read its last chunk (never
+  // stored).  Offsets are bytes from the stage's scalar base.
+  unsigned a_voff[AL], w_voff[BL];
+  int a_kc[AL], w_row[BL], w_col[BL];
 #pragma unroll
-    for (int r = 0; r < ACH; ++r) {
-      const int k = min(k0 + a_chunk[r] * 8, g.K - 8) - a_chunk[r] * 8;
-      areg[r] = *(const u32x4*)(a_src[r] + k);
-    }
+  for (int r = 0; r < AL; ++r) {
+    const int row = 8 * (wave * AL + r) + (lane >> 3);
+    a_kc[r] = 8 * a_pos(row, lane & 7);
+    a_voff[r] = (unsigned)((min(m0 + row, g.M - 1) - m0) * g.K + a_kc[r]) * 2u;
+  }
 #pragma unroll
-    for (int r = 0; r < BCH; ++r) {
-      const int k = min(k0 + b_row[r], g.K - 1);
-      breg[r] = *(const u32x4*)(b_src[r] + (int64_t)k * b_stride[r]);
+  for (int r = 0; r < BL; ++r) {
+    const int row = (wave * BL + r) * (1024 / (2 * BN)) + lane / BROW;
+    w_row[r] = row;
+    w_col[r] = min(ncol0 + 8 * b_pos<BN>(row, lane % BROW), wstride - 8);
+    w_voff[r] = (unsigned)(row * wstride + w_col[r]) * 2u;
+  }
+  // LDS byte addresses of the two rings (wave-uniform, computed once).
+  const unsigned as_lds = lds_addr(&As[0][0]);
+  const unsigned bs_lds = lds_addr(&Bs[0][0]);
+  auto issue = [&](int step, int buf) {
+    const int k0 = step * BK;
+    const unsigned a_dst = as_lds + (unsigned)(buf * BM * BK + wave * AL * 512) * 2u;
+    const unsigned b_dst = bs_lds + (unsigned)(buf * BK * BN + wave * BL * 512) * 2u;
+    if (!ktail || k0 + BK <= g.K) {
+      const char* ab = a_tile + k0 * 2;
+      const char* wb = w_seg + (int64_t)k0 * wstride * 2;
+#pragma unroll
+      for (int r = 0; r < AL; ++r) dma16_s(ab, a_voff[r], a_dst + 1024u * r);
+#pragma unroll
+      for (int r = 0; r < BL; ++r) dma16_s(wb, w_voff[r], b_dst + 1024u * r);
+    } else {  // last stage of a K that is not a multiple of 64: clamp per lane
+#pragma unroll
+      for (int r = 0; r < AL; ++r) {
+        const unsigned o = a_voff[r] + 2u * (unsigned)(min(k0 + a_kc[r], g.K - 8) - a_kc[r]);
+        dma16_s(a_tile, o, a_dst + 1024u * r);
+      }
+#pragma unroll
+      for (int r = 0; r < BL; ++r) {
+        const unsigned o = (unsigned)(min(k0 + w_row[r], g.K - 1) * wstride + w_col[r]) * 2u;
+        dma16_s(w_seg, o, b_dst + 1024u * r);
+      }
     }
   };
-  auto store_step = [&](int buf, int k0) {
+
+  // The last stage of a K that is not a multiple of 64 loaded clamped
+  // addresses past K; once it has landed, every lane clears the 16-byte
+  // chunks it loaded there, so those k contribute exact zeros.
+  auto zero_past_k = [&](int step, int buf) {
+    const int k0 = step * BK;
 #pragma unroll
-    for (int r = 0; r < ACH; ++r) {
-      const bool ok = k0 + a_chunk[r] * 8 < g.K;
-      *(u32x4*)&As[buf][a_off(a_row[r], a_chunk[r])] = ok ? areg[r] : u32x4{0, 0, 0, 0};
-    }
+    for (int r = 0; r < AL; ++r)
+      if (k0 + a_kc[r] >= g.K) *(u32x4*)&As[buf][(wave * AL + r) * 512 + 8 * lane] = u32x4{};
 #pragma unroll
-    for (int r = 0; r < BCH; ++r) {
-      const bool ok = k0 + b_row[r] < g.K;
-      *(u32x4*)&Bs[buf][b_off(b_row[r], b_chunk[r])] = ok ? breg[r] : u32x4{0, 0, 0, 0};
-    }
+    for (int r = 0; r < BL; ++r)
+      if (k0 + w_row[r] >= g.K) *(u32x4*)&Bs[buf][(wave * BL + r) * 512 + 8 * lane] = u32x4{};
   };
 
   f32x16 acc[MB][NB];
@@ -132,98 +238,149 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) acc[i][j] = f32x16{};
 
-  // Weight-operand source lane pattern of the transposing read: within each
-  // 16-lane group, lane s addresses row (s / 4) and columns 4 (s % 4) .. +3.
+  // LDS read offsets (elements within a stage), fixed across stages.
+  // Activation operand: row wm*BM/2 + 32i + col, chunk 2ks + grp.  Weight
+  // operand (transposing read): within each 16-lane group, lane s addresses
+  // row (s / 4) and columns 4 (s % 4) .. +3.
+  int x_off[MB][BK / 16];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) {
+    const int row = wm * (BM / 2) + 32 * i + col;
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) x_off[i][ks] = row * BK + 8 * a_pos(row, 2 * ks + grp);
+  }
   const int tr_k = (lane & 15) >> 2;
   const int tr_n = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-
-  const int steps = (g.K + BK - 1) / BK;
-  load_step(0);
-  store_step(0, 0);
-  load_step(BK);
-  for (int t = 0; t < steps; ++t) {
-    const int buf = t & 1;
-    __syncthreads();
-    store_step(buf ^ 1, (t + 1) * BK);
-    load_step((t + 2) * BK);
-    // Keep the loads here: sinking them toward their use (next step) would
-    // leave no compute to hide their latency.
-    __builtin_amdgcn_sched_barrier(0);
-    const __bf16* as = As[buf];
-    const __bf16* bs = Bs[buf];
+  int w_off[NB][BK / 16][2];
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int n = wn * (BN / 2) + 32 * j + tr_n;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[MB], bfr[NB];
+      const int k = 16 * ks + 8 * grp + tr_k;
+      w_off[j][ks][0] = k * BN + 8 * b_pos<BN>(k, n >> 3) + (n & 7);
+      w_off[j][ks][1] = (k + 4) * BN + 8 * b_pos<BN>(k + 4, n >> 3) + (n & 7);
+    }
+  }
+
+  auto compute = [&](const __bf16* as, const __bf16* bs) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
-        af[i] = *(const bf16x8*)&as[a_off(wm * (BM / 2) + 32 * i + col, 2 * ks + grp)];
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      bf16x8 xf[MB], wf[NB];
+#pragma unroll
+      for (int i = 0; i < MB; ++i) xf[i] = *(const bf16x8*)&as[x_off[i][ks]];
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const int k = 16 * ks + 8 * grp + tr_k;
-        const int n = wn * 64 + 32 * j + tr_n;
-        const i16x4 lo = tr_read(&bs[b_off(k, n >> 3) + (n & 7)]);
-        const i16x4 hi = tr_read(&bs[b_off(k + 4, n >> 3) + (n & 7)]);
-        bfr[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        const i16x4 lo = tr_read(&bs[w_off[j][ks][0]]);
+        const i16x4 hi = tr_read(&bs[w_off[j][ks][1]]);
+        wf[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
         for (int j = 0; j < NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], xf[i], acc[i][j], 0, 0, 0);
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nsteps) issue(s, s);
+
+  // The ring index is a compile-time constant in each unrolled copy, so every
+  // LDS address is a per-lane offset plus an immediate.
+  for (int t0 = 0; t0 < nsteps; t0 += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      const int t = t0 + u;
+      if (t < nsteps) {
+        wait_stage<LPS, NS>(min(NS - 2, nsteps - 1 - t));
+        if (ktail && t == nsteps - 1) zero_past_k(t, u);
+        __syncthreads();
+        if (t + NS - 1 < nsteps) issue(t + NS - 1, (u + NS - 1) % NS);
+        compute(As[u], Bs[u]);
+      }
     }
   }
 
-  // acc[i][j][e] = C[m0 + wm*BM/2 + 32i + 8(e/4) + 4grp + e%4][n0 + wn*64 + 32j + col]
+  // acc[i][j][e] = C[m][n], m = m0 + wm*BM/2 + 32i + col,
+  //                         n = n0 + wn*BN/2 + 32j + 8(e/4) + 4grp + e%4.
+  // A 32-column block lies in one segment and one head (segment widths and
+  // head widths are multiples of 32 unless there is a single segment with a
+  // single head), so its destination is fixed per block; N is a multiple of 8.
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int n = n0 + wn * 64 + 32 * j + col;
-    if (n >= N) continue;
-    int s = 0;
-    while (s + 1 < g.nseg && n >= g.col_start[s + 1]) ++s;
-    const GemmSeg& sg = g.seg[s];
-    const int c = n - g.col_start[s];
-    const int head = c / sg.hd;
-    const int dd = c - head * sg.hd;
-    __bf16* dst = (__bf16*)sg.dst + (int64_t)head * sg.rows * sg.hd + dd;
-    const int64_t batch_stride = (int64_t)sg.heads * sg.rows * sg.hd;
+    const int nb = n0 + wn * (BN / 2) + 32 * j;  // wave-uniform
+    if (nb >= N) continue;
+    const int s = seg_of(g, nb);
+    const int rows = seg_field(g, s, &GemmSeg::rows);
+    const int hd = seg_field(g, s, &GemmSeg::hd);
+    const int heads = seg_field(g, s, &GemmSeg::heads);
+    const int c = nb - seg_start(g, s);
+    const int head = heads == 1 ? 0 : c / hd;
+    __bf16* base = (__bf16*)seg_field(g, s, &GemmSeg::dst) + (int64_t)head * rows * hd +
+                   (c - head * hd) + 4 * grp;
+    const int64_t bstride = (int64_t)heads * rows * hd;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      // Rows of this lane: mb + {0,1,2,3, 8..11, 16..19, 24..27}, mb = first row.
-      const int mb = m0 + wm * (BM / 2) + 32 * i + 4 * grp;
-      int bb = mb / sg.rows;
-      int pos = mb - bb * sg.rows;
-      int m = mb;
+      const int m = m0 + wm * (BM / 2) + 32 * i + col;
+      if (m >= g.M) continue;
+      const int bb = m / rows;
+      const int pos = m - bb * rows;
+      __bf16* dst = base + bb * bstride + (int64_t)pos * hd;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int next = mb + 8 * (e >> 2) + (e & 3);
-        while (m < next) {  // advance (bb, pos) to row `next`
-          ++m;
-          if (++pos == sg.rows) { pos = 0; ++bb; }
-        }
-        if (m < g.M) dst[bb * batch_stride + (int64_t)pos * sg.hd] = (__bf16)acc[i][j][e];
+      for (int q = 0; q < 4; ++q) {
+        if (nb + 8 * q >= N) continue;
+        f32x4 v;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+        *(bf16x4*)(dst + 8 * q) = __builtin_convertvector(v, bf16x4);
       }
     }
   }
 }
 
-template <int BM>
+template <int BM, int BN, int NS>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
   const int N = g.col_start[g.nseg];
-  dim3 grid((N + BN - 1) / BN, (g.M + BM - 1) / BM);
+  const int tiles = ((N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
   void* args[] = {(void*)&g};
-  return hipExtLaunchKernel((const void*)gemm_bf16_kernel<BM>, grid, dim3(256), args, 0, s,
-                            ev.start, ev.stop, 0);
+  return hipExtLaunchKernel((const void*)gemm_bf16_kernel<BM, BN, NS>, dim3(tiles), dim3(256), args,
+                            0, s, ev.start, ev.stop, 0);
+}
+
+// Every segment must start on a multiple of the tile width (a tile's columns
+// lie in one segment) and N must be a multiple of 8.
+bool tiles_fit(const GemmArgs& g, int bn) {
+  for (int s = 0; s < g.nseg; ++s)
+    if (g.col_start[s] % bn != 0) return false;
+  return g.col_start[g.nseg] % 8 == 0 && g.K % 8 == 0;
 }
 
 }  // namespace
 
+hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, LaunchEvents ev) {
+  static const int kBN[] = {128, 128, 128, 128, 128, 64, 64, 64, 64};
+  if (cfg < 0 || cfg > 8 || !tiles_fit(g, kBN[cfg])) return hipErrorInvalidValue;
+  switch (cfg) {
+    case 0: return launch_tile<128, 128, 2>(g, s, ev);
+    case 1: return launch_tile<128, 128, 3>(g, s, ev);
+    case 2: return launch_tile<64, 128, 2>(g, s, ev);
+    case 3: return launch_tile<64, 128, 3>(g, s, ev);
+    case 4: return launch_tile<64, 128, 4>(g, s, ev);
+    case 5: return launch_tile<128, 64, 3>(g, s, ev);
+    case 6: return launch_tile<64, 64, 3>(g, s, ev);
+    case 7: return launch_tile<64, 64, 4>(g, s, ev);
+    default: return launch_tile<128, 64, 4>(g, s, ev);
+  }
+}
+
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
   const int N = g.col_start[g.nseg];
-  // 128-row tiles when they still give every compute unit two workgroups,
-  // otherwise 64-row tiles for more parallelism.
-  const long big = (long)((N + BN - 1) / BN) * ((g.M + 127) / 128);
-  if (big >= 512) return launch_tile<128>(g, s, ev);
-  return launch_tile<64>(g, s, ev);
+  if (!tiles_fit(g, 128)) return launch_gemm_bf16_cfg(g, 6, s, ev);
+  const long big = (long)((N + 127) / 128) * ((g.M + 127) / 128);
+  if (big >= 512) return launch_gemm_bf16_cfg(g, 1, s, ev);
+  return launch_gemm_bf16_cfg(g, 3, s, ev);
 }
 
 }  // namespace mha

@@ -57,7 +57,11 @@ struct LaunchEvents {
 };
 
 hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
+// One fixed attention configuration (index into the instantiated set); for sweeps.
+hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev = {});
+// One fixed tile configuration (index into the instantiated set); for sweeps.
+hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, LaunchEvents ev = {});
 
 }  // namespace mha

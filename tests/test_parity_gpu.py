@@ -281,12 +281,16 @@ def test_deterministic_and_in_bounds(dev):
 
 def test_mha_small_shapes(dev):
     """The whole block on small odd shapes: h = 1, odd batch, ragged rows,
-    cross-attention without padding, padding with causal self-attention."""
+    cross-attention without padding, padding with causal self-attention, and
+    model widths that are not a multiple of the GEMM's 64-wide K stage or
+    128-wide column tile (d_model = 200, 72)."""
     cases = [
         dict(B=1, n_q=1, n_k=1, d_model=64, h=1, mask=0, self_attn=True),
         dict(B=3, n_q=37, n_k=37, d_model=128, h=2, mask=1, self_attn=True),
         dict(B=2, n_q=50, n_k=130, d_model=192, h=3, mask=0, self_attn=False),
         dict(B=2, n_q=70, n_k=70, d_model=256, h=4, mask=3, self_attn=True, key_len_range=(1, 70)),
+        dict(B=3, n_q=45, n_k=45, d_model=200, h=3, mask=1, self_attn=True),
+        dict(B=2, n_q=33, n_k=66, d_model=72, h=2, mask=2, self_attn=False, key_len_range=(1, 66)),
     ]
     for c in cases:
         w = WORKLOADS["cross_padded_big"].replace(
