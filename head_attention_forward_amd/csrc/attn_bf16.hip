@@ -233,64 +233,46 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
     for (int s = 0; s < 4; ++s) qf[s] = src[2 * s + g];
   }
 
-  // Weights of one tile for reference value m: p = 2^(s c2 - m c2), rounded
-  // to bf16 (the P.V operand); returns this lane's sum of the rounded weights.
-  auto weights = [&](const f32x16& s0, const f32x16& s1, bf16x8 (&p)[4]) {
+  // The softmax bookkeeping runs per 32-key half tile: half h of a tile is
+  // the scores sh (keys k0 + 32h + 8(i/4) + 4g + i%4 for sh[i]), and its
+  // weights are the P.V operands p[2h], p[2h+1].  Working in halves lets the
+  // vector ALU work on one half while the matrix unit multiplies the other.
+  //
+  // Weights for reference value m: 2^(s c2 - m c2), rounded to bf16; returns
+  // this lane's sum of the rounded weights.
+  auto weights = [&](const f32x16& sh, bf16x8& pa, bf16x8& pb) {
     const float mc = m * c2;
     const bf16x2 one = {(__bf16)1.0f, (__bf16)1.0f};
     float lt = 0.f;
 #pragma unroll
-    for (int hf = 0; hf < 4; ++hf) {
+    for (int hf = 0; hf < 2; ++hf) {
       f32x8 w;
 #pragma unroll
-      for (int r = 0; r < 8; ++r)
-        w[r] = fast_exp2(fmaf(hf < 2 ? s0[8 * hf + r] : s1[8 * (hf - 2) + r], c2, -mc));
-      const bf16x8 pb = __builtin_convertvector(w, bf16x8);
-      p[hf] = pb;
+      for (int r = 0; r < 8; ++r) w[r] = fast_exp2(fmaf(sh[8 * hf + r], c2, -mc));
+      const bf16x8 pw = __builtin_convertvector(w, bf16x8);
+      if (hf == 0) pa = pw;
+      else pb = pw;
 #pragma unroll
       for (int r = 0; r < 8; r += 2)
-        lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pb[r], pb[r + 1]}, one, lt, false);
+        lt = __builtin_amdgcn_fdot2_f32_bf16(bf16x2{pw[r], pw[r + 1]}, one, lt, false);
     }
     return lt;
   };
-
-  auto step = [&](int t, const __bf16* ks, const __bf16* vs) {
-    const int k0 = t * KT;
-    if (k0 >= wv_keys) return;  // no visible key for any query of this wave
-    f32x16 s0 = {}, s1 = {};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const bf16x8 ka = *(const bf16x8*)&ks[kx[kk]];
-      const bf16x8 kb = *(const bf16x8*)&ks[kx[kk] + 32 * D];
-      s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qf[kk], s0, 0, 0, 0);
-      s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb, qf[kk], s1, 0, 0, 0);
-    }
-    // s0[i] is the score of key k0 + 8(i/4) + 4g + i%4, s1[i] of that key + 32.
-    if (k0 + KT > lim) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int key = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
-        if (key >= lim) s0[i] = -INFINITY;
-        if (key + 32 >= lim) s1[i] = -INFINITY;
-      }
-    }
-    // The weights are first taken with the current m.  If some weight of a
-    // row came out above 2^8 in total (or m is still the sentinel), that row's m
-    // moves to the exact maximum of everything it has seen, its acc and l
-    // are rescaled, and the tile's weights are taken again.
-    bf16x8 p[4];
-    float lt = weights(s0, s1, p);
+  // The weights are first taken with the current m.  If some weight of a
+  // row came out above 2^8 in total (or m is still the sentinel), that
+  // row's m moves to the exact maximum of everything it has seen, its acc
+  // and l are rescaled, and the half's weights are taken again.
+  auto half = [&](const f32x16& sh, bf16x8& pa, bf16x8& pb) {
+    float lt = weights(sh, pa, pb);
     unsigned need = lt > kMaxTileSum;  // lt is finite or +inf, never NaN
     {
       const auto r = __builtin_amdgcn_permlane32_swap(need, need, false, false);
       need = r[0] | r[1];  // both halves of a query row decide together
     }
     if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      float mt = fmaxf(s0[0], s0[1]);
+      float mt = fmaxf(sh[0], sh[1]);
 #pragma unroll
-      for (int i = 2; i < 16; i += 2) mt = fmaxf(mt, fmaxf(s0[i], s0[i + 1]));
-#pragma unroll
-      for (int i = 0; i < 16; i += 2) mt = fmaxf(mt, fmaxf(s1[i], s1[i + 1]));
+      for (int i = 2; i < 16; i += 2) mt = fmaxf(mt, fmaxf(sh[i], sh[i + 1]));
       mt = max_halves(mt);
       if (need) {
         const float m_new = fmaxf(m, mt);
@@ -300,20 +282,60 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
         o0 *= alpha;
         o1 *= alpha;
       }
-      lt = weights(s0, s1, p);
+      lt = weights(sh, pa, pb);
     }
     l += lt;
+  };
+  // O^T += V^T P^T over the 32 keys of half h (key blocks 2h, 2h+1).
+  auto pv_half = [&](const __bf16* vs, int h, const bf16x8& pa, const bf16x8& pb) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
+    for (int j = 0; j < 2; ++j) {
+      const int kk = 2 * h + j;
 #pragma unroll
       for (int db = 0; db < 2; ++db) {
         const i16x4 lo = tr_read(&vs[vx[db] + 16 * kk * D]);
         const i16x4 hi = tr_read(&vs[vx[db] + (16 * kk + 8) * D]);
         const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        if (db == 0) o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kk], o0, 0, 0, 0);
-        else o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, p[kk], o1, 0, 0, 0);
+        const bf16x8& pk = j == 0 ? pa : pb;
+        if (db == 0) o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk, o0, 0, 0, 0);
+        else o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pk, o1, 0, 0, 0);
       }
     }
+  };
+
+  auto step = [&](int t, const __bf16* ks, const __bf16* vs) {
+    const int k0 = t * KT;
+    if (k0 >= wv_keys) return;  // no visible key for any query of this wave
+    // S^T = K Q^T, first-half chain leading so that its softmax can start
+    // while the second half's products are still running.
+    f32x16 s0 = {}, s1 = {};
+    bf16x8 ka[4], kb[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      ka[kk] = *(const bf16x8*)&ks[kx[kk]];
+      kb[kk] = *(const bf16x8*)&ks[kx[kk] + 32 * D];
+    }
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[0], s0, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[1], qf[1], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[0], qf[0], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[2], qf[2], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[1], qf[1], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[3], qf[3], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[2], qf[2], s1, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[3], qf[3], s1, 0, 0, 0);
+    if (k0 + KT > lim) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key >= lim) s0[i] = -INFINITY;
+        if (key + 32 >= lim) s1[i] = -INFINITY;
+      }
+    }
+    bf16x8 p[4];
+    half(s0, p[0], p[1]);
+    pv_half(vs, 0, p[0], p[1]);
+    half(s1, p[2], p[3]);
+    pv_half(vs, 1, p[2], p[3]);
   };
 
   // The ring index is a compile-time constant in each unrolled copy.
