@@ -57,35 +57,49 @@ def parse_args():
 
 # ----------------------------------------------------------------------------- accounting
 
-def kernel_plan(w):
+def mha_launches(w):
+    """Kernels one multi-head step launches, as the library plans them."""
+    from head_attention_forward_amd import _binding as bnd
+    n = bnd.lib().mha_forward_launches(w.n_q, w.n_k, w.d_model, 1 if w.self_attn else 0)
+    if n < 0:
+        raise RuntimeError(f"mha_forward_launches failed with status {n}")
+    return n
+
+
+def kernel_plan(w, n_launches=None):
     """Launch order of one step with each kernel's algorithmic flops and bytes
-    (bytes: every input element read once, every output written once)."""
+    (bytes: every input element read once, every output written once).  The
+    attention's own counts (attention_accounting) are added to the kernel
+    named "attention", or to the fused projection + attention kernel."""
     e = 2 if w.dtype == "bf16" else 4
     B, h, nq, nk, dk, dv = w.B, w.h, w.n_q, w.n_k, w.d_k, w.d_v
-    # visible (query, key) pairs per (batch, head)
-    if w.mask & 1:
-        pairs_bh = [nq * (nq + 1) / 2.0] * B
-    elif w.mask & 2:
-        pairs_bh = None
-    else:
-        pairs_bh = [float(nq * nk)] * B
     plan = []
 
     def gemm(name, M, K, N):
         plan.append(dict(name=name, flops=2.0 * M * K * N, bytes=float(e * (M * K + K * N + M * N)),
-                         peak_kind="mfma"))
+                         peak_kind="mfma", has_attention=False))
 
-    if w.kind == "mha":
-        if w.self_attn:
+    if w.kind == "sdpa":
+        plan.append(dict(name="attention", flops=0.0, bytes=0.0,
+                         peak_kind="mfma" if w.dtype == "bf16" else "fp32", has_attention=True))
+        return plan, None
+    n = mha_launches(w) if n_launches is None else n_launches
+    if n == 2:
+        dm = w.d_model
+        flops = 2.0 * B * nq * dm * h * dk + 2.0 * B * nk * dm * h * (dk + dv)
+        x_bytes = B * nq * dm + (0 if w.self_attn else B * nk * dm)
+        byts = float(e * (x_bytes + dm * h * (2 * dk + dv) + B * nq * h * dv))
+        plan.append(dict(name="qkv_projection_attention", flops=flops, bytes=byts,
+                         peak_kind="mfma", has_attention=True))
+    else:
+        if n == 3:
             gemm("qkv_projection_gemm", B * nq, w.d_model, h * (2 * dk + dv))
         else:
             gemm("q_projection_gemm", B * nq, w.d_model, h * dk)
             gemm("kv_projection_gemm", B * nk, w.d_model, h * (dk + dv))
-    plan.append(dict(name="attention", flops=None, bytes=None,
-                     peak_kind="mfma" if w.dtype == "bf16" else "fp32"))
-    if w.kind == "mha":
-        gemm("output_projection_gemm", B * nq, h * dv, w.d_model)
-    return plan, pairs_bh
+        plan.append(dict(name="attention", flops=0.0, bytes=0.0, peak_kind="mfma", has_attention=True))
+    gemm("output_projection_gemm", B * nq, h * dv, w.d_model)
+    return plan, None
 
 
 def attention_accounting(w, key_lengths):
@@ -152,7 +166,7 @@ class Step:
                                   *[P(t.data_ptr()) for t in Ws], P(Y.data_ptr()),
                                   w.B, w.n_q, w.n_k, w.d_model, w.h, w.d_k, w.d_v, w.mask, self.kl,
                                   bnd.DTYPE_BF16, P(ws.data_ptr()), ws.numel()))
-        self.n_launches = 1 if w.kind == "sdpa" else (3 if w.self_attn else 4)
+        self.n_launches = 1 if w.kind == "sdpa" else mha_launches(w)
 
     def output(self, i):
         return self.keep[i][3]
@@ -397,15 +411,20 @@ def main():
         step.run_timed(k % sets, sp, pool.ptr(2 * nl * k), 2 * nl)
     torch.cuda.synchronize()
 
-    plan, _ = kernel_plan(w)
+    plan, _ = kernel_plan(w, nl)
     a_flops, a_bytes = attention_accounting(w, x["key_lengths"])
     kernels = []
     for j, kp in enumerate(plan):
         durs = [pool.elapsed_ms(2 * (nl * k + j), 2 * (nl * k + j) + 1) for k in range(K)]
         avg_us = 1e3 * float(np.mean(durs))
-        flops = a_flops if kp["name"] == "attention" else kp["flops"]
-        byts = a_bytes if kp["name"] == "attention" else kp["bytes"]
-        kernels.append(dict(name=kp["name"], avg_us=round(avg_us, 3),
+        flops, byts = kp["flops"], kp["bytes"]
+        if kp["has_attention"]:
+            flops += a_flops
+            # a standalone attention kernel moves Q, K, V and O through HBM;
+            # the fused kernel's bytes are its own inputs and output
+            if kp["name"] == "attention":
+                byts += a_bytes
+        kernels.append(dict(name=kp["name"], has_attention=kp["has_attention"], avg_us=round(avg_us, 3),
                             min_us=round(1e3 * float(np.min(durs)), 3),
                             tflops=round(flops / (avg_us * 1e-6) / 1e12, 2),
                             gbs=round(byts / (avg_us * 1e-6) / 1e9, 1),
@@ -429,7 +448,7 @@ def main():
 
     nominal = w.nominal_attention_flops()
     value = nominal / (ms_step * 1e-3) / 1e12
-    att = next(k for k in kernels if k["name"] == "attention")
+    att = next(k for k in kernels if k["has_attention"])
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -474,9 +493,12 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "f32",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/d_model) weights)",
         "config": cfg,
-        "attention_kernel": dict(avg_us=att["avg_us"], nominal_tflops=round(nominal / (att["avg_us"] * 1e-6) / 1e12, 2),
-                                 algorithmic_tflops=att["tflops"], gbs=att["gbs"]),
-        "kernels": [{k: v for k, v in kk.items() if k not in ("peak_kind",)} for kk in kernels],
+        # the kernel that runs the attention (fused with the input
+        # projections for short sequences); kernel_tflops counts all its flops
+        "attention_kernel": dict(kernel=att["name"], avg_us=att["avg_us"],
+                                 nominal_attention_tflops=round(nominal / (att["avg_us"] * 1e-6) / 1e12, 2),
+                                 kernel_tflops=att["tflops"], gbs=att["gbs"]),
+        "kernels": [{k: v for k, v in kk.items() if k not in ("peak_kind", "has_attention")} for kk in kernels],
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": parity,

@@ -40,6 +40,7 @@ _SIG = {
     "mha_attend": (_I, [_I, _I, _I, _I, _I, _I, _I, _P, _I, _P, ctypes.c_size_t, _P]),
     "mha_project_out": (_I, [_P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
     "mha_status_str": (ctypes.c_char_p, [_I]),
+    "mha_forward_launches": (_I, [_I, _I, _I, _I]),
     "sdpa_forward_timed": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _I,
                                 _P, _P, _I, _P]),
     "mha_forward_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _I,

@@ -28,7 +28,8 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 # contract (finite inputs; masked scores are -inf), so its float max needs no
 # NaN canonicalization: this lets v_max3_f32 take raw scores.  Host-side
 # argument checks (which do test for NaN) live in other files.
-EXTRA = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
+EXTRA = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+         "proj_attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _hipcc():

@@ -33,18 +33,12 @@
 // row-major tile order (whole rows of tiles), i.e. each XCD's L2 streams its
 // own band of activation rows and the (small) weight matrix, instead of
 // every XCD reading every activation row.
-#include "kernels.h"
+#include "device.h"
 
 namespace mha {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+using namespace dev;
 
 constexpr int BK = 64;
 constexpr int kXcds = 8;
@@ -57,17 +51,6 @@ template <int BN>
 __device__ __forceinline__ int b_pos(int k, int chunk) {
   if constexpr (BN == 128) return chunk ^ ((k & 3) << 2);
   else return chunk ^ (((k >> 1) & 1) << 2);
-}
-
-__device__ __forceinline__ i16x4 tr_read(const __bf16* p) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
-}
-
-// s_waitcnt vmcnt(N) (gfx9 encoding; expcnt and lgkmcnt left unconstrained)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
 // Waits until at most `later` stages issued after the current one are still
@@ -97,29 +80,6 @@ __device__ __forceinline__ const void* seg_ptr(const GemmArgs& g, int s) {
 }
 __device__ __forceinline__ int seg_start(const GemmArgs& g, int s) {
   return s == 0 ? g.col_start[0] : (s == 1 ? g.col_start[1] : g.col_start[2]);
-}
-
-// 16-byte global -> LDS copy per lane from a wave-uniform 64-bit base plus a
-// per-lane 32-bit byte offset (the saddr form: no vector address arithmetic);
-// lane l writes LDS byte address lds + 16 l.  Inline assembly, so that the
-// compiler does not wait for it before every LDS read; the kernel waits for
-// it explicitly (vmcnt) before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsigned lds) {
-  // The base is wave-uniform; readfirstlane pins it to SGPRs for the saddr operand.
-  const unsigned long long p = (unsigned long long)(size_t)sbase;
-  // (readfirstlane returns int: widen through unsigned, never sign-extend.)
-  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
-  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)p);
-  const unsigned long long sp = ((unsigned long long)hi << 32) | (unsigned long long)lo;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
-               :
-               : "s"(lds), "v"(voff), "s"((const void*)(size_t)sp)
-               : "memory", "m0");
-}
-
-__device__ __forceinline__ unsigned lds_addr(const void* p) {
-  return __builtin_amdgcn_readfirstlane(
-      (unsigned)(size_t)(const __attribute__((address_space(3))) char*)p);
 }
 
 template <int BM, int BN, int NS>

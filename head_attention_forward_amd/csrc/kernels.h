@@ -49,6 +49,23 @@ struct GemmArgs {
   int col_start[4];   // prefix sums of segment widths; col_start[nseg] = N
 };
 
+// Fused input projections + attention for short sequences (n_q, n_k <= 128,
+// d_model a multiple of 64, head size 64): one workgroup per (batch, head)
+// computes that head's Q, K, V tiles and its attention output.
+struct ProjAttnArgs {
+  const void* Xq;     // [B][n_q][d_model]
+  const void* Xkv;    // [B][n_k][d_model] (may equal Xq)
+  const void* Wq;     // [d_model][h*64]
+  const void* Wk;
+  const void* Wv;
+  void* O;            // concatenated heads [B][n_q][h*64]
+  int B, h, n_q, n_k, d_model;
+  float scale;
+  int causal;
+  int padded;
+  int32_t key_len[MHA_MAX_PADDED_BATCH];
+};
+
 // Launch-time events: when `start`/`stop` are non-null they are recorded at
 // the start and at the end of this kernel's execution (hipExtLaunchKernel).
 struct LaunchEvents {
@@ -61,6 +78,8 @@ hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents e
 hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev = {});
+bool proj_attn_supported(int n_q, int n_k, int d_model);
+hipError_t launch_proj_attn_bf16(const ProjAttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 // One fixed tile configuration (index into the instantiated set); for sweeps.
 hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, LaunchEvents ev = {});
 

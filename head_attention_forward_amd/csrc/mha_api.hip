@@ -110,9 +110,15 @@ struct Timer {
 
 LaunchEvents next_events(Timer* t) { return t ? t->next() : LaunchEvents{}; }
 
-// Launches an mha_forward call makes: one fused projection for
-// self-attention, two otherwise, then attention and the output projection.
-int mha_launch_count(const void* X_q, const void* X_kv, int n_q, int n_k) {
+// Short sequences (both <= 128 rows) with d_model a multiple of 64 take the
+// fused projection + attention kernel, then the output projection.
+bool use_fused(int n_q, int n_k, int d_model) { return proj_attn_supported(n_q, n_k, d_model); }
+
+// Launches an mha_forward call makes: fused path 2; otherwise one stacked
+// projection for self-attention (two for cross-attention), then attention
+// and the output projection.
+int mha_launch_count(const void* X_q, const void* X_kv, int n_q, int n_k, int d_model) {
+  if (use_fused(n_q, n_k, d_model)) return 2;
   return (X_q == X_kv && n_q == n_k) ? 3 : 4;
 }
 
@@ -228,6 +234,12 @@ const char* mha_status_str(int status) {
   }
 }
 
+int mha_forward_launches(int n_q, int n_k, int d_model, int self_attention) {
+  if (n_q <= 0 || n_k <= 0 || d_model <= 0) return MHA_ERR_DIM;
+  if (use_fused(n_q, n_k, d_model)) return 2;
+  return (self_attention && n_q == n_k) ? 3 : 4;
+}
+
 size_t mha_workspace_bytes(int B, int n_q, int n_k, int h, int d_k, int d_v, int dtype) {
   if (B <= 0 || n_q <= 0 || n_k <= 0 || h <= 0 || d_k <= 0 || d_v <= 0) return 0;
   if (dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_F32) return 0;
@@ -336,9 +348,31 @@ static int mha_impl(const void* X_q, const void* X_kv, const void* Wq, const voi
       !aligned16(Wv) || !aligned16(Wo) || !aligned16(Y))
     return MHA_ERR_UNSUPPORTED;
   const Workspace w = carve(workspace, B, n_q, n_k, h, d_k, d_v, dtype);
-  st = do_project_in(X_q, X_kv, Wq, Wk, Wv, B, n_q, n_k, d_model, h, d_k, d_v, w, stream, tm);
-  if (st != MHA_OK) return st;
-  st = do_attend(B, n_q, n_k, h, d_k, d_v, mask_kind, key_lengths, w, stream, tm);
+  if (use_fused(n_q, n_k, d_model)) {
+    ProjAttnArgs pa;
+    memset(&pa, 0, sizeof(pa));
+    pa.Xq = X_q;
+    pa.Xkv = X_kv;
+    pa.Wq = Wq;
+    pa.Wk = Wk;
+    pa.Wv = Wv;
+    pa.O = w.O;
+    pa.B = B;
+    pa.h = h;
+    pa.n_q = n_q;
+    pa.n_k = n_k;
+    pa.d_model = d_model;
+    pa.scale = 1.0f / sqrtf((float)d_k);
+    pa.causal = (mask_kind & MHA_MASK_CAUSAL) ? 1 : 0;
+    pa.padded = (mask_kind & MHA_MASK_KEY_PADDING) ? 1 : 0;
+    if (pa.padded)
+      for (int b = 0; b < B; ++b) pa.key_len[b] = key_lengths[b];
+    st = launch_status(launch_proj_attn_bf16(pa, stream, next_events(tm)));
+  } else {
+    st = do_project_in(X_q, X_kv, Wq, Wk, Wv, B, n_q, n_k, d_model, h, d_k, d_v, w, stream, tm);
+    if (st != MHA_OK) return st;
+    st = do_attend(B, n_q, n_k, h, d_k, d_v, mask_kind, key_lengths, w, stream, tm);
+  }
   if (st != MHA_OK) return st;
   return do_project_out(Wo, Y, B, n_q, d_model, h, d_v, w, stream, tm);
 }
@@ -357,7 +391,7 @@ int mha_forward_timed(const void* X_q, const void* X_kv, const void* Wq, const v
                       const int32_t* key_lengths, int dtype, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
                       int capacity, int* n_launches) {
-  const int need = 2 * mha_launch_count(X_q, X_kv, n_q, n_k);
+  const int need = 2 * mha_launch_count(X_q, X_kv, n_q, n_k, d_model);
   if (events == nullptr || capacity < need) return MHA_ERR_EVENTS;
   for (int i = 0; i < need; ++i)
     if (events[i] == nullptr) return MHA_ERR_EVENTS;

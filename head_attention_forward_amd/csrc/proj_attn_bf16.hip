@@ -1,0 +1,230 @@
+// Fused input projections and attention for short sequences, bf16 in /
+// bf16 out, fp32 accumulation, head size 64, for gfx950.
+//
+// One workgroup per (batch b, head i) computes, for its head only,
+//   Q_i = X_q,b W_i^Q,  K_i = X_kv,b W_i^K,  V_i = X_kv,b W_i^V
+// (devpress.csdn.net "【深度学习】Transformer", section 2.1, equations
+// (2.1)-(2.3) and section 2.2; hex4c59.cc "读懂 Attention Is All You Need",
+// sections "Q、K、V 是三种计算角色" and "多头注意力让一次读取有多组投影":
+// head i owns column block i of the stacked projections), keeps the three
+// tiles in LDS and then computes head_i = softmax(Q_i K_i^T / sqrt(d_k) + M) V_i
+// with the same per-wave attention as the standalone attention kernel
+// (wave_attention.h), writing head_i into its column block of the
+// concatenated output.  Q, K and V never travel through HBM.
+//
+// The projection is the same computation as the standalone projection GEMM
+// (the same bf16 MFMA 32x32x16 products in the same k order with the weight
+// fragment as first operand, rounded to bf16 the same way), so both paths
+// produce identical intermediates and outputs.
+//
+// Limits: n_q, n_k <= 128 (one 128-row tile each), d_model a multiple of 64.
+//
+// Work decomposition (8 waves): the projection output [128 rows x 192
+// columns] (Q | K | V, 64 columns each) is 4 x 6 MFMA tiles of 32 x 32;
+// wave w computes row block w & 3 and column blocks 3 (w >> 2) .. +2.  The
+// activation rows and the three 64-column weight slices stream in 64-wide k
+// stages through an LDS ring (global_load_lds_dwordx4, NS stages, NS-1
+// ahead).  Afterwards the ring is reused for the bf16 Q, K, V tiles, and
+// waves 0-3 run the attention of queries 32w .. 32w+31 over them.
+#include "wave_attention.h"
+
+namespace mha {
+namespace {
+
+using namespace dev;
+
+constexpr int ROWS = 128;  // rows of the projection tile (>= n_q, n_k)
+constexpr int BKP = 64;    // k per stage
+
+// Activation tile [128][64]: 128-byte rows; chunk c of row m at c ^ ((m >> 1) & 7).
+__device__ __forceinline__ int x_pos(int m, int chunk) { return chunk ^ ((m >> 1) & 7); }
+// Weight tile [64][64]: 128-byte rows; chunk c of row k at c ^ (((k >> 1) & 1) << 2).
+__device__ __forceinline__ int w_pos(int k, int chunk) { return chunk ^ (((k >> 1) & 1) << 2); }
+
+template <bool CROSS, int NS, int LPS>
+__device__ __forceinline__ void wait_stage(int later) {
+  if constexpr (NS >= 3) {
+    if (later >= 1) { wait_vmcnt<LPS>(); return; }
+  }
+  wait_vmcnt<0>();
+}
+
+template <bool CROSS, int NS>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void proj_attn_bf16_kernel(const ProjAttnArgs a) {
+  constexpr int XT = ROWS * BKP;               // elements of one activation tile
+  constexpr int WT = BKP * D;                  // elements of one weight tile
+  constexpr int NX = CROSS ? 2 : 1;            // activation tiles per stage
+  constexpr int STAGE = NX * XT + 3 * WT;      // elements per stage
+  constexpr int XL = XT * 2 / 1024 / 8;        // 1 KB activation loads per wave and tile (2)
+  constexpr int WL = 3 * WT * 2 / 1024 / 8;    // 1 KB weight loads per wave and stage (3)
+  constexpr int LPS = NX * XL + WL;
+  static_assert(NS * STAGE >= 3 * ROWS * D, "ring must hold the Q, K, V tiles");
+
+  __shared__ __attribute__((aligned(1024))) __bf16 ring[NS * STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int grp = lane >> 5;
+
+  const int bh = blockIdx.x;
+  const int b = __builtin_amdgcn_readfirstlane(bh / a.h);
+  const int hh = bh - b * a.h;
+  const int dm = a.d_model;
+  const int ldw = a.h * D;  // row stride of the stacked weights
+  const int nsteps = dm / BKP;
+
+  const char* xq = (const char*)a.Xq + (int64_t)b * a.n_q * dm * 2;
+  const char* xkv = (const char*)a.Xkv + (int64_t)b * a.n_k * dm * 2;
+
+  // DMA sources.  Activation load r of this wave fills block 2 wave + r of
+  // a tile (rows 8 blk .. +7); weight load r fills block 3 wave + r of the
+  // 24 weight blocks (block j: matrix j / 8, rows 8 (j % 8) .. +7).  Rows
+  // past n read the last row (their results are never used).  Byte offsets
+  // from the stage's scalar base.
+  unsigned xq_off[XL], xkv_off[XL], w_off[WL];
+  int w_mat[WL];
+#pragma unroll
+  for (int r = 0; r < XL; ++r) {
+    const int row = 8 * (XL * wave + r) + (lane >> 3);
+    const int c = x_pos(row, lane & 7);
+    xq_off[r] = (unsigned)(min(row, a.n_q - 1) * dm + 8 * c) * 2u;
+    xkv_off[r] = (unsigned)(min(row, a.n_k - 1) * dm + 8 * c) * 2u;
+  }
+#pragma unroll
+  for (int r = 0; r < WL; ++r) {
+    const int j = WL * wave + r;
+    const int row = 8 * (j & 7) + (lane >> 3);
+    const int c = w_pos(row, lane & 7);
+    w_mat[r] = j >> 3;
+    w_off[r] = (unsigned)(row * ldw + hh * D + 8 * c) * 2u;
+  }
+  const unsigned ring_lds = lds_addr(&ring[0]);
+  auto issue = [&](int step, int buf) {
+    const int k0 = step * BKP;
+    const unsigned base = ring_lds + (unsigned)(buf * STAGE) * 2u;
+#pragma unroll
+    for (int r = 0; r < XL; ++r)
+      dma16_s(xq + k0 * 2, xq_off[r], base + (unsigned)((XL * wave + r) * 1024));
+    if constexpr (CROSS) {
+#pragma unroll
+      for (int r = 0; r < XL; ++r)
+        dma16_s(xkv + k0 * 2, xkv_off[r], base + (unsigned)(XT * 2 + (XL * wave + r) * 1024));
+    }
+#pragma unroll
+    for (int r = 0; r < WL; ++r) {
+      const void* W = w_mat[r] == 0 ? a.Wq : (w_mat[r] == 1 ? a.Wk : a.Wv);
+      dma16_s((const char*)W + (int64_t)k0 * ldw * 2, w_off[r],
+              base + (unsigned)(NX * XT * 2 + (WL * wave + r) * 1024));
+    }
+  };
+
+  // This wave's three 32 x 32 output tiles: rows 32 rb .. +31, column
+  // blocks cb0 .. cb0 + 2 of (Q0 Q1 K0 K1 V0 V1).
+  const int rb = wave & 3;
+  const int cb0 = 3 * (wave >> 2);
+  f32x16 acc[3];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) acc[c] = f32x16{};
+  const int xrow = 32 * rb + col;
+  const int tr_k = (lane & 15) >> 2;
+  const int tr_n = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  auto compute = [&](const __bf16* st) {
+    const __bf16* xs_q = st;
+    const __bf16* xs_kv = CROSS ? st + XT : st;
+#pragma unroll
+    for (int ks = 0; ks < BKP / 16; ++ks) {
+      const int xo = xrow * BKP + 8 * x_pos(xrow, 2 * ks + grp);
+      const bf16x8 fq = *(const bf16x8*)&xs_q[xo];
+      const bf16x8 fkv = CROSS ? *(const bf16x8*)&xs_kv[xo] : fq;
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        const int cb = cb0 + c;  // wave-uniform
+        const __bf16* ws = st + NX * XT + (cb >> 1) * WT;
+        const int k = 16 * ks + 8 * grp + tr_k;
+        const int n = 32 * (cb & 1) + tr_n;
+        const i16x4 lo = tr_read(&ws[k * D + 8 * w_pos(k, n >> 3) + (n & 7)]);
+        const i16x4 hi = tr_read(&ws[(k + 4) * D + 8 * w_pos(k + 4, n >> 3) + (n & 7)]);
+        const bf16x8 wf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        acc[c] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf, cb < 2 ? fq : fkv, acc[c], 0, 0, 0);
+      }
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nsteps) issue(s, s);
+  for (int t = 0; t < nsteps; ++t) {
+    wait_stage<CROSS, NS, LPS>(min(NS - 2, nsteps - 1 - t));
+    __syncthreads();
+    if (t + NS - 1 < nsteps) issue(t + NS - 1, (t + NS - 1) % NS);
+    compute(&ring[(t % NS) * STAGE]);
+  }
+  wait_vmcnt<0>();
+  __syncthreads();  // every wave is done with the ring
+
+  // Q, K, V tiles (bf16, rounded as the projection GEMM rounds) into the
+  // ring: Q and K in the k_off layout, V in the v_off layout.
+  __bf16* Qs = &ring[0];
+  __bf16* Ks = &ring[ROWS * D];
+  __bf16* Vs = &ring[2 * ROWS * D];
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    const int cb = cb0 + c;
+    const int mat = cb >> 1;
+    __bf16* dst = mat == 0 ? Qs : (mat == 1 ? Ks : Vs);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int n = 32 * (cb & 1) + 8 * q + 4 * grp;  // 4 consecutive columns
+      const int off = (mat == 2 ? v_off(xrow, n >> 3) : k_off(xrow, n >> 3)) + (n & 7);
+      f32x4 v;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) v[r] = acc[c][4 * q + r];
+      *(bf16x4*)&dst[off] = __builtin_convertvector(v, bf16x4);
+    }
+  }
+  __syncthreads();
+
+  if (wave >= 4) return;  // n_q <= 128: four query blocks
+  const int qw0 = 32 * wave;
+  if (qw0 >= a.n_q) return;
+  const int my_q = qw0 + col;
+  int L = a.n_k;
+  if (a.padded) L = min(L, a.key_len[b]);
+  const int lim = a.causal ? min(L, my_q + 1) : L;
+  const int wv_last = min(qw0 + 32, a.n_q) - 1;
+  const int wv_keys = __builtin_amdgcn_readfirstlane(a.causal ? min(L, wv_last + 1) : L);
+  WaveAttention wa;
+  wa.init(lane, a.scale);
+  wa.load_q_lds(Qs, min(my_q, a.n_q - 1));
+#pragma unroll
+  for (int t = 0; t < ROWS / KT; ++t)
+    if (t * KT < wv_keys) wa.tile(Ks + t * KT * D, Vs + t * KT * D, t * KT, lim);
+  const float inv = wa.inv_sum();
+  if (my_q < a.n_q)
+    wa.store((__bf16*)a.O + ((int64_t)b * a.n_q + my_q) * ldw + hh * D, inv);
+}
+
+template <bool CROSS, int NS>
+hipError_t launch(const ProjAttnArgs& a, hipStream_t s, LaunchEvents ev) {
+  void* args[] = {(void*)&a};
+  return hipExtLaunchKernel((const void*)proj_attn_bf16_kernel<CROSS, NS>, dim3(a.B * a.h), dim3(512),
+                            args, 0, s, ev.start, ev.stop, 0);
+}
+
+}  // namespace
+
+bool proj_attn_supported(int n_q, int n_k, int d_model) {
+  return n_q <= ROWS && n_k <= ROWS && d_model % BKP == 0;
+}
+
+hipError_t launch_proj_attn_bf16(const ProjAttnArgs& a, hipStream_t s, LaunchEvents ev) {
+  if (!proj_attn_supported(a.n_q, a.n_k, a.d_model)) return hipErrorInvalidValue;
+  if (a.Xq == a.Xkv && a.n_q == a.n_k) return launch<false, 3>(a, s, ev);
+  return launch<true, 2>(a, s, ev);
+}
+
+}  // namespace mha

@@ -133,9 +133,15 @@ size_t mha_workspace_bytes(int B, int n_q, int n_k, int h, int d_k, int d_v, int
  *               owned by the caller, not read before it is written.
  *   dtype       MHA_DTYPE_BF16.
  *
- * When X_kv == X_q (same pointer) and n_q == n_k, the three input
- * projections run as one GEMM over the stacked weights.  Y must not overlap
- * any input or the workspace.
+ * Launch plan (see mha_forward_launches): when n_q <= 128, n_k <= 128 and
+ * d_model is a multiple of 64, one fused kernel per (batch, head) computes
+ * that head's Q, K, V tiles in on-chip memory and its attention output
+ * (written to the workspace's concatenated-heads region), then the output
+ * projection runs.  Otherwise, when X_kv == X_q (same pointer) and
+ * n_q == n_k, the three input projections run as one GEMM over the stacked
+ * weights (two GEMMs for cross-attention), then attention, then the output
+ * projection.  Both plans compute the same products in the same order and
+ * give identical results.  Y must not overlap any input or the workspace.
  */
 int mha_forward(const void* X_q, const void* X_kv,
                 const void* Wq, const void* Wk, const void* Wv, const void* Wo,
@@ -146,9 +152,11 @@ int mha_forward(const void* X_q, const void* X_kv,
 
 /*
  * The three stages of mha_forward, callable on their own with the same
- * arguments (each ignores what it does not use).  mha_forward is exactly
- * mha_project_in; mha_attend; mha_project_out on one stream.  They share
- * the workspace layout documented at mha_workspace_bytes.
+ * arguments (each ignores what it does not use).  mha_project_in;
+ * mha_attend; mha_project_out on one stream gives exactly mha_forward's
+ * result (and fills the workspace Q, K, V, which the fused plan of
+ * mha_forward does not write).  They share the workspace layout documented
+ * at mha_workspace_bytes.
  *
  * mha_project_in  -- Q = X_q W^Q, K = X_kv W^K, V = X_kv W^V, written per head
  *                    into the workspace (devpress.csdn.net section 2.1,
@@ -179,9 +187,10 @@ int mha_project_out(const void* Wo, void* Y,
  * kernel starts and events[2i+1] when it ends (AMD hipExtLaunchKernel launch
  * events; elapsed times between them are pure kernel execution).  The caller
  * creates the events (default flags) and owns them.  Launch counts:
- * sdpa_forward 1; mha_forward 3 when X_kv == X_q and n_q == n_k (fused input
- * projection, attention, output projection), otherwise 4 (Q projection,
- * K/V projection, attention, output projection).  `capacity` is the number of
+ * sdpa_forward 1; mha_forward as mha_forward_launches returns (2: fused
+ * projection + attention, output projection; 3: stacked input projection,
+ * attention, output projection; 4: Q projection, K/V projection,
+ * attention, output projection).  `capacity` is the number of
  * events passed; fewer than two per launch, or a NULL event among them, is
  * MHA_ERR_EVENTS.  *n_launches (if not NULL) receives the launch count.
  */
@@ -198,6 +207,14 @@ int mha_forward_timed(const void* X_q, const void* X_kv,
                       int mask_kind, const int32_t* key_lengths, int dtype,
                       void* workspace, size_t workspace_bytes, hipStream_t stream,
                       hipEvent_t* events, int capacity, int* n_launches);
+
+/*
+ * mha_forward_launches -- number of kernels mha_forward launches for these
+ * sizes (2, 3 or 4, see the launch plan at mha_forward); self_attention is
+ * nonzero when X_kv will be the same pointer as X_q.  Host-only, no HIP
+ * call.  MHA_ERR_DIM for non-positive sizes.
+ */
+int mha_forward_launches(int n_q, int n_k, int d_model, int self_attention);
 
 /* Text of a status code (static storage; never NULL). */
 const char* mha_status_str(int status);

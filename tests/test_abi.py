@@ -173,3 +173,16 @@ def test_generator_is_seeded_and_ordered():
     assert int(a["key_lengths"].min()) >= 2 and int(a["key_lengths"].max()) <= 7
     s = hafa.generate(hafa.WORKLOADS["encoder_self_base"].replace(B=2, n_q=3, n_k=3), seed=0)
     assert s["X_kv"] is s["X_q"]
+
+
+def test_launch_plan(L):
+    """Short sequences (<= 128 rows, d_model a multiple of 64) take the
+    fused projection + attention kernel; longer ones the stacked or split
+    projections."""
+    assert L.mha_forward_launches(100, 100, 512, 1) == 2
+    assert L.mha_forward_launches(96, 128, 1024, 0) == 2
+    assert L.mha_forward_launches(128, 128, 64, 1) == 2
+    assert L.mha_forward_launches(512, 512, 512, 1) == 3
+    assert L.mha_forward_launches(129, 129, 512, 0) == 4
+    assert L.mha_forward_launches(100, 100, 200, 1) == 3   # d_model not a multiple of 64
+    assert L.mha_forward_launches(0, 100, 512, 1) == -2

@@ -43,13 +43,29 @@ def test_causal_with_padding_counts():
 
 
 def test_gemm_plan():
-    plan, _ = bench.kernel_plan(WORKLOADS["encoder_self_base"])
+    plan, _ = bench.kernel_plan(WORKLOADS["encoder_self_base"], 3)
     assert [p["name"] for p in plan] == ["qkv_projection_gemm", "attention", "output_projection_gemm"]
     assert plan[0]["flops"] == 2 * 3200 * 512 * 1536
     assert plan[2]["flops"] == 2 * 3200 * 512 * 512
-    plan, _ = bench.kernel_plan(WORKLOADS["cross_padded_big"])
+    plan, _ = bench.kernel_plan(WORKLOADS["cross_padded_big"], 4)
     assert [p["name"] for p in plan][:2] == ["q_projection_gemm", "kv_projection_gemm"]
     assert abs((plan[0]["flops"] + plan[1]["flops"]) / 1e9 - 23.6) < 0.1
+
+
+def test_fused_plan():
+    """Short sequences: projection + attention in one kernel, whose flops
+    are the three projections (the attention's are added by the bench) and
+    whose bytes are X, the three weights and the concatenated heads."""
+    w = WORKLOADS["encoder_self_base"]
+    plan, _ = bench.kernel_plan(w, 2)
+    assert [p["name"] for p in plan] == ["qkv_projection_attention", "output_projection_gemm"]
+    assert plan[0]["flops"] == 2 * 3200 * 512 * 1536
+    assert plan[0]["bytes"] == 2 * (3200 * 512 + 512 * 1536 + 3200 * 512)
+    assert plan[0]["has_attention"] and not plan[1]["has_attention"]
+    w = WORKLOADS["cross_padded_big"]
+    plan, _ = bench.kernel_plan(w, 2)
+    assert plan[0]["flops"] == 2 * 32 * 96 * 1024 * 1024 + 2 * 32 * 128 * 1024 * 2048
+    assert plan[0]["bytes"] == 2 * (32 * 96 * 1024 + 32 * 128 * 1024 + 1024 * 3072 + 32 * 96 * 1024)
 
 
 def test_buffer_sets_exceed_infinity_cache():

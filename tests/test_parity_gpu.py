@@ -298,3 +298,31 @@ def test_mha_small_shapes(dev):
             mask=c["mask"], self_attn=c["self_attn"], key_len_range=c.get("key_len_range"),
             description=str(c))
         _mha_case(dev, w, seed=1)
+
+
+@pytest.mark.parametrize("case", [
+    dict(B=3, n_q=100, n_k=100, d_model=512, h=8, mask=0, self_attn=True),
+    dict(B=2, n_q=96, n_k=128, d_model=1024, h=16, mask=2, self_attn=False, key_len_range=(1, 128)),
+    dict(B=2, n_q=128, n_k=128, d_model=128, h=2, mask=1, self_attn=True),
+    dict(B=4, n_q=1, n_k=77, d_model=64, h=1, mask=0, self_attn=False),
+    dict(B=2, n_q=65, n_k=65, d_model=192, h=3, mask=3, self_attn=True, key_len_range=(1, 65)),
+])
+def test_fused_plan_equals_staged(dev, case):
+    """Short sequences take the fused projection + attention kernel; its
+    result equals the three stage calls (standalone projection GEMM,
+    attention, output projection) bit for bit, and the oracle within the
+    bf16 tolerance."""
+    w = WORKLOADS["cross_padded_big"].replace(
+        name="fused", B=case["B"], n_q=case["n_q"], n_k=case["n_k"], d_model=case["d_model"],
+        h=case["h"], mask=case["mask"], self_attn=case["self_attn"],
+        key_len_range=case.get("key_len_range"), description=str(case))
+    assert hafa.lib().mha_forward_launches(w.n_q, w.n_k, w.d_model, 1 if w.self_attn else 0) == 2
+    x, Xq, Xkv, Ws, kl, Y, inter = _mha_case(dev, w, seed=2)
+    ws = hafa.alloc_workspace(w.B, w.n_q, w.n_k, w.h, w.d_k, w.d_v, dev)
+    announce("staged path", w.description)
+    hafa.mha_project_in(Xq, Xkv, Ws[0], Ws[1], Ws[2], w.h, ws)
+    hafa.mha_attend(w.B, w.n_q, w.n_k, w.h, w.d_k, w.d_v, ws, w.mask, kl)
+    Y2 = torch.empty_like(Y)
+    hafa.mha_project_out(Ws[3], Y2, w.B, w.n_q, w.n_k, w.h, w.d_k, w.d_v, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
