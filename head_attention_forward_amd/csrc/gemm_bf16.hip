@@ -336,11 +336,15 @@ hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, Launc
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
+  // Measured on MI355X over the block's projection shapes: 128 x 128 tiles
+  // once there are enough of them to occupy the compute units (2-stage ring
+  // from two tiles per unit on), otherwise 64 x 64 tiles for parallelism.
   const int N = g.col_start[g.nseg];
   if (!tiles_fit(g, 128)) return launch_gemm_bf16_cfg(g, 6, s, ev);
-  const long big = (long)((N + 127) / 128) * ((g.M + 127) / 128);
-  if (big >= 512) return launch_gemm_bf16_cfg(g, 1, s, ev);
-  return launch_gemm_bf16_cfg(g, 3, s, ev);
+  const long t128 = (long)((N + 127) / 128) * ((g.M + 127) / 128);
+  if (t128 >= 512) return launch_gemm_bf16_cfg(g, 0, s, ev);
+  if (t128 >= 150) return launch_gemm_bf16_cfg(g, 1, s, ev);
+  return launch_gemm_bf16_cfg(g, 6, s, ev);
 }
 
 }  // namespace mha

@@ -69,7 +69,19 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
   const int col = lane & 31;
   const int grp = lane >> 5;
 
-  const int bh = blockIdx.x;
+  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin; unit
+  // (b, head) = b*h + head is remapped so that each XCD owns a contiguous
+  // run of units, i.e. whole batches: an activation row block is then read
+  // into one XCD's L2 only (every XCD reads the weights, which are smaller).
+  int bh;
+  {
+    const int T = a.B * a.h;
+    const int bid = blockIdx.x;
+    const int x = bid % 8;
+    const int per = T / 8;
+    const int rem = T - per * 8;
+    bh = __builtin_amdgcn_readfirstlane(x * per + min(x, rem) + bid / 8);
+  }
   const int b = __builtin_amdgcn_readfirstlane(bh / a.h);
   const int hh = bh - b * a.h;
   const int dm = a.d_model;
