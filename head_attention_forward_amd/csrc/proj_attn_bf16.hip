@@ -41,8 +41,13 @@ __device__ __forceinline__ int x_pos(int m, int chunk) { return chunk ^ ((m >> 1
 // Weight tile [64][64]: 128-byte rows; chunk c of row k at c ^ (((k >> 1) & 1) << 2).
 __device__ __forceinline__ int w_pos(int k, int chunk) { return chunk ^ (((k >> 1) & 1) << 2); }
 
-template <bool CROSS, int NS, int LPS>
+// Waits until at most `later` stages issued after the current one are still
+// in flight (LPS loads per stage and wave), i.e. the current stage landed.
+template <int NS, int LPS>
 __device__ __forceinline__ void wait_stage(int later) {
+  if constexpr (NS >= 4) {
+    if (later >= 2) { wait_vmcnt<2 * LPS>(); return; }
+  }
   if constexpr (NS >= 3) {
     if (later >= 1) { wait_vmcnt<LPS>(); return; }
   }
@@ -170,7 +175,7 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
   for (int s = 0; s < NS - 1; ++s)
     if (s < nsteps) issue(s, s);
   for (int t = 0; t < nsteps; ++t) {
-    wait_stage<CROSS, NS, LPS>(min(NS - 2, nsteps - 1 - t));
+    wait_stage<NS, LPS>(min(NS - 2, nsteps - 1 - t));
     __syncthreads();
     if (t + NS - 1 < nsteps) issue(t + NS - 1, (t + NS - 1) % NS);
     compute(&ring[(t % NS) * STAGE]);
