@@ -13,8 +13,8 @@
 // so the projection writes Q, K, V directly in the [B][h][n][d] layout the
 // attention kernel streams, and the output projection writes Y row-major.
 //
-// Tiling: 256 threads = 2 x 2 waves; a BM x BN output tile, each wave a
-// (BM/2) x (BN/2) block of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16).
+// Tiling: WM x WN waves (2 x 2 or 2 x 4); a BM x BN output tile, each wave a
+// (BM/WM) x (BN/WN) block of 32 x 32 MFMA tiles (v_mfma_f32_32x32x16_bf16).
 // K advances 64 per stage.  Stages go from global memory straight into LDS
 // (global_load_lds_dwordx4: no register staging) through a ring of NS
 // buffers, NS-1 stages ahead of the one being multiplied, one barrier per
@@ -82,15 +82,18 @@ __device__ __forceinline__ int seg_start(const GemmArgs& g, int s) {
   return s == 0 ? g.col_start[0] : (s == 1 ? g.col_start[1] : g.col_start[2]);
 }
 
-template <int BM, int BN, int NS>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
+template <int BM, int BN, int NS, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs g) {
   static_assert(BM == 64 || BM == 128, "tile rows");
   static_assert(BN == 64 || BN == 128, "tile columns");
   static_assert(NS >= 2 && NS <= 4, "ring depth");
-  constexpr int MB = BM / 64;          // 32-row MFMA tiles per wave
-  constexpr int NB = BN / 64;          // 32-column MFMA tiles per wave
-  constexpr int AL = BM * BK * 2 / 1024 / 4;   // 1 KB A loads per wave and stage
-  constexpr int BL = BK * BN * 2 / 1024 / 4;   // 1 KB W loads per wave and stage
+  constexpr int NWAVE = WM * WN;
+  constexpr int MB = BM / WM / 32;     // 32-row MFMA tiles per wave
+  constexpr int NB = BN / WN / 32;     // 32-column MFMA tiles per wave
+  static_assert(MB >= 1 && NB >= 1, "wave tile of at least 32 x 32");
+  constexpr int AL = BM * BK * 2 / 1024 / NWAVE;   // 1 KB A loads per wave and stage
+  constexpr int BL = BK * BN * 2 / 1024 / NWAVE;   // 1 KB W loads per wave and stage
+  static_assert(AL >= 1 && BL >= 1, "every wave loads part of each tile");
   constexpr int LPS = AL + BL;
   constexpr int BROW = BN / 8;                 // 16-byte chunks per W row
 
@@ -102,8 +105,8 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
   const int grp = lane >> 5;
-  const int wm = wave >> 1;
-  const int wn = wave & 1;
+  const int wm = wave / WN;
+  const int wn = wave % WN;
 
   const int N = g.col_start[g.nseg];
   const int MT = (g.M + BM - 1) / BM;
@@ -205,7 +208,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   int x_off[MB][BK / 16];
 #pragma unroll
   for (int i = 0; i < MB; ++i) {
-    const int row = wm * (BM / 2) + 32 * i + col;
+    const int row = wm * (BM / WM) + 32 * i + col;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) x_off[i][ks] = row * BK + 8 * a_pos(row, 2 * ks + grp);
   }
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   int w_off[NB][BK / 16][2];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int n = wn * (BN / 2) + 32 * j + tr_n;
+    const int n = wn * (BN / WN) + 32 * j + tr_n;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
       const int k = 16 * ks + 8 * grp + tr_k;
@@ -270,7 +273,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   // single head), so its destination is fixed per block; N is a multiple of 8.
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int nb = n0 + wn * (BN / 2) + 32 * j;  // wave-uniform
+    const int nb = n0 + wn * (BN / WN) + 32 * j;  // wave-uniform
     if (nb >= N) continue;
     const int s = seg_of(g, nb);
     const int rows = seg_field(g, s, &GemmSeg::rows);
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
     const int64_t bstride = (int64_t)heads * rows * hd;
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const int m = m0 + wm * (BM / 2) + 32 * i + col;
+      const int m = m0 + wm * (BM / WM) + 32 * i + col;
       if (m >= g.M) continue;
       const int bb = m / rows;
       const int pos = m - bb * rows;
@@ -300,13 +303,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_kernel(const GemmArgs g) {
   }
 }
 
-template <int BM, int BN, int NS>
+template <int BM, int BN, int NS, int WM = 2, int WN = 2>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
   const int N = g.col_start[g.nseg];
   const int tiles = ((N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
   void* args[] = {(void*)&g};
-  return hipExtLaunchKernel((const void*)gemm_bf16_kernel<BM, BN, NS>, dim3(tiles), dim3(256), args,
-                            0, s, ev.start, ev.stop, 0);
+  return hipExtLaunchKernel((const void*)gemm_bf16_kernel<BM, BN, NS, WM, WN>, dim3(tiles),
+                            dim3(64 * WM * WN), args, 0, s, ev.start, ev.stop, 0);
 }
 
 // Every segment must start on a multiple of the tile width (a tile's columns
@@ -320,8 +323,8 @@ bool tiles_fit(const GemmArgs& g, int bn) {
 }  // namespace
 
 hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, LaunchEvents ev) {
-  static const int kBN[] = {128, 128, 128, 128, 128, 64, 64, 64, 64};
-  if (cfg < 0 || cfg > 8 || !tiles_fit(g, kBN[cfg])) return hipErrorInvalidValue;
+  static const int kBN[] = {128, 128, 128, 128, 128, 64, 64, 64, 64, 128, 128, 128, 64};
+  if (cfg < 0 || cfg > 12 || !tiles_fit(g, kBN[cfg])) return hipErrorInvalidValue;
   switch (cfg) {
     case 0: return launch_tile<128, 128, 2>(g, s, ev);
     case 1: return launch_tile<128, 128, 3>(g, s, ev);
@@ -331,19 +334,24 @@ hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, Launc
     case 5: return launch_tile<128, 64, 3>(g, s, ev);
     case 6: return launch_tile<64, 64, 3>(g, s, ev);
     case 7: return launch_tile<64, 64, 4>(g, s, ev);
-    default: return launch_tile<128, 64, 4>(g, s, ev);
+    case 8: return launch_tile<128, 64, 4>(g, s, ev);
+    case 9: return launch_tile<128, 128, 2, 2, 4>(g, s, ev);
+    case 10: return launch_tile<128, 128, 3, 2, 4>(g, s, ev);
+    case 11: return launch_tile<64, 128, 2, 2, 4>(g, s, ev);
+    default: return launch_tile<128, 64, 2, 4, 2>(g, s, ev);
   }
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
   // Measured on MI355X over the block's projection shapes: 128 x 128 tiles
-  // once there are enough of them to occupy the compute units (2-stage ring
-  // from two tiles per unit on), otherwise 64 x 64 tiles for parallelism.
+  // with 8 waves (more waves issuing the stage copies) once there are enough
+  // tiles to occupy the compute units (2-stage ring from two tiles per unit
+  // on), otherwise 64 x 64 tiles with 4 waves for parallelism.
   const int N = g.col_start[g.nseg];
   if (!tiles_fit(g, 128)) return launch_gemm_bf16_cfg(g, 6, s, ev);
   const long t128 = (long)((N + 127) / 128) * ((g.M + 127) / 128);
-  if (t128 >= 512) return launch_gemm_bf16_cfg(g, 0, s, ev);
-  if (t128 >= 150) return launch_gemm_bf16_cfg(g, 1, s, ev);
+  if (t128 >= 512) return launch_gemm_bf16_cfg(g, 9, s, ev);
+  if (t128 >= 150) return launch_gemm_bf16_cfg(g, 10, s, ev);
   return launch_gemm_bf16_cfg(g, 6, s, ev);
 }
 
