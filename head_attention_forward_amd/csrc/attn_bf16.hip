@@ -45,10 +45,10 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
   const int qt = (int)gridDim.y - 1 - (int)blockIdx.y;
   const int q0 = qt * QT;
 
-  const __bf16* Qp = (const __bf16*)a.Q + b * a.q_sb + hh * a.q_sh;
-  const char* Kp = (const char*)((const __bf16*)a.K + b * a.k_sb + hh * a.k_sh);
-  const char* Vp = (const char*)((const __bf16*)a.V + b * a.v_sb + hh * a.v_sh);
-  __bf16* Op = (__bf16*)a.O + b * a.o_sb + hh * a.o_sh;
+  const __bf16* Qp = wave_uniform((const __bf16*)a.Q + b * a.q_sb + hh * a.q_sh);
+  const char* Kp = wave_uniform((const char*)((const __bf16*)a.K + b * a.k_sb + hh * a.k_sh));
+  const char* Vp = wave_uniform((const char*)((const __bf16*)a.V + b * a.v_sb + hh * a.v_sh));
+  __bf16* Op = wave_uniform((__bf16*)a.O + b * a.o_sb + hh * a.o_sh);
 
   int L = a.n_k;
   if (a.padded) L = min(L, a.key_len[b]);
@@ -57,6 +57,7 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
   const int qw0 = q0 + 32 * wave;
   const int my_q = qw0 + col;
   const int lim = a.causal ? min(L, my_q + 1) : L;
+  const int lim_min = __builtin_amdgcn_readfirstlane(a.causal ? min(L, qw0 + 1) : L);
   const int wv_last = min(qw0 + 32, a.n_q) - 1;
   const int wv_keys =
       __builtin_amdgcn_readfirstlane(wv_last < qw0 ? 0 : (a.causal ? min(L, wv_last + 1) : L));
@@ -82,13 +83,16 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
   }
   const unsigned ks_lds = lds_addr(&Ks[0][0]);
   const unsigned vs_lds = lds_addr(&Vs[0][0]);
+  // Tiles are issued in order; kb/vb point at the next one (wave-uniform,
+  // advanced with scalar adds).
+  const int64_t kstep = (int64_t)KT * a.k_sr * 2, vstep = (int64_t)KT * a.v_sr * 2;
+  const char* kb = Kp;
+  const char* vb = Vp;
   auto issue = [&](int tile, int buf) {
     const unsigned kd = ks_lds + (unsigned)(buf * KT * D + wave * CHW * 512) * 2u;
     const unsigned vd = vs_lds + (unsigned)(buf * KT * D + wave * CHW * 512) * 2u;
     const int k0 = tile * KT;
     if (k0 + KT <= a.n_k) {
-      const char* kb = Kp + (int64_t)k0 * a.k_sr * 2;
-      const char* vb = Vp + (int64_t)k0 * a.v_sr * 2;
 #pragma unroll
       for (int r = 0; r < CHW; ++r) {
         dma16_s(kb, koff[r], kd + 1024u * r);
@@ -104,6 +108,8 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
         dma16_s(Vp, (unsigned)(key * a.v_sr + vc) * 2u, vd + 1024u * r);
       }
     }
+    kb += kstep;
+    vb += vstep;
   };
 
   WaveAttention wa;
@@ -123,7 +129,7 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
         else wait_vmcnt<0>();
         __syncthreads();
         if (t + NS - 1 < ntiles) issue(t + NS - 1, (u + NS - 1) % NS);
-        if (t * KT < wv_keys) wa.tile(Ks[u], Vs[u], t * KT, lim);  // else no visible key
+        if (t * KT < wv_keys) wa.tile(Ks[u], Vs[u], t * KT, lim, lim_min);  // else no visible key
       }
     }
   }

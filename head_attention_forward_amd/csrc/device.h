@@ -48,6 +48,16 @@ __device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsign
                : "memory", "m0");
 }
 
+// A wave-uniform pointer pinned to SGPRs (uniform 64-bit products are
+// otherwise formed, and kept, in VGPRs).
+template <typename T>
+__device__ __forceinline__ T* wave_uniform(T* p) {
+  const unsigned long long v = (unsigned long long)(size_t)p;
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(v >> 32));
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)v);
+  return (T*)(size_t)(((unsigned long long)hi << 32) | (unsigned long long)lo);
+}
+
 // LDS byte address of a __shared__ object (wave-uniform).
 __device__ __forceinline__ unsigned lds_addr(const void* p) {
   return __builtin_amdgcn_readfirstlane(

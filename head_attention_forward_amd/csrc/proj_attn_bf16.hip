@@ -212,6 +212,7 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
   int L = a.n_k;
   if (a.padded) L = min(L, a.key_len[b]);
   const int lim = a.causal ? min(L, my_q + 1) : L;
+  const int lim_min = __builtin_amdgcn_readfirstlane(a.causal ? min(L, qw0 + 1) : L);
   const int wv_last = min(qw0 + 32, a.n_q) - 1;
   const int wv_keys = __builtin_amdgcn_readfirstlane(a.causal ? min(L, wv_last + 1) : L);
   WaveAttention wa;
@@ -219,7 +220,7 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
   wa.load_q_lds(Qs, min(my_q, a.n_q - 1));
 #pragma unroll
   for (int t = 0; t < ROWS / KT; ++t)
-    if (t * KT < wv_keys) wa.tile(Ks + t * KT * D, Vs + t * KT * D, t * KT, lim);
+    if (t * KT < wv_keys) wa.tile(Ks + t * KT * D, Vs + t * KT * D, t * KT, lim, lim_min);
   const float inv = wa.inv_sum();
   if (my_q < a.n_q)
     wa.store((__bf16*)a.O + ((int64_t)b * a.n_q + my_q) * ldw + hh * D, inv);

@@ -139,12 +139,15 @@ struct WaveAttention {
   // Softmax bookkeeping of one half tile (scores sh; weights into pa, pb).
   __device__ __forceinline__ void half(const f32x16& sh, bf16x8& pa, bf16x8& pb) {
     float lt = weights(sh, pa, pb);
-    unsigned need = lt > kMaxTileSum;  // lt is finite or +inf, never NaN
-    {
-      const auto r = __builtin_amdgcn_permlane32_swap(need, need, false, false);
-      need = r[0] | r[1];  // both halves of a query row decide together
-    }
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+    // One compare decides for the whole wave (its lane mask is the ballot;
+    // lt is finite or +inf, never NaN); on the exact path both halves of a
+    // query row decide together.
+    if (__builtin_amdgcn_ballot_w64(lt > kMaxTileSum) != 0) {
+      unsigned need = lt > kMaxTileSum;
+      {
+        const auto r = __builtin_amdgcn_permlane32_swap(need, need, false, false);
+        need = r[0] | r[1];
+      }
       float mt = fmaxf(sh[0], sh[1]);
 #pragma unroll
       for (int i = 2; i < 16; i += 2) mt = fmaxf(mt, fmaxf(sh[i], sh[i + 1]));
@@ -180,10 +183,11 @@ struct WaveAttention {
   }
 
   // One 64-key tile starting at key k0 (ks, vs: the tile in LDS).  Keys at or
-  // beyond `lim` are hidden from this lane's query.  The softmax runs per
-  // 32-key half, first half leading, so that the vector ALU works on one
-  // half while the matrix unit multiplies the other.
-  __device__ __forceinline__ void tile(const __bf16* ks, const __bf16* vs, int k0, int lim) {
+  // beyond `lim` are hidden from this lane's query; lim_min is the smallest
+  // lim of the wave (wave-uniform).  The softmax runs per 32-key half, first
+  // half leading, so that the vector ALU works on one half while the matrix
+  // unit multiplies the other.
+  __device__ __forceinline__ void tile(const __bf16* ks, const __bf16* vs, int k0, int lim, int lim_min) {
     f32x16 s0 = {}, s1 = {};
     bf16x8 ka[4], kb[4];
 #pragma unroll
@@ -200,7 +204,7 @@ struct WaveAttention {
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[2], qf[2], s1, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kb[3], qf[3], s1, 0, 0, 0);
     // s0[i] is the score of key k0 + 8(i/4) + 4g + i%4, s1[i] of that key + 32.
-    if (k0 + KT > lim) {
+    if (k0 + KT > lim_min) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int key = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
