@@ -163,12 +163,9 @@ hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, L
 }
 
 hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev) {
-  // Measured on MI355X: with many 128-query blocks (long sequences) 8-wave
-  // workgroups with a 2-tile ring and four waves per SIMD are fastest;
-  // otherwise 4-wave workgroups with a 2-tile ring and three waves per SIMD.
-  const long blocks = (long)a.B * a.h * ((a.n_q + 127) / 128);
-  if (blocks >= 2048) return launch_attn_bf16_d64_cfg(a, 3, s, ev);
-  return launch_attn_bf16_d64_cfg(a, 1, s, ev);
+  // Measured on MI355X: 4-wave workgroups (128 queries) with a 2-tile ring
+  // and four waves per SIMD are fastest for short and long sequences alike.
+  return launch_attn_bf16_d64_cfg(a, 0, s, ev);
 }
 
 }  // namespace mha

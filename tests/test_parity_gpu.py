@@ -236,6 +236,26 @@ def test_saturated_and_uniform(dev):
         assert_bf16_close(O, want, f"zero Q mask {mask}")
 
 
+@pytest.mark.parametrize("mask,kl", [(0, None), (1, None), (2, [300, 170])])
+def test_rising_scores_move_the_reference_every_half_tile(dev, mask, kl):
+    """Scores that climb by about 11 (log2 units) every 32 keys force the
+    streaming softmax to move its reference value in every half tile,
+    including a half whose scores were already taken against the old one."""
+    B, h, n = 2, 2, 300
+    g = torch.Generator("cpu")
+    g.manual_seed(21)
+    Q = torch.randn((B, h, n, 64), generator=g) * 0.05
+    K = torch.randn((B, h, n, 64), generator=g) * 0.05
+    V = torch.randn((B, h, n, 64), generator=g)
+    Q[..., 0] = 4.0
+    K[..., 0] = 0.5 * torch.arange(n, dtype=torch.float32)  # score ~ 2 j, x 0.125 x log2(e)
+    Q, K, V = Q.to(torch.bfloat16), K.to(torch.bfloat16), V.to(torch.bfloat16)
+    announce("rising scores", mask, kl)
+    O = run_sdpa(dev, Q, K, V, 0.125, mask, kl)
+    torch.cuda.synchronize()
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"rising scores mask {mask}")
+
+
 def test_masked_keys_have_exactly_zero_weight(dev):
     """Changing keys/values a query may not see leaves its output bit-exact:
     future rows under the causal mask, padded rows under key padding."""
