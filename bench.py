@@ -289,19 +289,38 @@ def cpu_baseline(w, x, target_s):
 
 # ----------------------------------------------------------------------------- traffic
 
-def kernel_source_sha():
+# HIP sources that determine a timed kernel's code and launch shape, by kernel
+# name (the name recorded with each counter entry).
+_COMMON_SOURCES = ("device.h", "kernels.h")
+KERNEL_SOURCES = {
+    "attn_fwd_bf16_d64_kernel": ("attn_bf16.hip", "wave_attention.h"),
+    "attn_fwd_f32_d64_kernel": ("attn_f32.hip",),
+    "proj_attn_bf16_kernel": ("proj_attn_bf16.hip", "wave_attention.h", "mha_api.hip"),
+    "gemm_bf16_kernel": ("gemm_bf16.hip", "mha_api.hip"),
+}
+
+
+def sources_of(kernel_name):
+    return KERNEL_SOURCES.get(kernel_name.split("<", 1)[0].strip())
+
+
+def kernel_source_sha(names=None):
+    """Hash of the named HIP sources (all of them when names is None)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "head_attention_forward_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(csrc, name), "rb") as f:
-                h.update(name.encode() + b"\0" + f.read())
+    if names is None:
+        files = sorted(n for n in os.listdir(csrc) if n.endswith((".hip", ".h")))
+    else:
+        files = sorted(set(names) | set(_COMMON_SOURCES))
+    for name in files:
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
 
 
 def recorded_traffic(workload, kernel):
     """HBM bytes per launch from the committed counter summary, if it was
-    taken on the current kernel sources; otherwise None."""
+    taken on the current sources of that kernel; otherwise None."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return None
@@ -310,10 +329,13 @@ def recorded_traffic(workload, kernel):
             rec = json.load(f)
     except Exception:
         return None
-    if rec.get("kernel_source_sha") != kernel_source_sha():
-        return None
     ent = rec.get("entries", {}).get(f"{workload}/{kernel}")
-    return None if ent is None else float(ent["bytes_per_launch"])
+    if ent is None:
+        return None
+    files = sources_of(ent.get("kernel", ""))
+    if files is None or ent.get("source_sha") != kernel_source_sha(files):
+        return None
+    return float(ent["bytes_per_launch"])
 
 
 # ----------------------------------------------------------------------------- main
