@@ -214,6 +214,41 @@ def test_sdpa_f32_edges(dev, B, h, n_q, n_k, mask, kl):
     assert_f32_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"f32 edge {n_q}x{n_k} m{mask}")
 
 
+@pytest.mark.parametrize("mask", [2, 3])
+def test_sdpa_bf16_max_padded_batch(dev, mask):
+    """The largest batch that takes per-batch key lengths (256, passed in the
+    kernel arguments): every batch's lengths are honoured."""
+    B, h, n = 256, 1, 24
+    Q, K, V = sdpa_inputs(B, h, n, n, torch.bfloat16, seed=31)
+    g = torch.Generator("cpu")
+    g.manual_seed(32)
+    kl = torch.randint(1, n + 1, (B,), generator=g).tolist()
+    kl[0], kl[-1] = 1, n
+    announce("sdpa max padded batch", mask)
+    O = run_sdpa(dev, Q, K, V, 0.125, mask, kl)
+    torch.cuda.synchronize()
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"B=256 mask {mask}")
+
+
+def test_mha_max_padded_batch_and_fused_boundary(dev):
+    """The whole block at the largest padded batch (fused path), and just past
+    the fused kernel's 128-row limit (n = 129: the staged path)."""
+    cases = [
+        dict(B=256, n_q=16, n_k=16, d_model=64, h=1, mask=3, self_attn=True, key_len_range=(1, 16)),
+        dict(B=2, n_q=129, n_k=129, d_model=128, h=2, mask=1, self_attn=True),
+        dict(B=2, n_q=128, n_k=129, d_model=128, h=2, mask=2, self_attn=False, key_len_range=(1, 129)),
+    ]
+    for c in cases:
+        w = WORKLOADS["cross_padded_big"].replace(
+            name="limits", B=c["B"], n_q=c["n_q"], n_k=c["n_k"], d_model=c["d_model"], h=c["h"],
+            mask=c["mask"], self_attn=c["self_attn"], key_len_range=c.get("key_len_range"),
+            description=str(c))
+        fused = max(w.n_q, w.n_k) <= 128
+        assert hafa.lib().mha_forward_launches(w.n_q, w.n_k, w.d_model, 1 if w.self_attn else 0) == \
+            (2 if fused else (3 if w.self_attn else 4))
+        _mha_case(dev, w, seed=3)
+
+
 def test_saturated_and_uniform(dev):
     """Large-magnitude scores (softmax saturation) stay finite and accurate;
     Q = 0 gives uniform weights: outputs are means of the visible V rows."""
