@@ -29,6 +29,7 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC",
 # NaN canonicalization: this lets v_max3_f32 take raw scores.  Host-side
 # argument checks (which do test for NaN) live in other files.
 EXTRA = {"attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
+         "attn_decode_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"],
          "proj_attn_bf16.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 

@@ -163,6 +163,9 @@ hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, L
 }
 
 hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev) {
+  // A few queries over many keys: split the keys over waves instead
+  // (attn_decode_bf16.hip).
+  if (attn_decode_applies(a)) return launch_attn_decode_bf16_d64(a, s, ev);
   // Measured on MI355X: 4-wave workgroups (128 queries) with a 2-tile ring
   // and four waves per SIMD are fastest for short and long sequences alike.
   return launch_attn_bf16_d64_cfg(a, 0, s, ev);

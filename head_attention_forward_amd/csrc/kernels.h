@@ -73,6 +73,10 @@ struct LaunchEvents {
   hipEvent_t stop = nullptr;
 };
 
+// Few queries (n_q <= 32, no causal mask) over more than 128 keys: the keys
+// of each (batch, head) are split over the workgroup's waves.
+bool attn_decode_applies(const AttnArgs& a);
+hipError_t launch_attn_decode_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev);
 hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 // One fixed attention configuration (index into the instantiated set); for sweeps.
 hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, LaunchEvents ev = {});

@@ -84,6 +84,15 @@ WORKLOADS = {
         "long_causal_sdpa", "sdpa", "bf16", B=4, n_q=4096, n_k=4096, h=16, d_k=64, d_v=64,
         mask=MASK_CAUSAL,
         description="bare causal attention, bf16, B=4 h=16 n=4096 d=64"),
+    # One generation step of incremental decoding: each sequence's newest
+    # query against its cached keys and values (cache capacity 4096, current
+    # lengths in [1024, 4096]); the pages give no decoding shapes, these are
+    # the big model's 16 heads at batch 32.
+    "decode_step_sdpa": Workload(
+        "decode_step_sdpa", "sdpa", "bf16", B=32, n_q=1, n_k=4096, h=16, d_k=64, d_v=64,
+        mask=MASK_KEY_PADDING, key_len_range=(1024, 4096),
+        description="bare attention, one query per sequence over a 4096-key cache, bf16, "
+                    "B=32 h=16 d=64, cache lengths in [1024,4096]"),
 }
 
 ORDER = ["sdpa_f32_tiny", "encoder_self_base", "decoder_causal_base", "cross_padded_big",

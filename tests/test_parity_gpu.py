@@ -249,6 +249,29 @@ def test_mha_max_padded_batch_and_fused_boundary(dev):
         _mha_case(dev, w, seed=3)
 
 
+@pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", [
+    (2, 3, 1, 129, 0, None), (3, 2, 1, 300, 2, [300, 1, 191]), (2, 2, 5, 1000, 2, [1000, 650]),
+    (1, 4, 32, 777, 0, None), (4, 2, 1, 4096, 2, [4096, 2049, 1, 3000]), (1, 2, 17, 8193, 0, None),
+])
+def test_sdpa_decode_shapes(dev, B, h, n_q, n_k, mask, kl):
+    """Few queries over long key ranges (one new query per sequence against
+    cached keys, with per-sequence cache lengths): the keys are split over
+    waves and the partial softmaxes merged."""
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.bfloat16, seed=41)
+    announce("sdpa decode", B, h, n_q, n_k, mask, kl)
+    O = run_sdpa(dev, Q, K, V, 0.125, mask, kl)
+    torch.cuda.synchronize()
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"decode {B}x{h} {n_q}x{n_k}")
+    if kl is not None:  # keys past a sequence's length have exactly zero weight
+        K2, V2 = K.clone(), V.clone()
+        for b, L in enumerate(kl):
+            K2[b, :, L:] = 40.0
+            V2[b, :, L:] = -9.0
+        O2 = run_sdpa(dev, Q, K2, V2, 0.125, mask, kl)
+        torch.cuda.synchronize()
+        assert torch.equal(O2.cpu(), O.cpu())
+
+
 def test_saturated_and_uniform(dev):
     """Large-magnitude scores (softmax saturation) stay finite and accurate;
     Q = 0 gives uniform weights: outputs are means of the visible V rows."""
