@@ -293,7 +293,8 @@ def cpu_baseline(w, x, target_s):
 # name (the name recorded with each counter entry).
 _COMMON_SOURCES = ("device.h", "kernels.h")
 KERNEL_SOURCES = {
-    "attn_fwd_bf16_d64_kernel": ("attn_bf16.hip", "wave_attention.h"),
+    "attn_fwd_bf16_d64_kernel": ("attn_bf16.hip", "attn_decode_bf16.hip", "wave_attention.h"),
+    "attn_decode_bf16_d64_kernel": ("attn_decode_bf16.hip", "attn_bf16.hip", "wave_attention.h"),
     "attn_fwd_f32_d64_kernel": ("attn_f32.hip",),
     "proj_attn_bf16_kernel": ("proj_attn_bf16.hip", "wave_attention.h", "mha_api.hip"),
     "gemm_bf16_kernel": ("gemm_bf16.hip", "mha_api.hip"),
