@@ -95,7 +95,11 @@ extern "C" {
  *
  * The n_q x n_k score matrix is never stored: one fused kernel streams K/V
  * tiles and keeps a running row maximum and row sum (an exact reformulation
- * of the row softmax).  O must not overlap Q, K or V.
+ * of the row softmax).  With bf16, at most 32 queries, no causal bit and
+ * more than 128 keys (one new query per sequence against its cached keys,
+ * the incremental-decoding shape), the kernel splits each head's keys over
+ * its waves and merges their partial row states: the same softmax, summed in
+ * another order.  O must not overlap Q, K or V.
  */
 int sdpa_forward(const void* Q, const void* K, const void* V, void* O,
                  int B, int h, int n_q, int n_k, int d_k, int d_v,
