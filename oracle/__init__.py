@@ -11,7 +11,9 @@ Two independent formulations are provided:
 
 * ``oracle.attention``  -- numpy, float64, the matrix form of the definition
   (projections, per-head scores, additive mask, row softmax, weighted sum of
-  values, concat, output projection), one function per step.
+  values, concat, output projection), one function per step;
+  ``oracle.layer`` -- the same for residual + LayerNorm and the
+  position-wise feed-forward network of an encoder layer.
 * ``oracle.bruteforce`` -- pure-Python loops with ``math.exp``/``math.fsum``,
   one query row at a time, for tiny inputs; it cross-checks the matrix form.
 
@@ -33,6 +35,9 @@ computed):
   section 3.2 (cross-attention).
 * wiki.hugogu.cn, "Attention Is All You Need" notes: the masked
   self-attention paragraph and the table of the three attention uses.
+* For the rest of the encoder layer (``oracle.layer``): hex4c59.cc sections
+  "前馈网络为什么放在注意力后面？" and "Add & Norm 里究竟发生了什么？";
+  devpress.csdn.net section 2.3 (encoder block order, FFN formula).
 
 Parity status of every function is stated in its docstring.  All functions
 are pinned by ``tests/test_oracle.py`` (printed values from the pages,
@@ -55,4 +60,10 @@ from .attention import (  # noqa: F401
     split_heads,
     concat_heads,
 )
-from .bruteforce import attention_bruteforce, mha_bruteforce  # noqa: F401
+from .bruteforce import (  # noqa: F401
+    attention_bruteforce,
+    ffn_bruteforce,
+    layer_norm_bruteforce,
+    mha_bruteforce,
+)
+from .layer import add_layer_norm, encoder_layer_ref, ffn, layer_norm  # noqa: F401

@@ -89,3 +89,31 @@ def mha_bruteforce(X_q, X_kv, Wq, Wk, Wv, Wo, h, mask_kind=0, key_lengths=None):
         concat = [[heads[i][r][j] for i in range(h) for j in range(d_v)] for r in range(len(Qb))]
         Y.append(_matmul(concat, Wo))
     return Y
+
+
+def layer_norm_bruteforce(U, gamma, beta, eps):
+    """LayerNorm by loops, one row at a time: mean and population variance of
+    the row's d features with math.fsum, then gamma_j (u_j - mean) /
+    sqrt(var + eps) + beta_j (hex4c59.cc, section "Add & Norm 里究竟发生了什么？").
+    U nested [rows][d]; returns nested lists."""
+    out = []
+    for row in U:
+        d = len(row)
+        mean = math.fsum(float(x) for x in row) / d
+        var = math.fsum((float(x) - mean) ** 2 for x in row) / d
+        den = math.sqrt(var + eps)
+        out.append([float(gamma[j]) * (float(row[j]) - mean) / den + float(beta[j]) for j in range(d)])
+    return out
+
+
+def ffn_bruteforce(X, W1, b1, W2, b2):
+    """Position-wise feed-forward network by loops: for every row,
+    hidden_j = max(0, sum_t x_t W1[t][j] + b1_j), out_j = sum_j' hidden_j'
+    W2[j'][j] + b2_j (devpress.csdn.net, section 2.3).  X nested [rows][d]."""
+    out = []
+    for row in X:
+        hid = [max(0.0, math.fsum(float(row[t]) * float(W1[t][j]) for t in range(len(row))) + float(b1[j]))
+               for j in range(len(b1))]
+        out.append([math.fsum(hid[t] * float(W2[t][j]) for t in range(len(hid))) + float(b2[j])
+                    for j in range(len(b2))])
+    return out

@@ -444,3 +444,202 @@ ALL_MHA_CHECKS = [
     check_mha_identity_reduction,
     check_mha_cross_sources,
 ]
+
+
+# ------------------------------------------------------------ encoder layer pins
+# Implementation interface for these: layer_norm(U, gamma, beta, eps),
+# ffn(X, W1, b1, W2, b2), encoder_layer_ref(X, Wq, Wk, Wv, Wo, h, g1, be1,
+# W1, b1, W2, b2, g2, be2, eps, mask_kind, key_lengths).
+
+def check_layernorm_worked_row(impl):
+    """u = (1, 2, 3, 4): mean 2.5, population variance 1.25 (the mean and
+    variance of the row's own features, hex4c59.cc section "Add & Norm 里究竟
+    发生了什么？"), so with gamma = 1, beta = 0, eps = 1e-5 the outputs are
+    (-1.5, -0.5, 0.5, 1.5) / sqrt(1.25001)."""
+    u = np.array([[1.0, 2.0, 3.0, 4.0]])
+    out = impl.layer_norm(u, np.ones(4), np.zeros(4), 1e-5)
+    den = math.sqrt(1.25001)
+    assert np.allclose(out, [[-1.5 / den, -0.5 / den, 0.5 / den, 1.5 / den]], atol=1e-14, rtol=0)
+
+
+def check_layernorm_moments(impl):
+    """With eps = 0, gamma = 1, beta = 0 every normalised row has mean 0 and
+    mean square 1 (closed form of standardisation)."""
+    r = _rng(21)
+    U = r.standard_normal((7, 33)) * 3.0 + 1.5
+    out = impl.layer_norm(U, np.ones(33), np.zeros(33), 0.0)
+    assert np.allclose(out.mean(axis=1), 0.0, atol=1e-14)
+    assert np.allclose((out ** 2).mean(axis=1), 1.0, atol=1e-13)
+
+
+def check_layernorm_affine_and_invariances(impl):
+    """gamma and beta act per feature after normalising; adding a constant to
+    a row changes nothing; scaling a row by a > 0 (eps = 0) changes nothing,
+    by a < 0 flips the sign."""
+    r = _rng(22)
+    U = r.standard_normal((5, 12))
+    g = r.standard_normal(12)
+    b = r.standard_normal(12)
+    base = impl.layer_norm(U, np.ones(12), np.zeros(12), 1e-5)
+    assert np.allclose(impl.layer_norm(U, g, b, 1e-5), g * base + b, atol=1e-14)
+    assert np.allclose(impl.layer_norm(U + 7.25, np.ones(12), np.zeros(12), 1e-5), base, atol=1e-12)
+    n0 = impl.layer_norm(U, np.ones(12), np.zeros(12), 0.0)
+    assert np.allclose(impl.layer_norm(3.5 * U, np.ones(12), np.zeros(12), 0.0), n0, atol=1e-13)
+    assert np.allclose(impl.layer_norm(-2.0 * U, np.ones(12), np.zeros(12), 0.0), -n0, atol=1e-13)
+
+
+def check_layernorm_bruteforce(impl):
+    """The matrix form against the loop form on a small input."""
+    import oracle
+    r = _rng(23)
+    U = r.standard_normal((4, 9))
+    g = r.standard_normal(9)
+    b = r.standard_normal(9)
+    want = np.array(oracle.layer_norm_bruteforce(U.tolist(), g.tolist(), b.tolist(), 1e-5))
+    assert np.allclose(impl.layer_norm(U, g, b, 1e-5), want, atol=1e-13)
+
+
+def check_ffn_relu_identity(impl):
+    """W1 = W2 = identity, b2 = 0: FFN(x) = max(0, x + b1) -- the bias enters
+    before the ReLU (devpress.csdn.net section 2.3, max(0, x W1 + b1) W2 + b2)."""
+    r = _rng(24)
+    d = 6
+    X = r.standard_normal((5, d))
+    b1 = r.standard_normal(d)
+    I = np.eye(d)
+    out = impl.ffn(X, I, b1, I, np.zeros(d))
+    assert np.allclose(out, np.maximum(0.0, X + b1), atol=1e-15)
+    b2 = r.standard_normal(d)
+    assert np.allclose(impl.ffn(X, I, b1, I, b2), np.maximum(0.0, X + b1) + b2, atol=1e-15)
+
+
+def check_ffn_position_wise(impl):
+    """Each row is transformed on its own (hex4c59.cc section "前馈网络为什么放在
+    注意力后面？": a row does not read another row): permuting rows permutes
+    the outputs, changing one row changes only its output."""
+    r = _rng(25)
+    X = r.standard_normal((6, 5))
+    W1, b1 = r.standard_normal((5, 11)), r.standard_normal(11)
+    W2, b2 = r.standard_normal((11, 5)), r.standard_normal(5)
+    Y = impl.ffn(X, W1, b1, W2, b2)
+    p = r.permutation(6)
+    assert np.allclose(impl.ffn(X[p], W1, b1, W2, b2), Y[p], atol=1e-13)
+    X2 = X.copy()
+    X2[2] += 1.0
+    Y2 = impl.ffn(X2, W1, b1, W2, b2)
+    assert np.allclose(np.delete(Y2, 2, axis=0), np.delete(Y, 2, axis=0), atol=1e-14)
+    assert np.abs(Y2[2] - Y[2]).max() > 1e-6
+
+
+def check_ffn_bruteforce(impl):
+    import oracle
+    r = _rng(26)
+    X = r.standard_normal((3, 4))
+    W1, b1 = r.standard_normal((4, 7)), r.standard_normal(7)
+    W2, b2 = r.standard_normal((7, 4)), r.standard_normal(4)
+    want = np.array(oracle.ffn_bruteforce(X.tolist(), W1.tolist(), b1.tolist(), W2.tolist(), b2.tolist()))
+    assert np.allclose(impl.ffn(X, W1, b1, W2, b2), want, atol=1e-13)
+
+
+def _layer_weights(r, dm, h, d, dff):
+    return dict(Wq=r.standard_normal((dm, h * d)), Wk=r.standard_normal((dm, h * d)),
+                Wv=r.standard_normal((dm, h * d)), Wo=r.standard_normal((h * d, dm)),
+                W1=r.standard_normal((dm, dff)), b1=r.standard_normal(dff),
+                W2=r.standard_normal((dff, dm)), b2=r.standard_normal(dm))
+
+
+def _layer(impl, X, w, h, g1, be1, g2, be2, eps, kind=NONE, kl=None):
+    return impl.encoder_layer_ref(X, w["Wq"], w["Wk"], w["Wv"], w["Wo"], h, g1, be1, w["W1"], w["b1"],
+                                  w["W2"], w["b2"], g2, be2, eps, kind, kl)
+
+
+def check_layer_zero_sublayers(impl):
+    """Post-LN with both sublayers silenced (W^O = 0, W2 = 0, b2 = 0, gamma = 1,
+    beta = 0, eps = 0): each wrapper is LayerNorm(x + 0), so the layer is
+    LayerNorm(LayerNorm(X)) = LayerNorm(X) (standardisation is idempotent).
+    A missing residual, a residual outside the norm, or Pre-LN all differ."""
+    r = _rng(27)
+    B, n, dm, h, d, dff = 2, 5, 8, 2, 4, 16
+    X = r.standard_normal((B, n, dm)) * 2.0 + 0.5
+    w = _layer_weights(r, dm, h, d, dff)
+    w["Wo"] = np.zeros_like(w["Wo"])
+    w["W2"] = np.zeros_like(w["W2"])
+    w["b2"] = np.zeros_like(w["b2"])
+    one, zero = np.ones(dm), np.zeros(dm)
+    out = _layer(impl, X, w, h, one, zero, one, zero, 0.0)
+    mu = X.mean(axis=-1, keepdims=True)
+    sd = np.sqrt(((X - mu) ** 2).mean(axis=-1, keepdims=True))
+    assert np.allclose(out, (X - mu) / sd, atol=1e-12)
+
+
+def check_layer_output_normalised(impl):
+    """The layer ends in LayerNorm: with gamma2 = 1, beta2 = 0, eps = 0 every
+    output row has mean 0 and mean square 1; beta2 then shifts the row mean
+    to mean(beta2)."""
+    r = _rng(28)
+    B, n, dm, h, d, dff = 2, 4, 8, 2, 4, 12
+    X = r.standard_normal((B, n, dm))
+    w = _layer_weights(r, dm, h, d, dff)
+    g1, be1 = r.standard_normal(dm), r.standard_normal(dm)
+    out = _layer(impl, X, w, h, g1, be1, np.ones(dm), np.zeros(dm), 0.0)
+    assert np.allclose(out.mean(axis=-1), 0.0, atol=1e-13)
+    assert np.allclose((out ** 2).mean(axis=-1), 1.0, atol=1e-12)
+    be2 = r.standard_normal(dm)
+    out2 = _layer(impl, X, w, h, g1, be1, np.ones(dm), be2, 0.0)
+    assert np.allclose(out2.mean(axis=-1), be2.mean(), atol=1e-13)
+
+
+def check_layer_ffn_residual(impl):
+    """With W2 = 0 the FFN sublayer is the constant b2: a b2 that is the same
+    for every feature is removed by the second norm (shift invariance), a
+    b2 that varies across features is not -- the FFN output is added to x1
+    inside the norm."""
+    r = _rng(29)
+    B, n, dm, h, d, dff = 1, 4, 6, 2, 3, 8
+    X = r.standard_normal((B, n, dm))
+    w = _layer_weights(r, dm, h, d, dff)
+    w["W2"] = np.zeros_like(w["W2"])
+    one, zero = np.ones(dm), np.zeros(dm)
+    w["b2"] = np.zeros(dm)
+    base = _layer(impl, X, w, h, one, zero, one, zero, 1e-5)
+    w["b2"] = np.full(dm, 3.0)
+    assert np.allclose(_layer(impl, X, w, h, one, zero, one, zero, 1e-5), base, atol=1e-12)
+    w["b2"] = np.linspace(-1.0, 1.0, dm)
+    assert np.abs(_layer(impl, X, w, h, one, zero, one, zero, 1e-5) - base).max() > 1e-3
+
+
+def check_layer_bruteforce(impl):
+    """Tiny layer against the loop forms of every step (multi-head block,
+    LayerNorm, FFN), composed in the pages' order, with a padding mask."""
+    import oracle
+    r = _rng(30)
+    B, n, dm, h, d, dff = 2, 3, 4, 2, 2, 6
+    X = r.standard_normal((B, n, dm))
+    w = _layer_weights(r, dm, h, d, dff)
+    g1, be1, g2, be2 = (r.standard_normal(dm) for _ in range(4))
+    kl = [3, 2]
+    got = _layer(impl, X, w, h, g1, be1, g2, be2, 1e-5, PAD, np.array(kl))
+    for b in range(B):
+        A = oracle.mha_bruteforce([X[b].tolist()], [X[b].tolist()], w["Wq"].tolist(), w["Wk"].tolist(),
+                                  w["Wv"].tolist(), w["Wo"].tolist(), h, PAD, [kl[b]])[0]
+        s1 = [[X[b][i][j] + A[i][j] for j in range(dm)] for i in range(n)]
+        x1 = oracle.layer_norm_bruteforce(s1, g1.tolist(), be1.tolist(), 1e-5)
+        F = oracle.ffn_bruteforce(x1, w["W1"].tolist(), w["b1"].tolist(), w["W2"].tolist(), w["b2"].tolist())
+        s2 = [[x1[i][j] + F[i][j] for j in range(dm)] for i in range(n)]
+        want = oracle.layer_norm_bruteforce(s2, g2.tolist(), be2.tolist(), 1e-5)
+        assert np.allclose(got[b], np.array(want), atol=1e-12)
+
+
+ALL_LAYER_CHECKS = [
+    check_layernorm_worked_row,
+    check_layernorm_moments,
+    check_layernorm_affine_and_invariances,
+    check_layernorm_bruteforce,
+    check_ffn_relu_identity,
+    check_ffn_position_wise,
+    check_ffn_bruteforce,
+    check_layer_zero_sublayers,
+    check_layer_output_normalised,
+    check_layer_ffn_residual,
+    check_layer_bruteforce,
+]

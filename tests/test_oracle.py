@@ -15,6 +15,11 @@ def test_sdpa_pin(check):
     check(oracle)
 
 
+@pytest.mark.parametrize("check", pins.ALL_LAYER_CHECKS, ids=lambda f: f.__name__)
+def test_layer_pin(check):
+    check(oracle)
+
+
 @pytest.mark.parametrize("check", pins.ALL_MHA_CHECKS, ids=lambda f: f.__name__)
 def test_mha_pin(check):
     check(oracle)

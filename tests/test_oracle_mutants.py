@@ -151,3 +151,79 @@ def test_unmutated_copy_passes_every_pin():
 def test_mutant_is_caught(name):
     failed = _fails_some_pin(MUTANTS[name]())
     assert failed, f"planted mistake {name!r} passed every pin"
+
+
+# ------------------------------------------------------------ encoder layer mutants
+
+def _ln(var_ddof=0, eps_on=True, affine_swap=False):
+    def layer_norm(U, gamma, beta, eps):
+        U = np.asarray(U, dtype=np.float64)
+        mu = U.mean(axis=-1, keepdims=True)
+        var = U.var(axis=-1, ddof=var_ddof, keepdims=True)
+        z = (U - mu) / np.sqrt(var + (eps if eps_on else 0.0))
+        return (z * beta + gamma) if affine_swap else (gamma * z + beta)
+    return layer_norm
+
+
+def _ffn(relu=True, bias_after_relu=False):
+    def ffn(X, W1, b1, W2, b2):
+        H = np.asarray(X, dtype=np.float64) @ W1
+        if not bias_after_relu:
+            H = H + b1
+        if relu:
+            H = np.maximum(0.0, H)
+        if bias_after_relu:
+            H = H + b1
+        return H @ W2 + b2
+    return ffn
+
+
+def _build_layer(layer_norm=None, ffn=None, order="post", residual=True):
+    layer_norm = layer_norm or oracle.layer_norm
+    ffn = ffn or oracle.ffn
+
+    def encoder_layer_ref(X, Wq, Wk, Wv, Wo, h, g1, be1, W1, b1, W2, b2, g2, be2, eps,
+                          mask_kind=0, key_lengths=None):
+        X = np.asarray(X, dtype=np.float64)
+        r = 1.0 if residual else 0.0
+        if order == "pre":  # x + Sublayer(LayerNorm(x))
+            Xn = layer_norm(X, g1, be1, eps)
+            x1 = X + oracle.mha_ref(Xn, Xn, Wq, Wk, Wv, Wo, h, mask_kind, key_lengths)
+            return x1 + ffn(layer_norm(x1, g2, be2, eps), W1, b1, W2, b2)
+        A = oracle.mha_ref(X, X, Wq, Wk, Wv, Wo, h, mask_kind, key_lengths)
+        x1 = layer_norm(r * X + A, g1, be1, eps)
+        return layer_norm(r * x1 + ffn(x1, W1, b1, W2, b2), g2, be2, eps)
+
+    return types.SimpleNamespace(layer_norm=layer_norm, ffn=ffn, encoder_layer_ref=encoder_layer_ref)
+
+
+LAYER_MUTANTS = {
+    "ln_unbiased_variance": lambda: _build_layer(layer_norm=_ln(var_ddof=1)),
+    "ln_eps_dropped": lambda: _build_layer(layer_norm=_ln(eps_on=False)),
+    "ln_gamma_beta_swapped": lambda: _build_layer(layer_norm=_ln(affine_swap=True)),
+    "ffn_no_relu": lambda: _build_layer(ffn=_ffn(relu=False)),
+    "ffn_bias_after_relu": lambda: _build_layer(ffn=_ffn(bias_after_relu=True)),
+    "layer_pre_ln": lambda: _build_layer(order="pre"),
+    "layer_no_residual": lambda: _build_layer(residual=False),
+}
+
+
+def _fails_some_layer_pin(impl):
+    failed = []
+    for check in pins.ALL_LAYER_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check(impl)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            failed.append(check.__name__)
+    return failed
+
+
+def test_unmutated_layer_copy_passes_every_pin():
+    assert _fails_some_layer_pin(_build_layer()) == []
+
+
+@pytest.mark.parametrize("name", sorted(LAYER_MUTANTS))
+def test_layer_mutant_is_caught(name):
+    failed = _fails_some_layer_pin(LAYER_MUTANTS[name]())
+    assert failed, f"planted mistake {name!r} passed every pin"
