@@ -4,7 +4,8 @@
 
 A step is one pass of the whole path over one batch: for a multi-head block
 the input projection(s), the fused attention and the output projection; for
-bare attention the fused attention kernel.  Inputs are seeded synthetic
+bare attention the fused attention kernel; for an encoder layer the block,
+residual + LayerNorm, the two FFN GEMMs and residual + LayerNorm.  Inputs are seeded synthetic
 tensors of the workload's shapes, resident in GPU memory before timing, and
 rotated through enough buffer sets that every step reads memory no earlier
 step left in the 256 MB Infinity Cache.
@@ -66,6 +67,20 @@ def mha_launches(w):
     return n
 
 
+def layer_launches(w):
+    from head_attention_forward_amd import _binding as bnd
+    n = bnd.lib().encoder_layer_launches(w.n_q, w.d_model)
+    if n < 0:
+        raise RuntimeError(f"encoder_layer_launches failed with status {n}")
+    return n
+
+
+def step_launches(w):
+    if w.kind == "sdpa":
+        return 1
+    return layer_launches(w) if w.kind == "layer" else mha_launches(w)
+
+
 def kernel_plan(w, n_launches=None):
     """Launch order of one step with each kernel's algorithmic flops and bytes
     (bytes: every input element read once, every output written once).  The
@@ -75,15 +90,23 @@ def kernel_plan(w, n_launches=None):
     B, h, nq, nk, dk, dv = w.B, w.h, w.n_q, w.n_k, w.d_k, w.d_v
     plan = []
 
-    def gemm(name, M, K, N):
-        plan.append(dict(name=name, flops=2.0 * M * K * N, bytes=float(e * (M * K + K * N + M * N)),
+    def gemm(name, M, K, N, bias=False):
+        plan.append(dict(name=name, flops=2.0 * M * K * N,
+                         bytes=float(e * (M * K + K * N + M * N + (N if bias else 0))),
                          peak_kind="mfma", has_attention=False))
+
+    def layernorm(name, M, d):
+        # read x and the sublayer output, gamma and beta; write the result
+        plan.append(dict(name=name, flops=0.0, bytes=float(e * (3 * M * d + 2 * d)),
+                         peak_kind="hbm", has_attention=False))
 
     if w.kind == "sdpa":
         plan.append(dict(name="attention", flops=0.0, bytes=0.0,
                          peak_kind="mfma" if w.dtype == "bf16" else "fp32", has_attention=True))
         return plan, None
-    n = mha_launches(w) if n_launches is None else n_launches
+    n = step_launches(w) if n_launches is None else n_launches
+    if w.kind == "layer":
+        n -= 4  # the block's own launches
     if n == 2:
         dm = w.d_model
         flops = 2.0 * B * nq * dm * h * dk + 2.0 * B * nk * dm * h * (dk + dv)
@@ -99,6 +122,12 @@ def kernel_plan(w, n_launches=None):
             gemm("kv_projection_gemm", B * nk, w.d_model, h * (dk + dv))
         plan.append(dict(name="attention", flops=0.0, bytes=0.0, peak_kind="mfma", has_attention=True))
     gemm("output_projection_gemm", B * nq, h * dv, w.d_model)
+    if w.kind == "layer":
+        M = B * nq
+        layernorm("residual_layernorm_1", M, w.d_model)
+        gemm("ffn_gemm_1", M, w.d_model, w.d_ff, bias=True)
+        gemm("ffn_gemm_2", M, w.d_ff, w.d_model, bias=True)
+        layernorm("residual_layernorm_2", M, w.d_model)
     return plan, None
 
 
@@ -155,6 +184,17 @@ class Step:
                 self.sets.append((P(Q.data_ptr()), P(K.data_ptr()), P(V.data_ptr()), P(O.data_ptr()),
                                   w.B, w.h, w.n_q, w.n_k, w.d_k, w.d_v, float(x["scale"]), w.mask,
                                   self.kl, code))
+            elif w.kind == "layer":
+                X = x["X"].to(dev)
+                ps = [x[k].to(dev) for k in bnd.LAYER_PARAMS]
+                Y = torch.empty_like(X)
+                nbytes = bnd.encoder_layer_workspace_bytes(w.B, w.n_q, w.d_model, w.h, w.d_k,
+                                                           w.d_v, w.d_ff)
+                ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+                self.keep.append((X, ps, ws, Y))
+                self.sets.append((P(X.data_ptr()), *[P(t.data_ptr()) for t in ps], P(Y.data_ptr()),
+                                  w.B, w.n_q, w.d_model, w.h, w.d_k, w.d_v, w.d_ff, float(w.eps),
+                                  w.mask, self.kl, bnd.DTYPE_BF16, P(ws.data_ptr()), nbytes))
             else:
                 Xq = x["X_q"].to(dev)
                 Xkv = Xq if w.self_attn else x["X_kv"].to(dev)
@@ -166,19 +206,20 @@ class Step:
                                   *[P(t.data_ptr()) for t in Ws], P(Y.data_ptr()),
                                   w.B, w.n_q, w.n_k, w.d_model, w.h, w.d_k, w.d_v, w.mask, self.kl,
                                   bnd.DTYPE_BF16, P(ws.data_ptr()), ws.numel()))
-        self.n_launches = 1 if w.kind == "sdpa" else mha_launches(w)
+        self.n_launches = step_launches(w)
+        names = {"sdpa": "sdpa_forward", "mha": "mha_forward", "layer": "encoder_layer_forward"}
+        self.entry = names[w.kind]
 
     def output(self, i):
         return self.keep[i][3]
 
     def run(self, i, stream):
-        f = self.lib.sdpa_forward if self.w.kind == "sdpa" else self.lib.mha_forward
-        st = f(*self.sets[i], stream)
+        st = getattr(self.lib, self.entry)(*self.sets[i], stream)
         if st != 0:
             raise RuntimeError(f"launch failed with status {st}")
 
     def run_timed(self, i, stream, events_ptr, cap):
-        f = self.lib.sdpa_forward_timed if self.w.kind == "sdpa" else self.lib.mha_forward_timed
+        f = getattr(self.lib, self.entry + "_timed")
         n = ctypes.c_int()
         st = f(*self.sets[i], stream, events_ptr, cap, ctypes.byref(n))
         if st != 0 or n.value != self.n_launches:
@@ -192,7 +233,19 @@ def set_bytes(w):
     xs = w.B * w.n_q * w.d_model * (1 if w.self_attn else 1) + (0 if w.self_attn else w.B * w.n_k * w.d_model)
     ws = w.B * w.h * (w.n_q * w.d_k + w.n_k * (w.d_k + w.d_v) + w.n_q * w.d_v)
     weights = w.d_model * w.h * (2 * w.d_k + w.d_v) + w.h * w.d_v * w.d_model
-    return e * (xs + ws + weights + w.B * w.n_q * w.d_model)
+    total = xs + ws + weights + w.B * w.n_q * w.d_model
+    if w.kind == "layer":
+        M, D, F = w.B * w.n_q, w.d_model, w.d_ff
+        total += 2 * M * D + M * F + 2 * D * F + F + 5 * D  # S, x1, H; FFN and LayerNorm parameters
+    return e * total
+
+
+def layer_flops(w):
+    """All matrix-product flops of one encoder-layer step (projections,
+    attention at nominal dense count, FFN)."""
+    M, D, F = w.B * w.n_q, w.d_model, w.d_ff
+    proj = 2.0 * M * D * w.h * (2 * w.d_k + w.d_v) + 2.0 * M * w.h * w.d_v * D
+    return proj + w.nominal_attention_flops() + 4.0 * M * D * F
 
 
 # ----------------------------------------------------------------------------- parity
@@ -205,6 +258,18 @@ def parity_check(w, x, out):
     from head_attention_forward_amd.workloads import to_f64
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
     rows = "all"
+    if w.kind == "layer":
+        from head_attention_forward_amd._binding import LAYER_PARAMS
+        p = [to_f64(x[k]) for k in LAYER_PARAMS]
+        want = oracle.encoder_layer_ref(to_f64(x["X"]), *p[:4], w.h, *p[4:], w.eps, w.mask, kl)
+        got = to_f64(out)
+        err = got - want
+        # elementwise 2e-2 + 2u|want| (u = 2^-8, bf16): LayerNorm outputs reach
+        # magnitude ~5, where the output's own rounding is already u * 5
+        worst = float((np.abs(err) / (2e-2 + 2 * 2.0 ** -8 * np.abs(want))).max())
+        rel = float(np.linalg.norm(err) / np.linalg.norm(want))
+        return dict(max_abs=float(np.abs(err).max()), rel_l2=rel, worst_over_bound=worst,
+                    ok=bool(worst <= 1.0 and rel <= 5e-3), rows=rows)
     if w.kind == "mha":
         want = oracle.mha_ref(to_f64(x["X_q"]), to_f64(x["X_kv"]),
                               *[to_f64(x[k]) for k in ("Wq", "Wk", "Wv", "Wo")], w.h, w.mask, kl)
@@ -248,7 +313,17 @@ def cpu_baseline(w, x, target_s):
         threads = 1
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
 
-    if w.kind == "mha":
+    if w.kind == "layer":
+        from head_attention_forward_amd._binding import LAYER_PARAMS
+        X = to_f64(x["X"])
+        p = [to_f64(x[k]) for k in LAYER_PARAMS]
+
+        def run(b):
+            oracle.encoder_layer_ref(X[:b], *p[:4], w.h, *p[4:], w.eps, w.mask,
+                                     None if kl is None else kl[:b])
+        unit_flops = 4.0 * w.h * w.n_q * w.n_k * w.d_k  # per sequence, the metric's count
+        n_units, what = w.B, "sequences (whole encoder layers)"
+    elif w.kind == "mha":
         Xq, Xkv = to_f64(x["X_q"]), to_f64(x["X_kv"])
         Ws = [to_f64(x[k]) for k in ("Wq", "Wk", "Wv", "Wo")]
 
@@ -298,6 +373,7 @@ KERNEL_SOURCES = {
     "attn_fwd_f32_d64_kernel": ("attn_f32.hip",),
     "proj_attn_bf16_kernel": ("proj_attn_bf16.hip", "wave_attention.h", "mha_api.hip"),
     "gemm_bf16_kernel": ("gemm_bf16.hip", "mha_api.hip"),
+    "add_layernorm_bf16_kernel": ("add_layernorm_bf16.hip", "mha_api.hip"),
 }
 
 
@@ -488,12 +564,16 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: {n} bytes read, {n} bytes written")
 
+    kinds = {"mha": "multi-head block (projections + attention + output projection)",
+             "sdpa": "bare attention",
+             "layer": "encoder layer, Post-LN (block, residual + LayerNorm, FFN, residual + LayerNorm)"}
     cfg = dict(workload=w.name, B=w.B, n_q=w.n_q, n_k=w.n_k, h=w.h, d_k=w.d_k, d_v=w.d_v,
                mask={0: "none", 1: "causal", 2: "key_padding", 3: "causal+key_padding"}[w.mask],
-               kind="multi-head block (projections + attention + output projection)"
-               if w.kind == "mha" else "bare attention", buffer_sets=sets)
-    if w.kind == "mha":
+               kind=kinds[w.kind], buffer_sets=sets)
+    if w.kind in ("mha", "layer"):
         cfg.update(d_model=w.d_model, self_attention=w.self_attn)
+    if w.kind == "layer":
+        cfg.update(d_ff=w.d_ff, eps=w.eps)
     if x["key_lengths"] is not None:
         cfg["key_lengths_mean"] = float(x["key_lengths"].float().mean())
     out = {
@@ -527,6 +607,13 @@ def main():
         "parity": parity,
         "kernel_source_sha": kernel_source_sha(),
     }
+    if w.kind == "layer":
+        lf = layer_flops(w)
+        out["layer"] = dict(matmul_flops_per_step=lf,
+                            tflops=round(lf / (ms_step * 1e-3) / 1e12, 2),
+                            tokens_per_s=round(w.B * w.n_q / (ms_step * 1e-3), 1))
+        out["data"] = ("synthetic (seeded N(0,1) activations, N(0,1/fan_in) weights, "
+                       "0.1*N(0,1) biases and LayerNorm shifts, 1+0.1*N(0,1) LayerNorm scales)")
     print(json.dumps(out), flush=True)
 
 

@@ -6,7 +6,12 @@ synthetic workloads used by the tests and the bench.
 """
 
 from ._binding import (  # noqa: F401
+    LAYER_PARAMS,
     MHAError,
+    add_layernorm_forward,
+    encoder_layer_forward,
+    encoder_layer_workspace_bytes,
+    ffn_forward,
     alloc_workspace,
     lib,
     mha_attend,

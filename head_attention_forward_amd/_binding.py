@@ -45,6 +45,15 @@ _SIG = {
                                 _P, _P, _I, _P]),
     "mha_forward_timed": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _I,
                                _P, ctypes.c_size_t, _P, _P, _I, _P]),
+    "add_layernorm_forward": (_I, [_P, _P, _P, _P, _P, _I, _I, ctypes.c_float, _I, _P]),
+    "ffn_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "ffn_forward": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _P, ctypes.c_size_t, _P]),
+    "encoder_layer_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I, _I]),
+    "encoder_layer_forward": (_I, [_P] * 14 + [_I] * 7 + [ctypes.c_float, _I, _P, _I, _P,
+                                                        ctypes.c_size_t, _P]),
+    "encoder_layer_forward_timed": (_I, [_P] * 14 + [_I] * 7 + [ctypes.c_float, _I, _P, _I, _P,
+                                                              ctypes.c_size_t, _P, _P, _I, _P]),
+    "encoder_layer_launches": (_I, [_I, _I]),
 }
 
 _lib = None
@@ -237,3 +246,85 @@ def workspace_views(workspace, B, n_q, n_k, h, d_k, d_v):
         return flat[offs[i]:offs[i] + e * sizes[i]].view(torch.bfloat16).view(*shape)
     return (view(0, (B, h, n_q, d_k)), view(1, (B, h, n_k, d_k)), view(2, (B, h, n_k, d_v)),
             view(3, (B, n_q, h * d_v)))
+
+
+def add_layernorm_forward(X, F, gamma, beta, eps=1e-5, out=None, stream=None):
+    """Y = LayerNorm(X + F) over the last axis (population variance), scaled
+    by gamma and shifted by beta.  X, F [..., d] bf16 on the GPU; out may be
+    X or F."""
+    d = X.shape[-1]
+    if F.shape != X.shape or gamma.shape != (d,) or beta.shape != (d,):
+        raise ValueError("X, F, gamma, beta shapes disagree")
+    M = X.numel() // d
+    if out is None:
+        out = torch.empty_like(X)
+    elif out.shape != X.shape or out.dtype != X.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    st = lib().add_layernorm_forward(_dev(X, "X"), _dev(F, "F"), _dev(gamma, "gamma"),
+                                     _dev(beta, "beta"), _dev(out, "out"), M, d, float(eps),
+                                     _dtype_code(X), _stream(stream))
+    _check("add_layernorm_forward", st)
+    return out
+
+
+def ffn_forward(X, W1, b1, W2, b2, out=None, workspace=None, stream=None):
+    """Y = max(0, X W1 + b1) W2 + b2 on every row.  X [..., d_model] bf16 on
+    the GPU, W1 [d_model][d_ff], W2 [d_ff][d_model]."""
+    d_model = X.shape[-1]
+    d_ff = W1.shape[1]
+    if W1.shape != (d_model, d_ff) or b1.shape != (d_ff,) or W2.shape != (d_ff, d_model) \
+            or b2.shape != (d_model,):
+        raise ValueError("FFN weight shapes disagree")
+    M = X.numel() // d_model
+    code = _dtype_code(X)
+    if out is None:
+        out = torch.empty_like(X)
+    if workspace is None:
+        n = int(lib().ffn_workspace_bytes(M, d_model, d_ff, code))
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=X.device)
+    st = lib().ffn_forward(_dev(X, "X"), _dev(W1, "W1"), _dev(b1, "b1"), _dev(W2, "W2"),
+                           _dev(b2, "b2"), _dev(out, "out"), M, d_model, d_ff, code,
+                           _dev(workspace, "workspace"),
+                           workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("ffn_forward", st)
+    return out
+
+
+LAYER_PARAMS = ("Wq", "Wk", "Wv", "Wo", "ln1_gamma", "ln1_beta", "W1", "b1", "W2", "b2",
+                "ln2_gamma", "ln2_beta")
+
+
+def encoder_layer_workspace_bytes(B, n, d_model, h, d_k, d_v, d_ff, dtype=torch.bfloat16):
+    code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_F32
+    return int(lib().encoder_layer_workspace_bytes(B, n, d_model, h, d_k, d_v, d_ff, code))
+
+
+def _layer_dims(X, p, h):
+    B, n, d_model = X.shape
+    d_k = p["Wq"].shape[1] // h
+    d_v = p["Wv"].shape[1] // h
+    d_ff = p["W1"].shape[1]
+    return B, n, d_model, d_k, d_v, d_ff
+
+
+def encoder_layer_forward(X, params, h, eps=1e-5, mask_kind=0, key_lengths=None, out=None,
+                          workspace=None, stream=None):
+    """One Post-LN encoder layer: x1 = LN1(X + MultiHead(X)), Y = LN2(x1 + FFN(x1)).
+
+    X [B][n][d_model] bf16 on the GPU; params maps the names in LAYER_PARAMS to
+    GPU tensors (Wq, Wk, Wv [d_model][h*d], Wo [h*d][d_model], W1 [d_model][d_ff],
+    b1 [d_ff], W2 [d_ff][d_model], the other vectors [d_model])."""
+    B, n, d_model, d_k, d_v, d_ff = _layer_dims(X, params, h)
+    if out is None:
+        out = torch.empty_like(X)
+    if workspace is None:
+        nbytes = encoder_layer_workspace_bytes(B, n, d_model, h, d_k, d_v, d_ff, X.dtype)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X.device)
+    arr, kl = _key_lengths(mask_kind, key_lengths, B)
+    ptrs = [_dev(params[k], k) for k in LAYER_PARAMS]
+    st = lib().encoder_layer_forward(_dev(X, "X"), *ptrs, _dev(out, "out"), B, n, d_model, h, d_k,
+                                     d_v, d_ff, float(eps), int(mask_kind), kl, _dtype_code(X),
+                                     _dev(workspace, "workspace"),
+                                     workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("encoder_layer_forward", st)
+    return out

@@ -284,6 +284,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
     __bf16* base = (__bf16*)seg_field(g, s, &GemmSeg::dst) + (int64_t)head * rows * hd +
                    (c - head * hd) + 4 * grp;
     const int64_t bstride = (int64_t)heads * rows * hd;
+    // Bias of this lane's columns nb + 8q + 4grp .. +3 (zero without one).
+    f32x4 bq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      bq[q] = f32x4{};
+      if (g.bias != nullptr && nb + 8 * q < N)
+        bq[q] = __builtin_convertvector(*(const bf16x4*)((const __bf16*)g.bias + nb + 8 * q + 4 * grp),
+                                        f32x4);
+    }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       const int m = m0 + wm * (BM / WM) + 32 * i + col;
@@ -296,7 +305,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
         if (nb + 8 * q >= N) continue;
         f32x4 v;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+        for (int r = 0; r < 4; ++r) {
+          v[r] = acc[i][j][4 * q + r] + bq[q][r];
+          if (g.relu) v[r] = fmaxf(v[r], 0.f);
+        }
         *(bf16x4*)(dst + 8 * q) = __builtin_convertvector(v, bf16x4);
       }
     }

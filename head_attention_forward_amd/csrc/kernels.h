@@ -47,6 +47,23 @@ struct GemmArgs {
   int nseg;
   GemmSeg seg[3];
   int col_start[4];   // prefix sums of segment widths; col_start[nseg] = N
+  // Epilogue (single-segment GEMMs only): bias[N] (bf16, may be null) is
+  // added to every row before rounding, then max(0, .) when relu != 0.
+  const void* bias;
+  int relu;
+};
+
+// Residual + LayerNorm over rows of d features (bf16):
+//   Y[m] = gamma * norm(X[m] + F[m]) + beta,  norm(u) = (u - mean) / sqrt(var + eps)
+constexpr int kLnMaxWidth = 4096;
+struct LnArgs {
+  const void* X;      // [M][d]
+  const void* F;      // [M][d]
+  const void* gamma;  // [d]
+  const void* beta;   // [d]
+  void* Y;            // [M][d]; may be X or F
+  int M, d;
+  float eps;
 };
 
 // Fused input projections + attention for short sequences (n_q, n_k <= 128,
@@ -82,6 +99,7 @@ hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents e
 hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_add_layernorm_bf16(const LnArgs& a, hipStream_t s, LaunchEvents ev = {});
 bool proj_attn_supported(int n_q, int n_k, int d_model);
 hipError_t launch_proj_attn_bf16(const ProjAttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 // One fixed tile configuration (index into the instantiated set); for sweeps.

@@ -12,6 +12,9 @@ namespace mha {
 namespace {
 
 constexpr int64_t kIndexLimit = (int64_t)1 << 31;  // row/column counts stay int32
+// GEMM operand widths (d_model, h*d_k, h*d_v, d_ff): a stage's per-lane byte
+// offsets (up to 128 rows of a row-major operand) stay within 32 bits.
+constexpr int64_t kMaxWidth = (int64_t)1 << 20;
 constexpr size_t kAlign = 256;
 
 size_t elt_size(int dtype) { return dtype == MHA_DTYPE_F32 ? 4 : 2; }
@@ -82,9 +85,10 @@ int check_block(const void* ws, size_t ws_bytes, int B, int n_q, int n_k, int h,
 // The projections additionally need d_model rows in whole 16-byte chunks.
 int check_mha(const void* ws, size_t ws_bytes, int B, int n_q, int n_k, int d_model, int h,
               int d_k, int d_v, int dtype) {
-  if (d_model <= 0 || d_model >= kIndexLimit / 8) return MHA_ERR_DIM;
+  if (d_model <= 0 || d_model > kMaxWidth) return MHA_ERR_DIM;
   int st = check_block(ws, ws_bytes, B, n_q, n_k, h, d_k, d_v, dtype);
   if (st != MHA_OK) return st;
+  if ((int64_t)h * d_k > kMaxWidth || (int64_t)h * d_v > kMaxWidth) return MHA_ERR_DIM;
   if (d_model % 8 != 0) return MHA_ERR_UNSUPPORTED;
   return MHA_OK;
 }
@@ -209,6 +213,83 @@ int do_project_out(const void* Wo, void* Y, int B, int n_q, int d_model, int h, 
   g.col_start[0] = 0;
   g.col_start[1] = d_model;
   return launch_status(launch_gemm_bf16(g, stream, next_events(tm)));
+}
+
+// Plain row-major GEMM Y[M][N] = A[M][K] . W[K][N] (+ bias, ReLU).
+int do_linear(const void* A, const void* W, const void* bias, int relu, void* Y, int M, int K,
+              int N, hipStream_t stream, Timer* tm) {
+  GemmArgs g{};
+  g.A = A;
+  g.M = M;
+  g.K = K;
+  g.nseg = 1;
+  g.seg[0] = GemmSeg{W, Y, N, N, 1, M};
+  g.col_start[0] = 0;
+  g.col_start[1] = N;
+  g.bias = bias;
+  g.relu = relu;
+  return launch_status(launch_gemm_bf16(g, stream, next_events(tm)));
+}
+
+int do_add_layernorm(const void* X, const void* F, const void* gamma, const void* beta, void* Y,
+                     int M, int d, float eps, hipStream_t stream, Timer* tm) {
+  LnArgs a{X, F, gamma, beta, Y, M, d, eps};
+  return launch_status(launch_add_layernorm_bf16(a, stream, next_events(tm)));
+}
+
+int check_ln(int M, int d, float eps, int dtype) {
+  if (M <= 0 || d <= 0 || (int64_t)M * d >= ((int64_t)1 << 40)) return MHA_ERR_DIM;
+  if (!(isfinite(eps) && eps >= 0.f)) return MHA_ERR_SCALE;
+  if (dtype != MHA_DTYPE_BF16) return MHA_ERR_UNSUPPORTED;
+  if (d % 8 != 0 || d > kLnMaxWidth) return MHA_ERR_UNSUPPORTED;
+  return MHA_OK;
+}
+
+// Rows and widths of the feed-forward GEMMs: whole 16-byte chunks.
+int check_ffn(int M, int d_model, int d_ff, int dtype) {
+  if (M <= 0 || d_model <= 0 || d_ff <= 0) return MHA_ERR_DIM;
+  if (M >= kIndexLimit || d_model > kMaxWidth || d_ff > kMaxWidth) return MHA_ERR_DIM;
+  if (dtype != MHA_DTYPE_BF16) return MHA_ERR_UNSUPPORTED;
+  if (d_model % 8 != 0 || d_ff % 8 != 0) return MHA_ERR_UNSUPPORTED;
+  return MHA_OK;
+}
+
+size_t ffn_ws(int M, int d_ff) { return round_up((size_t)2 * M * d_ff); }
+
+int do_ffn(const void* X, const void* W1, const void* b1, const void* W2, const void* b2, void* Y,
+           int M, int d_model, int d_ff, void* H, hipStream_t stream, Timer* tm) {
+  int st = do_linear(X, W1, b1, 1, H, M, d_model, d_ff, stream, tm);
+  if (st != MHA_OK) return st;
+  return do_linear(H, W2, b2, 0, Y, M, d_ff, d_model, stream, tm);
+}
+
+// Encoder-layer workspace: the block's workspace, then the sublayer output
+// S [M][d_model] (attention output, later the FFN output), x1 [M][d_model]
+// and the FFN hidden layer H [M][d_ff].
+struct LayerWorkspace {
+  Workspace blk;
+  void* S;
+  void* x1;
+  void* H;
+  size_t bytes;
+};
+
+LayerWorkspace carve_layer(void* base, int B, int n, int d_model, int h, int d_k, int d_v,
+                           int d_ff) {
+  LayerWorkspace w;
+  w.blk = carve(base, B, n, n, h, d_k, d_v, MHA_DTYPE_BF16);
+  const size_t M = (size_t)B * n;
+  const size_t act = round_up(2 * M * d_model);
+  char* p = (char*)base + w.blk.bytes;
+  w.S = p;
+  w.x1 = p + act;
+  w.H = p + 2 * act;
+  w.bytes = w.blk.bytes + 2 * act + ffn_ws((int)M, d_ff);
+  return w;
+}
+
+int layer_launch_count(int n, int d_model) {
+  return (use_fused(n, n, d_model) ? 2 : 3) + 4;
 }
 
 }  // namespace
@@ -398,6 +479,119 @@ int mha_forward_timed(const void* X_q, const void* X_kv, const void* Wq, const v
   Timer tm{events, capacity, 0};
   const int st = mha_impl(X_q, X_kv, Wq, Wk, Wv, Wo, Y, B, n_q, n_k, d_model, h, d_k, d_v,
                           mask_kind, key_lengths, dtype, workspace, workspace_bytes, stream, &tm);
+  if (n_launches) *n_launches = tm.used;
+  return st;
+}
+
+int add_layernorm_forward(const void* X, const void* F, const void* gamma, const void* beta,
+                          void* Y, int M, int d, float eps, int dtype, hipStream_t stream) {
+  if (!X || !F || !gamma || !beta || !Y) return MHA_ERR_NULL;
+  const int st = check_ln(M, d, eps, dtype);
+  if (st != MHA_OK) return st;
+  if (!aligned16(X) || !aligned16(F) || !aligned16(gamma) || !aligned16(beta) || !aligned16(Y))
+    return MHA_ERR_UNSUPPORTED;
+  return do_add_layernorm(X, F, gamma, beta, Y, M, d, eps, stream, nullptr);
+}
+
+size_t ffn_workspace_bytes(int M, int d_model, int d_ff, int dtype) {
+  if (check_ffn(M, d_model, d_ff, dtype) != MHA_OK) return 0;
+  return ffn_ws(M, d_ff);
+}
+
+int ffn_forward(const void* X, const void* W1, const void* b1, const void* W2, const void* b2,
+                void* Y, int M, int d_model, int d_ff, int dtype, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  if (!X || !W1 || !b1 || !W2 || !b2 || !Y) return MHA_ERR_NULL;
+  int st = check_ffn(M, d_model, d_ff, dtype);
+  if (st != MHA_OK) return st;
+  if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0 ||
+      workspace_bytes < ffn_ws(M, d_ff))
+    return MHA_ERR_WORKSPACE;
+  if (!aligned16(X) || !aligned16(W1) || !aligned16(b1) || !aligned16(W2) || !aligned16(b2) ||
+      !aligned16(Y))
+    return MHA_ERR_UNSUPPORTED;
+  return do_ffn(X, W1, b1, W2, b2, Y, M, d_model, d_ff, workspace, stream, nullptr);
+}
+
+size_t encoder_layer_workspace_bytes(int B, int n, int d_model, int h, int d_k, int d_v, int d_ff,
+                                     int dtype) {
+  if (B <= 0 || n <= 0 || d_model <= 0 || h <= 0 || d_k <= 0 || d_v <= 0 || d_ff <= 0) return 0;
+  if (dtype != MHA_DTYPE_BF16) return 0;
+  if ((int64_t)B * n >= kIndexLimit) return 0;
+  return carve_layer(nullptr, B, n, d_model, h, d_k, d_v, d_ff).bytes;
+}
+
+int encoder_layer_launches(int n, int d_model) {
+  if (n <= 0 || d_model <= 0) return MHA_ERR_DIM;
+  return layer_launch_count(n, d_model);
+}
+
+static int layer_impl(const void* X, const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                      const void* g1, const void* be1, const void* W1, const void* b1,
+                      const void* W2, const void* b2, const void* g2, const void* be2, void* Y,
+                      int B, int n, int d_model, int h, int d_k, int d_v, int d_ff, float eps,
+                      int mask_kind, const int32_t* key_lengths, int dtype, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, Timer* tm) {
+  if (!X || !Wq || !Wk || !Wv || !Wo || !g1 || !be1 || !W1 || !b1 || !W2 || !b2 || !g2 || !be2 ||
+      !Y)
+    return MHA_ERR_NULL;
+  int st = check_attn_dims(B, h, n, n, d_k, d_v);
+  if (st != MHA_OK) return st;
+  st = check_ffn(B * n, d_model, d_ff, dtype);
+  if (st != MHA_OK) return st;
+  st = check_ln(B * n, d_model, eps, dtype);
+  if (st != MHA_OK) return st;
+  st = check_mask(mask_kind, B, n, n, key_lengths);
+  if (st != MHA_OK) return st;
+  if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0 ||
+      workspace_bytes < carve_layer(nullptr, B, n, d_model, h, d_k, d_v, d_ff).bytes)
+    return MHA_ERR_WORKSPACE;
+  const void* ptrs[] = {X, Wq, Wk, Wv, Wo, g1, be1, W1, b1, W2, b2, g2, be2, Y};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MHA_ERR_UNSUPPORTED;
+  const LayerWorkspace w = carve_layer(workspace, B, n, d_model, h, d_k, d_v, d_ff);
+  const int M = B * n;
+  // Sublayer 1: S = MultiHead(X, X, X); x1 = LayerNorm1(X + S).
+  st = mha_impl(X, X, Wq, Wk, Wv, Wo, w.S, B, n, n, d_model, h, d_k, d_v, mask_kind, key_lengths,
+                dtype, workspace, w.blk.bytes, stream, tm);
+  if (st != MHA_OK) return st;
+  st = do_add_layernorm(X, w.S, g1, be1, w.x1, M, d_model, eps, stream, tm);
+  if (st != MHA_OK) return st;
+  // Sublayer 2: S = FFN(x1); Y = LayerNorm2(x1 + S).
+  st = do_ffn(w.x1, W1, b1, W2, b2, w.S, M, d_model, d_ff, w.H, stream, tm);
+  if (st != MHA_OK) return st;
+  return do_add_layernorm(w.x1, w.S, g2, be2, Y, M, d_model, eps, stream, tm);
+}
+
+int encoder_layer_forward(const void* X, const void* Wq, const void* Wk, const void* Wv,
+                          const void* Wo, const void* ln1_gamma, const void* ln1_beta,
+                          const void* W1, const void* b1, const void* W2, const void* b2,
+                          const void* ln2_gamma, const void* ln2_beta, void* Y, int B, int n,
+                          int d_model, int h, int d_k, int d_v, int d_ff, float eps,
+                          int mask_kind, const int32_t* key_lengths, int dtype, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return layer_impl(X, Wq, Wk, Wv, Wo, ln1_gamma, ln1_beta, W1, b1, W2, b2, ln2_gamma, ln2_beta, Y,
+                    B, n, d_model, h, d_k, d_v, d_ff, eps, mask_kind, key_lengths, dtype,
+                    workspace, workspace_bytes, stream, nullptr);
+}
+
+int encoder_layer_forward_timed(const void* X, const void* Wq, const void* Wk, const void* Wv,
+                                const void* Wo, const void* ln1_gamma, const void* ln1_beta,
+                                const void* W1, const void* b1, const void* W2, const void* b2,
+                                const void* ln2_gamma, const void* ln2_beta, void* Y, int B,
+                                int n, int d_model, int h, int d_k, int d_v, int d_ff, float eps,
+                                int mask_kind, const int32_t* key_lengths, int dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* events, int capacity, int* n_launches) {
+  if (n <= 0 || d_model <= 0) return MHA_ERR_DIM;
+  const int need = 2 * layer_launch_count(n, d_model);
+  if (events == nullptr || capacity < need) return MHA_ERR_EVENTS;
+  for (int i = 0; i < need; ++i)
+    if (events[i] == nullptr) return MHA_ERR_EVENTS;
+  Timer tm{events, capacity, 0};
+  const int st = layer_impl(X, Wq, Wk, Wv, Wo, ln1_gamma, ln1_beta, W1, b1, W2, b2, ln2_gamma,
+                            ln2_beta, Y, B, n, d_model, h, d_k, d_v, d_ff, eps, mask_kind,
+                            key_lengths, dtype, workspace, workspace_bytes, stream, &tm);
   if (n_launches) *n_launches = tm.used;
   return st;
 }

@@ -19,6 +19,14 @@ the multi-head block and Q, K, V for bare attention; then a round-to-nearest-
 even cast to bf16 (fp32 workloads stay fp32).  Projection weights have
 variance 1/d_model.  Key lengths are integers drawn uniformly from
 [lo, hi] inclusive.
+
+Encoder layer (kind "layer"; the rest of the layer as hex4c59.cc, sections
+"前馈网络为什么放在注意力后面？" and "Add & Norm 里究竟发生了什么？", describe
+it: FFN width 2048 for the base model): draws in the order X, Wq, Wk, Wv,
+Wo, ln1_gamma, ln1_beta, W1, b1, W2, b2, ln2_gamma, ln2_beta, key_lengths.
+W1 has variance 1/d_model, W2 1/d_ff; biases and LayerNorm shifts are
+0.1 * N(0, 1), LayerNorm scales 1 + 0.1 * N(0, 1) (non-trivial values, so
+that every term of the layer shows in its output).
 """
 
 import dataclasses
@@ -49,6 +57,8 @@ class Workload:
     self_attn: bool = False
     key_len_range: Optional[Tuple[int, int]] = None
     description: str = ""
+    d_ff: int = 0        # encoder layer: FFN hidden width
+    eps: float = 1e-5    # encoder layer: LayerNorm epsilon
 
     @property
     def torch_dtype(self):
@@ -93,6 +103,13 @@ WORKLOADS = {
         mask=MASK_KEY_PADDING, key_len_range=(1024, 4096),
         description="bare attention, one query per sequence over a 4096-key cache, bf16, "
                     "B=32 h=16 d=64, cache lengths in [1024,4096]"),
+    # One Post-LN encoder layer of the base model (multi-head self-attention,
+    # residual + LayerNorm, FFN 512 -> 2048 -> 512, residual + LayerNorm) on
+    # the encoder block's batch.
+    "encoder_layer_base": Workload(
+        "encoder_layer_base", "layer", "bf16", B=32, n_q=100, n_k=100, h=8, d_k=64, d_v=64,
+        mask=MASK_NONE, d_model=512, self_attn=True, d_ff=2048, eps=1e-5,
+        description="encoder layer (Post-LN), bf16, B=32 n=100 d_model=512 h=8 d_ff=2048"),
 }
 
 ORDER = ["sdpa_f32_tiny", "encoder_self_base", "decoder_causal_base", "cross_padded_big",
@@ -114,6 +131,9 @@ def generate(w: Workload, seed: int = 0):
     mha:  X_q [B][n_q][d_model], X_kv (the same tensor object for
           self-attention), Wq/Wk [d_model][h*d_k], Wv [d_model][h*d_v],
           Wo [h*d_v][d_model], key_lengths.
+    layer: X [B][n][d_model], the block's Wq, Wk, Wv, Wo, then ln1_gamma,
+          ln1_beta [d_model], W1 [d_model][d_ff], b1 [d_ff], W2 [d_ff][d_model],
+          b2, ln2_gamma, ln2_beta [d_model], key_lengths.
     """
     g = torch.Generator("cpu")
     g.manual_seed(seed)
@@ -124,6 +144,24 @@ def generate(w: Workload, seed: int = 0):
         out["K"] = _normal(g, (w.B, w.h, w.n_k, w.d_k), 1.0, dt)
         out["V"] = _normal(g, (w.B, w.h, w.n_k, w.d_v), 1.0, dt)
         out["scale"] = 1.0 / math.sqrt(w.d_k)
+    elif w.kind == "layer":
+        if w.n_q != w.n_k:
+            raise ValueError("an encoder layer attends to its own positions (n_q == n_k)")
+        D, F = w.d_model, w.d_ff
+        std = 1.0 / math.sqrt(D)
+        out["X"] = _normal(g, (w.B, w.n_q, D), 1.0, dt)
+        out["Wq"] = _normal(g, (D, w.h * w.d_k), std, dt)
+        out["Wk"] = _normal(g, (D, w.h * w.d_k), std, dt)
+        out["Wv"] = _normal(g, (D, w.h * w.d_v), std, dt)
+        out["Wo"] = _normal(g, (w.h * w.d_v, D), std, dt)
+        out["ln1_gamma"] = (1.0 + 0.1 * torch.randn((D,), generator=g)).to(dt)
+        out["ln1_beta"] = _normal(g, (D,), 0.1, dt)
+        out["W1"] = _normal(g, (D, F), std, dt)
+        out["b1"] = _normal(g, (F,), 0.1, dt)
+        out["W2"] = _normal(g, (F, D), 1.0 / math.sqrt(F), dt)
+        out["b2"] = _normal(g, (D,), 0.1, dt)
+        out["ln2_gamma"] = (1.0 + 0.1 * torch.randn((D,), generator=g)).to(dt)
+        out["ln2_beta"] = _normal(g, (D,), 0.1, dt)
     else:
         std = 1.0 / math.sqrt(w.d_model)
         out["X_q"] = _normal(g, (w.B, w.n_q, w.d_model), 1.0, dt)

@@ -9,7 +9,11 @@
  *   head_i   = Attention(X_q W_i^Q, X_kv W_i^K, X_kv W_i^V)
  *   MultiHead = Concat(head_1, ..., head_h) W^O
  *
- * with M an additive 0 / -inf mask applied before the row softmax.
+ * with M an additive 0 / -inf mask applied before the row softmax; and,
+ * around the block, one Post-LN encoder layer:
+ *
+ *   x1 = LayerNorm(X + MultiHead(X, X, X)),  Y = LayerNorm(x1 + FFN(x1)),
+ *   FFN(x) = max(0, x W1 + b1) W2 + b2.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -18,7 +22,8 @@
  *   `key_lengths`, which is a HOST pointer (read during the call only).
  * - Math orientation is X.W as on the pages: W^Q, W^K are d_model x (h*d_k),
  *   W^V is d_model x (h*d_v), W^O is (h*d_v) x d_model.  Holders of weights in
- *   [out][in] layout pass the transpose.  There are no biases.
+ *   [out][in] layout pass the transpose.  The attention block has no biases
+ *   (the feed-forward and LayerNorm entry points at the end carry theirs).
  * - Head i owns the contiguous column block [i*d, (i+1)*d) of a stacked
  *   projection and the row block [i*d_v, (i+1)*d_v) of W^O.
  * - Accumulation is always fp32.  bf16 intermediates (Q, K, V, softmax
@@ -219,6 +224,122 @@ int mha_forward_timed(const void* X_q, const void* X_kv,
  * call.  MHA_ERR_DIM for non-positive sizes.
  */
 int mha_forward_launches(int n_q, int n_k, int d_model, int self_attention);
+
+/*
+ * ---------------------------------------------------------------------------
+ * The rest of an encoder layer around the attention block: residual +
+ * LayerNorm (Post-LN) and the position-wise feed-forward network.  These
+ * entry points DO take biases and per-feature scale/shift vectors, because
+ * their defining formulas carry them.  All vectors (gamma, beta, b1, b2) are
+ * device arrays in the element type (bf16).  Only MHA_DTYPE_BF16.
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * add_layernorm_forward -- Y = LayerNorm(X + F), row by row:
+ *   u = X[m] + F[m];  Y[m] = gamma * (u - mean(u)) / sqrt(var(u) + eps) + beta
+ * with mean and variance over the row's d features; the variance is the
+ * population variance (divides by d).  Sources: hex4c59.cc "读懂 Attention Is
+ * All You Need", section "Add & Norm 里究竟发生了什么？" (the sublayer output is
+ * added back to its input and the sum normalised over one token's features,
+ * then scaled and shifted per feature: Post-LN); devpress.csdn.net
+ * "【深度学习】Transformer", section 2.3 (x + sublayer(x), then the norm).
+ *
+ *   X, F [M][d]   input and sublayer output;  gamma, beta [d];  Y [M][d]
+ *   Y may be the same buffer as X or as F (not a partial overlap).
+ *   eps finite and >= 0 (else MHA_ERR_SCALE); the pages give no value.
+ *   d % 8 == 0 and d <= 4096, pointers 16-byte aligned (else
+ *   MHA_ERR_UNSUPPORTED).  Sums in fp32, two-pass variance, Y rounded to bf16.
+ */
+int add_layernorm_forward(const void* X, const void* F, const void* gamma, const void* beta,
+                          void* Y, int M, int d, float eps, int dtype, hipStream_t stream);
+
+/*
+ * ffn_workspace_bytes -- device scratch of ffn_forward: the hidden layer
+ * H [M][d_ff] in the element type.  0 for invalid or unsupported sizes.
+ */
+size_t ffn_workspace_bytes(int M, int d_model, int d_ff, int dtype);
+
+/*
+ * ffn_forward -- position-wise feed-forward network, each row on its own:
+ *   Y = max(0, X W1 + b1) W2 + b2
+ * Sources: devpress.csdn.net "【深度学习】Transformer", section 2.3 (the FFN
+ * formula); hex4c59.cc "读懂 Attention Is All You Need", section "前馈网络为什么
+ * 放在注意力后面？" (ReLU between two linear maps, applied per position;
+ * 512 -> 2048 -> 512 in the base model).
+ *
+ *   X [M][d_model], W1 [d_model][d_ff], b1 [d_ff], W2 [d_ff][d_model],
+ *   b2 [d_model], Y [M][d_model] (must not overlap X or the workspace).
+ *   workspace   >= ffn_workspace_bytes(...), 256-byte aligned, caller-owned;
+ *               receives H = max(0, X W1 + b1) rounded to bf16.
+ *   d_model, d_ff multiples of 8 (else MHA_ERR_UNSUPPORTED), at most 2^20
+ *               (else MHA_ERR_DIM).
+ * Two GEMM launches; the bias (and the ReLU) are applied to the fp32
+ * accumulators before rounding.
+ */
+int ffn_forward(const void* X, const void* W1, const void* b1, const void* W2, const void* b2,
+                void* Y, int M, int d_model, int d_ff, int dtype, void* workspace,
+                size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * encoder_layer_workspace_bytes -- device scratch of encoder_layer_forward:
+ * the multi-head block's workspace (as mha_workspace_bytes with n_q = n_k =
+ * n), then the sublayer output [B*n][d_model], x1 [B*n][d_model] and the FFN
+ * hidden layer [B*n][d_ff], each 256-byte aligned.  0 for invalid sizes.
+ */
+size_t encoder_layer_workspace_bytes(int B, int n, int d_model, int h, int d_k, int d_v,
+                                     int d_ff, int dtype);
+
+/*
+ * encoder_layer_forward -- one encoder layer, self-attention, Post-LN:
+ *   x1 = LayerNorm1(X + MultiHead(X, X, X))
+ *   Y  = LayerNorm2(x1 + FFN(x1))
+ * Sources: hex4c59.cc "读懂 Attention Is All You Need", sections "前馈网络为什么
+ * 放在注意力后面？" and "Add & Norm 里究竟发生了什么？" (two sublayers, each
+ * wrapped as LayerNorm(x + Sublayer(x))); devpress.csdn.net
+ * "【深度学习】Transformer", section 2.3 (the block's order); wiki.hugogu.cn
+ * "Attention Is All You Need", the FFN and normalisation paragraph (the
+ * encoder layer's data flow).  No dropout (inference).
+ *
+ *   X [B][n][d_model]; Wq, Wk, Wv, Wo as mha_forward; ln1_gamma, ln1_beta,
+ *   ln2_gamma, ln2_beta, b2 [d_model]; W1, b1, W2 as ffn_forward;
+ *   Y [B][n][d_model] (must not overlap X or the workspace).
+ *   mask_kind / key_lengths as mha_forward (self-attention: n_q = n_k = n;
+ *   the encoder uses NONE or KEY_PADDING for padded source sentences).
+ *   eps as add_layernorm_forward; d_model % 8 == 0 and <= 4096.
+ * Launches, in order (see encoder_layer_launches): the multi-head block
+ * (mha_forward's plan, writing the sublayer output into the workspace),
+ * residual + LayerNorm1, FFN first GEMM (+ b1, ReLU), FFN second GEMM (+ b2),
+ * residual + LayerNorm2.
+ */
+int encoder_layer_forward(const void* X, const void* Wq, const void* Wk, const void* Wv,
+                          const void* Wo, const void* ln1_gamma, const void* ln1_beta,
+                          const void* W1, const void* b1, const void* W2, const void* b2,
+                          const void* ln2_gamma, const void* ln2_beta, void* Y,
+                          int B, int n, int d_model, int h, int d_k, int d_v, int d_ff,
+                          float eps, int mask_kind, const int32_t* key_lengths, int dtype,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * encoder_layer_forward_timed -- encoder_layer_forward with launch events,
+ * as the other _timed variants (events[2i], events[2i+1] around launch i).
+ */
+int encoder_layer_forward_timed(const void* X, const void* Wq, const void* Wk, const void* Wv,
+                                const void* Wo, const void* ln1_gamma, const void* ln1_beta,
+                                const void* W1, const void* b1, const void* W2, const void* b2,
+                                const void* ln2_gamma, const void* ln2_beta, void* Y,
+                                int B, int n, int d_model, int h, int d_k, int d_v, int d_ff,
+                                float eps, int mask_kind, const int32_t* key_lengths, int dtype,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream,
+                                hipEvent_t* events, int capacity, int* n_launches);
+
+/*
+ * encoder_layer_launches -- kernels encoder_layer_forward launches for
+ * sequences of n positions and width d_model: the block's (2 on the fused
+ * short-sequence plan, else 3) plus 4.  Host-only.  MHA_ERR_DIM for
+ * non-positive sizes.
+ */
+int encoder_layer_launches(int n, int d_model);
 
 /* Text of a status code (static storage; never NULL). */
 const char* mha_status_str(int status);

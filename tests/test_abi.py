@@ -186,3 +186,90 @@ def test_launch_plan(L):
     assert L.mha_forward_launches(129, 129, 512, 0) == 4
     assert L.mha_forward_launches(100, 100, 200, 1) == 3   # d_model not a multiple of 64
     assert L.mha_forward_launches(0, 100, 512, 1) == -2
+
+
+def test_width_limit(L):
+    assert mha(L, d_model=(1 << 20) + 8) == DIM            # GEMM widths up to 2^20
+
+
+def ln(L, X=FAKE, F=FAKE, g=FAKE, b=FAKE, Y=FAKE2, M=4, d=512, eps=1e-5, dtype=BF16):
+    return L.add_layernorm_forward(X, F, g, b, Y, M, d, eps, dtype, None)
+
+
+def test_add_layernorm_rejections(L):
+    assert ln(L, X=None) == NULL
+    assert ln(L, b=None) == NULL
+    assert ln(L, M=0) == DIM
+    assert ln(L, d=-8) == DIM
+    assert ln(L, eps=-1e-5) == SCALE
+    assert ln(L, eps=float("nan")) == SCALE
+    assert ln(L, eps=float("inf")) == SCALE
+    assert ln(L, d=500) == UNSUP                          # not whole 16-byte chunks
+    assert ln(L, d=4104) == UNSUP                         # above the row width limit
+    assert ln(L, dtype=F32) == UNSUP
+    assert ln(L, g=MISALIGNED) == UNSUP
+
+
+def ffn(L, X=FAKE, W=FAKE, Y=FAKE2, M=64, d_model=512, d_ff=2048, dtype=BF16, ws=FAKE,
+        ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = L.ffn_workspace_bytes(M, d_model, d_ff, BF16)
+    return L.ffn_forward(X, W, W, W, W, Y, M, d_model, d_ff, dtype, ws, ws_bytes, None)
+
+
+def test_ffn_rejections(L):
+    assert L.ffn_workspace_bytes(64, 512, 2048, BF16) == 64 * 2048 * 2
+    assert L.ffn_workspace_bytes(3, 512, 24, BF16) == 256          # rounded to 256 bytes
+    assert L.ffn_workspace_bytes(0, 512, 2048, BF16) == 0
+    assert L.ffn_workspace_bytes(64, 512, 2048, F32) == 0
+    assert ffn(L, X=None) == NULL
+    assert ffn(L, M=0, ws_bytes=1 << 20) == DIM
+    assert ffn(L, d_ff=(1 << 20) + 8, ws_bytes=1 << 40) == DIM
+    assert ffn(L, d_ff=2044, ws_bytes=1 << 20) == UNSUP
+    assert ffn(L, dtype=F32, ws_bytes=1 << 20) == UNSUP
+    assert ffn(L, ws=None) == WS
+    assert ffn(L, ws_bytes=1024) == WS
+    assert ffn(L, ws=ctypes.c_void_p(0x10010)) == WS
+    assert ffn(L, Y=MISALIGNED) == UNSUP
+
+
+def layer(L, X=FAKE, W=FAKE, Y=FAKE2, B=2, n=8, d_model=64, h=2, d_k=64, d_v=64, d_ff=128,
+          eps=1e-5, mask=0, kl=None, dtype=BF16, ws=FAKE, ws_bytes=None, timed=None):
+    if ws_bytes is None:
+        ws_bytes = L.encoder_layer_workspace_bytes(B, n, d_model, h, d_k, d_v, d_ff, BF16)
+    args = [X] + [W] * 12 + [Y, B, n, d_model, h, d_k, d_v, d_ff, eps, mask, kl, dtype, ws,
+                             ws_bytes, None]
+    if timed is None:
+        return L.encoder_layer_forward(*args)
+    ev, cap = timed
+    return L.encoder_layer_forward_timed(*args, ev, cap, None)
+
+
+def test_encoder_layer_rejections(L):
+    def up(x):
+        return (x + 255) // 256 * 256
+    B, n, dm, h, d, dff = 2, 8, 64, 2, 64, 128
+    want = L.mha_workspace_bytes(B, n, n, h, d, d, BF16) + 2 * up(2 * B * n * dm) + up(2 * B * n * dff)
+    assert L.encoder_layer_workspace_bytes(B, n, dm, h, d, d, dff, BF16) == want
+    assert L.encoder_layer_workspace_bytes(B, n, dm, h, d, d, dff, F32) == 0
+    assert L.encoder_layer_workspace_bytes(0, n, dm, h, d, d, dff, BF16) == 0
+    assert layer(L, X=None) == NULL
+    assert layer(L, W=None) == NULL
+    assert layer(L, B=0, ws_bytes=1 << 20) == DIM
+    assert layer(L, d_k=32) == UNSUP
+    assert layer(L, d_ff=100) == UNSUP
+    assert layer(L, d_model=4160, h=2) == UNSUP          # wider than the LayerNorm limit
+    assert layer(L, eps=-1.0) == SCALE
+    assert layer(L, mask=2) == KEYLEN
+    assert layer(L, mask=9) == MASK
+    assert layer(L, dtype=F32, ws_bytes=1 << 20) == UNSUP
+    assert layer(L, ws=None) == WS
+    assert layer(L, ws_bytes=4096) == WS
+    assert layer(L, Y=MISALIGNED) == UNSUP
+    assert layer(L, timed=(None, 0)) == -9                 # events missing
+
+
+def test_encoder_layer_launch_plan(L):
+    assert L.encoder_layer_launches(100, 512) == 6        # fused block plan + 4
+    assert L.encoder_layer_launches(512, 512) == 7        # stacked projection plan + 4
+    assert L.encoder_layer_launches(0, 512) == DIM
