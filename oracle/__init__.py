@@ -13,7 +13,9 @@ Two independent formulations are provided:
   (projections, per-head scores, additive mask, row softmax, weighted sum of
   values, concat, output projection), one function per step;
   ``oracle.layer`` -- the same for residual + LayerNorm and the
-  position-wise feed-forward network of an encoder layer.
+  position-wise feed-forward network of an encoder layer;
+  ``oracle.embedding`` -- the scaled token embedding plus the sinusoidal
+  positional encoding.
 * ``oracle.bruteforce`` -- pure-Python loops with ``math.exp``/``math.fsum``,
   one query row at a time, for tiny inputs; it cross-checks the matrix form.
 
@@ -38,6 +40,9 @@ computed):
 * For the rest of the encoder layer (``oracle.layer``): hex4c59.cc sections
   "前馈网络为什么放在注意力后面？" and "Add & Norm 里究竟发生了什么？";
   devpress.csdn.net section 2.3 (encoder block order, FFN formula).
+* For the input side (``oracle.embedding``): devpress.csdn.net section 4
+  (equation (4.1), Table 4.1, the worked example, the shift identity);
+  hex4c59.cc section "没有循环，模型怎样知道词序？".
 
 Parity status of every function is stated in its docstring.  All functions
 are pinned by ``tests/test_oracle.py`` (printed values from the pages,
@@ -62,8 +67,10 @@ from .attention import (  # noqa: F401
 )
 from .bruteforce import (  # noqa: F401
     attention_bruteforce,
+    embed_positional_bruteforce,
     ffn_bruteforce,
     layer_norm_bruteforce,
     mha_bruteforce,
 )
+from .embedding import embed_positional_ref, positional_encoding  # noqa: F401
 from .layer import add_layer_norm, encoder_layer_ref, ffn, layer_norm  # noqa: F401

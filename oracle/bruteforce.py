@@ -117,3 +117,23 @@ def ffn_bruteforce(X, W1, b1, W2, b2):
         out.append([math.fsum(hid[t] * float(W2[t][j]) for t in range(len(hid))) + float(b2[j])
                     for j in range(len(b2))])
     return out
+
+
+def embed_positional_bruteforce(tokens, E, pos0=0):
+    """Loop form of the scaled embedding plus sinusoidal encoding: for each
+    sequence b, position p and coordinate j, E[token][j] * sqrt(d) plus
+    sin or cos of (pos0 + p) / 10000^(2 (j // 2) / d), sine on even j."""
+    d = len(E[0])
+    out = []
+    for row in tokens:
+        seq = []
+        for p, t in enumerate(row):
+            pos = pos0 + p
+            vec = []
+            for j in range(d):
+                angle = pos / 10000.0 ** (2 * (j // 2) / d)
+                enc = math.sin(angle) if j % 2 == 0 else math.cos(angle)
+                vec.append(E[t][j] * math.sqrt(d) + enc)
+            seq.append(vec)
+        out.append(seq)
+    return out

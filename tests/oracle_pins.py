@@ -643,3 +643,75 @@ ALL_LAYER_CHECKS = [
     check_layer_ffn_residual,
     check_layer_bruteforce,
 ]
+
+
+# ------------------------------------------------------------ input embedding pins
+# Implementation interface: positional_encoding(n, d_model, pos0),
+# embed_positional_ref(tokens, E, pos0).
+
+def check_pe_printed_table(impl):
+    """Table 4.1 of devpress.csdn.net section 4: d_model = 4, positions 0..4,
+    printed to 4 decimals.  Tolerance one unit of the last printed digit:
+    cos(0.01) = 0.999950000... is printed 0.9999 (the page's single-precision
+    value lies just below the rounding point), every other entry is the
+    correctly rounded value."""
+    g = _golden("positional_encoding_table_4_1.json")
+    pe = impl.positional_encoding(len(g["pe"]), g["d_model"], 0)
+    assert np.abs(pe - np.array(g["pe"])).max() <= 1e-4 + 1e-12, pe
+
+
+def check_embedding_worked_example(impl):
+    """The worked example of the same section: x (5 positions, d_model 4) is
+    scaled by sqrt(4) = 2 and the Table 4.1 encoding added.  Token p picks
+    row p of a 5-row table holding the printed x."""
+    g = _golden("positional_encoding_table_4_1.json")
+    x = np.array(g["x"])
+    out = impl.embed_positional_ref(np.arange(5)[None, :], x, 0)
+    want = g["xscale"] * x + np.array(g["pe"])
+    assert g["xscale"] == math.sqrt(g["d_model"])
+    assert np.abs(out[0] - want).max() <= 1e-4 + 1e-12, out
+
+
+def check_pe_pairs_and_origin(impl):
+    """Each (sin, cos) pair has unit norm; position 0 is (0, 1, 0, 1, ...);
+    the first pair turns at frequency 1 (sin pos, cos pos); positions
+    pos0 .. pos0+n-1 are rows pos0.. of the encoding from 0."""
+    d = 512
+    pe = impl.positional_encoding(300, d, 0)
+    assert np.allclose(pe[:, 0::2] ** 2 + pe[:, 1::2] ** 2, 1.0, atol=1e-15)
+    assert np.array_equal(pe[0], np.tile([0.0, 1.0], d // 2))
+    pos = np.arange(300.0)
+    assert np.allclose(pe[:, 0], np.sin(pos), atol=1e-15) and np.allclose(pe[:, 1], np.cos(pos), atol=1e-15)
+    assert np.allclose(impl.positional_encoding(40, d, 123), pe[123:163], atol=1e-15)
+
+
+def check_pe_shift_identity(impl):
+    """devpress.csdn.net section 4: PE(pos + k) is PE(pos) with each pair
+    rotated by omega_i k, omega_i = 10000^(-2i/d_model) -- pins every
+    pair's frequency at d_model = 512."""
+    d = 512
+    pe = impl.positional_encoding(200, d, 0)
+    omega = 10000.0 ** (-2.0 * np.arange(d // 2) / d)
+    for k in (1, 7, 50):
+        s, c = pe[:-k, 0::2], pe[:-k, 1::2]
+        rs = s * np.cos(omega * k) + c * np.sin(omega * k)
+        rc = c * np.cos(omega * k) - s * np.sin(omega * k)
+        assert np.allclose(pe[k:, 0::2], rs, atol=1e-12) and np.allclose(pe[k:, 1::2], rc, atol=1e-12)
+
+
+def check_embedding_bruteforce(impl):
+    import oracle
+    r = _rng(31)
+    E = r.standard_normal((11, 6))
+    tokens = r.integers(0, 11, (2, 5))
+    want = np.array(oracle.embed_positional_bruteforce(tokens.tolist(), E.tolist(), 3))
+    assert np.allclose(impl.embed_positional_ref(tokens, E, 3), want, atol=1e-13)
+
+
+ALL_EMBED_CHECKS = [
+    check_pe_printed_table,
+    check_embedding_worked_example,
+    check_pe_pairs_and_origin,
+    check_pe_shift_identity,
+    check_embedding_bruteforce,
+]

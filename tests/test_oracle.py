@@ -15,6 +15,18 @@ def test_sdpa_pin(check):
     check(oracle)
 
 
+@pytest.mark.parametrize("check", pins.ALL_EMBED_CHECKS, ids=lambda f: f.__name__)
+def test_embed_pin(check):
+    check(oracle)
+
+
+def test_embedding_rejects_ids_outside_the_vocabulary():
+    with pytest.raises(ValueError):
+        oracle.embed_positional_ref(np.array([[0, 5]]), np.zeros((5, 4)))
+    with pytest.raises(ValueError):
+        oracle.embed_positional_ref(np.array([[-1]]), np.zeros((5, 4)))
+
+
 @pytest.mark.parametrize("check", pins.ALL_LAYER_CHECKS, ids=lambda f: f.__name__)
 def test_layer_pin(check):
     check(oracle)

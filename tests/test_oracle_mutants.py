@@ -227,3 +227,60 @@ def test_unmutated_layer_copy_passes_every_pin():
 def test_layer_mutant_is_caught(name):
     failed = _fails_some_layer_pin(LAYER_MUTANTS[name]())
     assert failed, f"planted mistake {name!r} passed every pin"
+
+
+# ------------------------------------------------------------ input embedding mutants
+
+def _pe(swap=False, exponent="pair", origin=0):
+    def positional_encoding(n, d_model, pos0=0):
+        pos = np.arange(pos0 + origin, pos0 + origin + n, dtype=np.float64)[:, None]
+        i = np.arange(d_model // 2, dtype=np.float64)[None, :]
+        e = {"pair": 2.0 * i / d_model, "half": i / d_model, "coord": 4.0 * i / d_model}[exponent]
+        ang = pos / np.power(10000.0, e)
+        pe = np.empty((n, d_model))
+        pe[:, 0::2] = np.cos(ang) if swap else np.sin(ang)
+        pe[:, 1::2] = np.sin(ang) if swap else np.cos(ang)
+        return pe
+    return positional_encoding
+
+
+def _build_embed(pe=None, scale=lambda d: math.sqrt(d)):
+    pe = pe or oracle.positional_encoding
+
+    def embed_positional_ref(tokens, E, pos0=0):
+        E = np.asarray(E, dtype=np.float64)
+        tokens = np.asarray(tokens)
+        return E[tokens] * scale(E.shape[1]) + pe(tokens.shape[1], E.shape[1], pos0)[None]
+
+    return types.SimpleNamespace(positional_encoding=pe, embed_positional_ref=embed_positional_ref)
+
+
+EMBED_MUTANTS = {
+    "pe_sin_cos_swapped": lambda: _build_embed(pe=_pe(swap=True)),
+    "pe_exponent_i_over_d": lambda: _build_embed(pe=_pe(exponent="half")),
+    "pe_exponent_by_coordinate": lambda: _build_embed(pe=_pe(exponent="coord")),
+    "pe_positions_from_one": lambda: _build_embed(pe=_pe(origin=1)),
+    "embedding_unscaled": lambda: _build_embed(scale=lambda d: 1.0),
+    "embedding_scaled_by_d": lambda: _build_embed(scale=lambda d: float(d)),
+}
+
+
+def _fails_some_embed_pin(impl):
+    failed = []
+    for check in pins.ALL_EMBED_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check(impl)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            failed.append(check.__name__)
+    return failed
+
+
+def test_unmutated_embed_copy_passes_every_pin():
+    assert _fails_some_embed_pin(_build_embed()) == []
+
+
+@pytest.mark.parametrize("name", sorted(EMBED_MUTANTS))
+def test_embed_mutant_is_caught(name):
+    failed = _fails_some_embed_pin(EMBED_MUTANTS[name]())
+    assert failed, f"planted mistake {name!r} passed every pin"
