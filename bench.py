@@ -5,7 +5,9 @@
 A step is one pass of the whole path over one batch: for a multi-head block
 the input projection(s), the fused attention and the output projection; for
 bare attention the fused attention kernel; for an encoder layer the block,
-residual + LayerNorm, the two FFN GEMMs and residual + LayerNorm.  Inputs are seeded synthetic
+residual + LayerNorm, the two FFN GEMMs and residual + LayerNorm; for the
+input embedding the fused lookup x sqrt(d_model) + positional encoding
+(no attention: its line carries the roofline and a null metric value).  Inputs are seeded synthetic
 tensors of the workload's shapes, resident in GPU memory before timing, and
 rotated through enough buffer sets that every step reads memory no earlier
 step left in the 256 MB Infinity Cache.
@@ -76,7 +78,7 @@ def layer_launches(w):
 
 
 def step_launches(w):
-    if w.kind == "sdpa":
+    if w.kind in ("sdpa", "embed"):
         return 1
     return layer_launches(w) if w.kind == "layer" else mha_launches(w)
 
@@ -103,6 +105,12 @@ def kernel_plan(w, n_launches=None):
     if w.kind == "sdpa":
         plan.append(dict(name="attention", flops=0.0, bytes=0.0,
                          peak_kind="mfma" if w.dtype == "bf16" else "fp32", has_attention=True))
+        return plan, None
+    if w.kind == "embed":
+        # gather one table row per token, write one row per token, read the ids
+        plan.append(dict(name="embed_positional", flops=0.0,
+                         bytes=float(2 * e * B * nq * w.d_model + 4 * B * nq),
+                         peak_kind="hbm", has_attention=False))
         return plan, None
     n = step_launches(w) if n_launches is None else n_launches
     if w.kind == "layer":
@@ -184,6 +192,14 @@ class Step:
                 self.sets.append((P(Q.data_ptr()), P(K.data_ptr()), P(V.data_ptr()), P(O.data_ptr()),
                                   w.B, w.h, w.n_q, w.n_k, w.d_k, w.d_v, float(x["scale"]), w.mask,
                                   self.kl, code))
+            elif w.kind == "embed":
+                T = x["tokens"].to(dev)
+                E = x["E"].to(dev)
+                O = torch.empty((w.B, w.n_q, w.d_model), dtype=E.dtype, device=dev)
+                self.keep.append((T, E, None, O))
+                code = bnd.DTYPE_BF16 if w.dtype == "bf16" else bnd.DTYPE_F32
+                self.sets.append((P(T.data_ptr()), P(E.data_ptr()), P(O.data_ptr()), w.B, w.n_q,
+                                  w.vocab, w.d_model, int(x["pos0"]), code))
             elif w.kind == "layer":
                 X = x["X"].to(dev)
                 ps = [x[k].to(dev) for k in bnd.LAYER_PARAMS]
@@ -207,7 +223,8 @@ class Step:
                                   w.B, w.n_q, w.n_k, w.d_model, w.h, w.d_k, w.d_v, w.mask, self.kl,
                                   bnd.DTYPE_BF16, P(ws.data_ptr()), ws.numel()))
         self.n_launches = step_launches(w)
-        names = {"sdpa": "sdpa_forward", "mha": "mha_forward", "layer": "encoder_layer_forward"}
+        names = {"sdpa": "sdpa_forward", "mha": "mha_forward", "layer": "encoder_layer_forward",
+                 "embed": "embed_positional_forward"}
         self.entry = names[w.kind]
 
     def output(self, i):
@@ -228,6 +245,8 @@ class Step:
 
 def set_bytes(w):
     e = 2 if w.dtype == "bf16" else 4
+    if w.kind == "embed":
+        return e * (w.vocab * w.d_model + w.B * w.n_q * w.d_model) + 4 * w.B * w.n_q
     if w.kind == "sdpa":
         return e * w.B * w.h * (w.n_q * (w.d_k + w.d_v) + w.n_k * (w.d_k + w.d_v))
     xs = w.B * w.n_q * w.d_model * (1 if w.self_attn else 1) + (0 if w.self_attn else w.B * w.n_k * w.d_model)
@@ -258,6 +277,16 @@ def parity_check(w, x, out):
     from head_attention_forward_amd.workloads import to_f64
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
     rows = "all"
+    if w.kind == "embed":
+        want = oracle.embed_positional_ref(x["tokens"].numpy(), to_f64(x["E"]), x["pos0"])
+        got = to_f64(out)
+        err = np.abs(got - want)
+        # one rounding of the exact value (double-precision encoding, fp32 sum)
+        u = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -24
+        worst = float((err / (u * np.abs(want) + 1e-5)).max())
+        rel = float(np.linalg.norm(got - want) / np.linalg.norm(want))
+        return dict(max_abs=float(err.max()), rel_l2=rel, worst_over_bound=worst,
+                    ok=bool(worst <= 1.0), rows=rows)
     if w.kind == "layer":
         from head_attention_forward_amd._binding import LAYER_PARAMS
         p = [to_f64(x[k]) for k in LAYER_PARAMS]
@@ -313,6 +342,26 @@ def cpu_baseline(w, x, target_s):
         threads = 1
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
 
+    if w.kind == "embed":
+        tokens, E = x["tokens"].numpy(), to_f64(x["E"])
+        e = 2 if w.dtype == "bf16" else 4
+
+        def run(b):
+            oracle.embed_positional_ref(tokens[:b], E, x["pos0"])
+        # in the unit of this workload's roofline: algorithmic GB/s
+        run(1)
+        t0 = time.perf_counter()
+        run(w.B)
+        t1 = max(time.perf_counter() - t0, 1e-6)
+        reps = int(max(1, min(10000, target_s / t1)))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            run(w.B)
+        t = time.perf_counter() - t0
+        byts = float(2 * e * w.B * w.n_q * w.d_model + 4 * w.B * w.n_q) * reps
+        return dict(value=byts / t / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                    sample=f"{w.B} of {w.B} sequences, {reps} passes; {t:.2f} s, numpy float64",
+                    seconds=round(t, 3))
     if w.kind == "layer":
         from head_attention_forward_amd._binding import LAYER_PARAMS
         X = to_f64(x["X"])
@@ -374,6 +423,7 @@ KERNEL_SOURCES = {
     "proj_attn_bf16_kernel": ("proj_attn_bf16.hip", "wave_attention.h", "mha_api.hip"),
     "gemm_bf16_kernel": ("gemm_bf16.hip", "mha_api.hip"),
     "add_layernorm_bf16_kernel": ("add_layernorm_bf16.hip", "mha_api.hip"),
+    "embed_positional_kernel": ("embed_positional.hip", "mha_api.hip"),
 }
 
 
@@ -546,8 +596,8 @@ def main():
                 algorithmic_flops=dom["flops"], algorithmic_bytes=dom["bytes"])
 
     nominal = w.nominal_attention_flops()
-    value = nominal / (ms_step * 1e-3) / 1e12
-    att = next(k for k in kernels if k["has_attention"])
+    att = next((k for k in kernels if k["has_attention"]), None)
+    value = nominal / (ms_step * 1e-3) / 1e12 if att is not None else None
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -566,6 +616,7 @@ def main():
 
     kinds = {"mha": "multi-head block (projections + attention + output projection)",
              "sdpa": "bare attention",
+             "embed": "token embedding x sqrt(d_model) + sinusoidal positional encoding",
              "layer": "encoder layer, Post-LN (block, residual + LayerNorm, FFN, residual + LayerNorm)"}
     cfg = dict(workload=w.name, B=w.B, n_q=w.n_q, n_k=w.n_k, h=w.h, d_k=w.d_k, d_v=w.d_v,
                mask={0: "none", 1: "causal", 2: "key_padding", 3: "causal+key_padding"}[w.mask],
@@ -574,13 +625,16 @@ def main():
         cfg.update(d_model=w.d_model, self_attention=w.self_attn)
     if w.kind == "layer":
         cfg.update(d_ff=w.d_ff, eps=w.eps)
+    if w.kind == "embed":
+        cfg = dict(workload=w.name, B=w.B, n=w.n_q, d_model=w.d_model, vocab=w.vocab, pos0=0,
+                   kind=kinds[w.kind], buffer_sets=sets)
     if x["key_lengths"] is not None:
         cfg["key_lengths_mean"] = float(x["key_lengths"].float().mean())
     out = {
         "metric": METRIC,
-        "value": round(value, 3),
+        "value": None if value is None else round(value, 3),
         "unit": "TFLOP/s",
-        "pct_of_bf16_mfma_peak": round(100 * value / PEAK_BF16_TFLOPS, 3),
+        "pct_of_bf16_mfma_peak": None if value is None else round(100 * value / PEAK_BF16_TFLOPS, 3),
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -598,15 +652,18 @@ def main():
         "config": cfg,
         # the kernel that runs the attention (fused with the input
         # projections for short sequences); kernel_tflops counts all its flops
-        "attention_kernel": dict(kernel=att["name"], avg_us=att["avg_us"],
-                                 nominal_attention_tflops=round(nominal / (att["avg_us"] * 1e-6) / 1e12, 2),
-                                 kernel_tflops=att["tflops"], gbs=att["gbs"]),
+        "attention_kernel": None if att is None else dict(
+            kernel=att["name"], avg_us=att["avg_us"],
+            nominal_attention_tflops=round(nominal / (att["avg_us"] * 1e-6) / 1e12, 2),
+            kernel_tflops=att["tflops"], gbs=att["gbs"]),
         "kernels": [{k: v for k, v in kk.items() if k not in ("peak_kind", "has_attention")} for kk in kernels],
         "roofline": roof,
         "cpu_baseline": cpu,
         "parity": parity,
         "kernel_source_sha": kernel_source_sha(),
     }
+    if w.kind == "embed":
+        out["data"] = "synthetic (seeded uniform token ids, N(0,1/d_model) embedding table)"
     if w.kind == "layer":
         lf = layer_flops(w)
         out["layer"] = dict(matmul_flops_per_step=lf,

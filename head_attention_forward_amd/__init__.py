@@ -9,6 +9,7 @@ from ._binding import (  # noqa: F401
     LAYER_PARAMS,
     MHAError,
     add_layernorm_forward,
+    embed_positional_forward,
     encoder_layer_forward,
     encoder_layer_workspace_bytes,
     ffn_forward,

@@ -54,6 +54,8 @@ _SIG = {
     "encoder_layer_forward_timed": (_I, [_P] * 14 + [_I] * 7 + [ctypes.c_float, _I, _P, _I, _P,
                                                               ctypes.c_size_t, _P, _P, _I, _P]),
     "encoder_layer_launches": (_I, [_I, _I]),
+    "embed_positional_forward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
+    "embed_positional_forward_timed": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P]),
 }
 
 _lib = None
@@ -327,4 +329,23 @@ def encoder_layer_forward(X, params, h, eps=1e-5, mask_kind=0, key_lengths=None,
                                      _dev(workspace, "workspace"),
                                      workspace.numel() * workspace.element_size(), _stream(stream))
     _check("encoder_layer_forward", st)
+    return out
+
+
+def embed_positional_forward(tokens, E, pos0=0, out=None, stream=None):
+    """out[b][p] = E[tokens[b][p]] * sqrt(d_model) + PE(pos0 + p) (sinusoidal).
+
+    tokens int32 [B][n] and E [vocab][d_model] (bf16 or fp32) on the GPU.
+    Ids outside [0, vocab) give rows of NaN.  Returns out [B][n][d_model]."""
+    if tokens.dtype != torch.int32:
+        raise TypeError("tokens must be int32")
+    B, n = tokens.shape
+    vocab, d_model = E.shape
+    if out is None:
+        out = torch.empty((B, n, d_model), dtype=E.dtype, device=E.device)
+    elif out.shape != (B, n, d_model) or out.dtype != E.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    st = lib().embed_positional_forward(_dev(tokens, "tokens"), _dev(E, "E"), _dev(out, "out"), B, n,
+                                        vocab, d_model, int(pos0), _dtype_code(E), _stream(stream))
+    _check("embed_positional_forward", st)
     return out

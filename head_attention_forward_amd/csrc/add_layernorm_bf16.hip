@@ -34,12 +34,6 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
-__device__ __forceinline__ void load8(const __bf16* p, float* f) {
-  const bf16x8 v = *(const bf16x8*)p;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) f[e] = (float)v[e];
-}
-
 template <int CH>
 __global__ __launch_bounds__(64 * kRowsPerBlock) void add_layernorm_bf16_kernel(const LnArgs a) {
   const int lane = threadIdx.x & 63;
@@ -50,23 +44,26 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void add_layernorm_bf16_kernel(
   const __bf16* X = (const __bf16*)a.X + base;
   const __bf16* F = (const __bf16*)a.F + base;
 
+  // Every load of the row (inputs, gamma, beta) is issued before the first
+  // use, so their latencies overlap.  Chunks past the row read chunk 0.
+  bf16x8 xv[CH], fv[CH], gv[CH], bv[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const int c = lane + 64 * j < nch ? lane + 64 * j : 0;
+    xv[j] = *(const bf16x8*)(X + 8 * c);
+    fv[j] = *(const bf16x8*)(F + 8 * c);
+    gv[j] = *(const bf16x8*)((const __bf16*)a.gamma + 8 * c);
+    bv[j] = *(const bf16x8*)((const __bf16*)a.beta + 8 * c);
+  }
   float u[CH][8];
   float s = 0.f;
 #pragma unroll
   for (int j = 0; j < CH; ++j) {
-    const int c = lane + 64 * j;
-    if (c < nch) {
-      float x[8], f[8];
-      load8(X + 8 * c, x);
-      load8(F + 8 * c, f);
+    const bool in = lane + 64 * j < nch;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        u[j][e] = x[e] + f[e];
-        s += u[j][e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) u[j][e] = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      u[j][e] = in ? (float)xv[j][e] + (float)fv[j][e] : 0.f;
+      s += u[j][e];
     }
   }
   const float inv_d = 1.0f / (float)a.d;
@@ -89,12 +86,9 @@ __global__ __launch_bounds__(64 * kRowsPerBlock) void add_layernorm_bf16_kernel(
   for (int j = 0; j < CH; ++j) {
     const int c = lane + 64 * j;
     if (c < nch) {
-      float g[8], b[8];
-      load8((const __bf16*)a.gamma + 8 * c, g);
-      load8((const __bf16*)a.beta + 8 * c, b);
       f32x8 y;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) y[e] = g[e] * (u[j][e] * rstd) + b[e];
+      for (int e = 0; e < 8; ++e) y[e] = (float)gv[j][e] * (u[j][e] * rstd) + (float)bv[j][e];
       *(bf16x8*)(Y + 8 * c) = __builtin_convertvector(y, bf16x8);
     }
   }

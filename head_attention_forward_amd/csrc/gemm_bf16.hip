@@ -285,13 +285,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
                    (c - head * hd) + 4 * grp;
     const int64_t bstride = (int64_t)heads * rows * hd;
     // Bias of this lane's columns nb + 8q + 4grp .. +3 (zero without one).
+    // The four loads are issued together (columns clamped into the row; a
+    // block past N is never stored), so their latencies overlap.
     f32x4 bq[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      bq[q] = f32x4{};
-      if (g.bias != nullptr && nb + 8 * q < N)
-        bq[q] = __builtin_convertvector(*(const bf16x4*)((const __bf16*)g.bias + nb + 8 * q + 4 * grp),
-                                        f32x4);
+    for (int q = 0; q < 4; ++q) bq[q] = f32x4{};
+    if (g.bias != nullptr) {
+      bf16x4 braw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        braw[q] = *(const bf16x4*)((const __bf16*)g.bias + min(nb + 8 * q + 4 * grp, N - 4));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bq[q] = __builtin_convertvector(braw[q], f32x4);
     }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
@@ -355,14 +360,16 @@ hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, Launc
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
-  // Measured on MI355X over the block's projection shapes: 128 x 128 tiles
-  // with 8 waves (more waves issuing the stage copies) once there are enough
-  // tiles to occupy the compute units (2-stage ring from two tiles per unit
-  // on), otherwise 64 x 64 tiles with 4 waves for parallelism.
+  // Measured on MI355X over the block's projection shapes and the FFN's:
+  // 128 x 128 tiles with 8 waves (more waves issuing the stage copies) once
+  // there are enough tiles to occupy the compute units (2-stage ring, two
+  // workgroups per unit, from about 1.5 tiles per unit on), otherwise 64 x 64
+  // tiles with 4 waves for parallelism.  Larger tiles (256 x 128) were
+  // slower on every shape measured.
   const int N = g.col_start[g.nseg];
   if (!tiles_fit(g, 128)) return launch_gemm_bf16_cfg(g, 6, s, ev);
   const long t128 = (long)((N + 127) / 128) * ((g.M + 127) / 128);
-  if (t128 >= 512) return launch_gemm_bf16_cfg(g, 9, s, ev);
+  if (t128 >= 400) return launch_gemm_bf16_cfg(g, 9, s, ev);
   if (t128 >= 150) return launch_gemm_bf16_cfg(g, 10, s, ev);
   return launch_gemm_bf16_cfg(g, 6, s, ev);
 }

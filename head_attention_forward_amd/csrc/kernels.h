@@ -66,6 +66,15 @@ struct LnArgs {
   float eps;
 };
 
+// Scaled token embedding plus sinusoidal positional encoding:
+//   out[b][p] = E[tokens[b][p]] * sqrt(d) + PE(pos0 + p)
+struct EmbedArgs {
+  const int32_t* tokens;  // [B][n] (device)
+  const void* E;          // [vocab][d]
+  void* out;              // [B][n][d]
+  int B, n, vocab, d, pos0;
+};
+
 // Fused input projections + attention for short sequences (n_q, n_k <= 128,
 // d_model a multiple of 64, head size 64): one workgroup per (batch, head)
 // computes that head's Q, K, V tiles and its attention output.
@@ -100,6 +109,8 @@ hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, L
 hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_add_layernorm_bf16(const LnArgs& a, hipStream_t s, LaunchEvents ev = {});
+// f32 != 0: E and out are fp32, else bf16.
+hipError_t launch_embed_positional(const EmbedArgs& a, int f32, hipStream_t s, LaunchEvents ev = {});
 bool proj_attn_supported(int n_q, int n_k, int d_model);
 hipError_t launch_proj_attn_bf16(const ProjAttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 // One fixed tile configuration (index into the instantiated set); for sweeps.

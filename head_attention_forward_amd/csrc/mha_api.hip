@@ -596,4 +596,34 @@ int encoder_layer_forward_timed(const void* X, const void* Wq, const void* Wk, c
   return st;
 }
 
+static int embed_impl(const int32_t* tokens, const void* E, void* out, int B, int n, int vocab,
+                      int d_model, int pos0, int dtype, hipStream_t stream, Timer* tm) {
+  if (!tokens || !E || !out) return MHA_ERR_NULL;
+  if (B <= 0 || n <= 0 || vocab <= 0 || d_model <= 0 || pos0 < 0) return MHA_ERR_DIM;
+  if ((int64_t)pos0 + n > ((int64_t)1 << 31) - 1) return MHA_ERR_DIM;
+  if ((int64_t)B * n >= kIndexLimit || d_model > kMaxWidth) return MHA_ERR_DIM;
+  if (B > 65535 * 8) return MHA_ERR_DIM;
+  if (dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_F32) return MHA_ERR_UNSUPPORTED;
+  if (d_model % 8 != 0) return MHA_ERR_UNSUPPORTED;
+  if (((uintptr_t)tokens & 3u) != 0 || !aligned16(E) || !aligned16(out)) return MHA_ERR_UNSUPPORTED;
+  EmbedArgs a{tokens, E, out, B, n, vocab, d_model, pos0};
+  return launch_status(launch_embed_positional(a, dtype == MHA_DTYPE_F32, stream, next_events(tm)));
+}
+
+int embed_positional_forward(const int32_t* tokens, const void* E, void* out, int B, int n,
+                             int vocab, int d_model, int pos0, int dtype, hipStream_t stream) {
+  return embed_impl(tokens, E, out, B, n, vocab, d_model, pos0, dtype, stream, nullptr);
+}
+
+int embed_positional_forward_timed(const int32_t* tokens, const void* E, void* out, int B, int n,
+                                   int vocab, int d_model, int pos0, int dtype, hipStream_t stream,
+                                   hipEvent_t* events, int capacity, int* n_launches) {
+  if (events == nullptr || capacity < 2 || events[0] == nullptr || events[1] == nullptr)
+    return MHA_ERR_EVENTS;
+  Timer tm{events, capacity, 0};
+  const int st = embed_impl(tokens, E, out, B, n, vocab, d_model, pos0, dtype, stream, &tm);
+  if (n_launches) *n_launches = tm.used;
+  return st;
+}
+
 }  // extern "C"

@@ -77,7 +77,12 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
   // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin; unit
   // (b, head) = b*h + head is remapped so that each XCD owns a contiguous
   // run of units, i.e. whole batches: an activation row block is then read
-  // into one XCD's L2 only (every XCD reads the weights, which are smaller).
+  // into one XCD's L2 only.  When the run is made of whole batches, the
+  // XCD's units are taken head by head (all of its batches for one head,
+  // then the next head), so the workgroups resident together share few
+  // heads' weight slices and their batches' rows, and later workgroups find
+  // both in L2 (measured on the cross-attention block, whose XCD runs take
+  // two rounds: 1.45x fewer bytes fetched from memory, same time).
   int bh;
   {
     const int T = a.B * a.h;
@@ -85,7 +90,15 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
     const int x = bid % 8;
     const int per = T / 8;
     const int rem = T - per * 8;
-    bh = __builtin_amdgcn_readfirstlane(x * per + min(x, rem) + bid / 8);
+    const int start = x * per + min(x, rem);
+    const int len = per + (x < rem ? 1 : 0);
+    const int j = bid / 8;
+    int u = start + j;
+    if (len % a.h == 0 && start % a.h == 0) {
+      const int nb = len / a.h;  // whole batches in this XCD's run
+      u = start + (j % nb) * a.h + j / nb;
+    }
+    bh = __builtin_amdgcn_readfirstlane(u);
   }
   const int b = __builtin_amdgcn_readfirstlane(bh / a.h);
   const int hh = bh - b * a.h;

@@ -27,6 +27,11 @@ Wo, ln1_gamma, ln1_beta, W1, b1, W2, b2, ln2_gamma, ln2_beta, key_lengths.
 W1 has variance 1/d_model, W2 1/d_ff; biases and LayerNorm shifts are
 0.1 * N(0, 1), LayerNorm scales 1 + 0.1 * N(0, 1) (non-trivial values, so
 that every term of the layer shows in its output).
+
+Input embedding (kind "embed"): token ids uniform over the vocabulary, drawn
+first, then the table E [vocab][d_model] with variance 1/d_model (so that
+E * sqrt(d_model) has unit variance, the scale of the encoding); positions
+from 0.
 """
 
 import dataclasses
@@ -59,6 +64,7 @@ class Workload:
     description: str = ""
     d_ff: int = 0        # encoder layer: FFN hidden width
     eps: float = 1e-5    # encoder layer: LayerNorm epsilon
+    vocab: int = 0       # input embedding: vocabulary size
 
     @property
     def torch_dtype(self):
@@ -110,6 +116,15 @@ WORKLOADS = {
         "encoder_layer_base", "layer", "bf16", B=32, n_q=100, n_k=100, h=8, d_k=64, d_v=64,
         mask=MASK_NONE, d_model=512, self_attn=True, d_ff=2048, eps=1e-5,
         description="encoder layer (Post-LN), bf16, B=32 n=100 d_model=512 h=8 d_ff=2048"),
+    # The model's input for the encoder batch: token ids into a vocabulary of
+    # about 37000 sub-words (wiki.hugogu.cn "Attention Is All You Need", the
+    # input-embedding paragraph), embedding rows scaled by sqrt(d_model) plus
+    # the sinusoidal encoding.
+    "embed_positional_base": Workload(
+        "embed_positional_base", "embed", "bf16", B=32, n_q=100, n_k=100, h=0, d_k=0, d_v=0,
+        mask=MASK_NONE, d_model=512, vocab=37000,
+        description="token embedding x sqrt(d_model) + sinusoidal encoding, bf16, B=32 n=100 "
+                    "d_model=512 vocab=37000"),
 }
 
 ORDER = ["sdpa_f32_tiny", "encoder_self_base", "decoder_causal_base", "cross_padded_big",
@@ -131,6 +146,7 @@ def generate(w: Workload, seed: int = 0):
     mha:  X_q [B][n_q][d_model], X_kv (the same tensor object for
           self-attention), Wq/Wk [d_model][h*d_k], Wv [d_model][h*d_v],
           Wo [h*d_v][d_model], key_lengths.
+    embed: tokens int32 [B][n], E [vocab][d_model], pos0.
     layer: X [B][n][d_model], the block's Wq, Wk, Wv, Wo, then ln1_gamma,
           ln1_beta [d_model], W1 [d_model][d_ff], b1 [d_ff], W2 [d_ff][d_model],
           b2, ln2_gamma, ln2_beta [d_model], key_lengths.
@@ -144,6 +160,10 @@ def generate(w: Workload, seed: int = 0):
         out["K"] = _normal(g, (w.B, w.h, w.n_k, w.d_k), 1.0, dt)
         out["V"] = _normal(g, (w.B, w.h, w.n_k, w.d_v), 1.0, dt)
         out["scale"] = 1.0 / math.sqrt(w.d_k)
+    elif w.kind == "embed":
+        out["tokens"] = torch.randint(0, w.vocab, (w.B, w.n_q), generator=g, dtype=torch.int32)
+        out["E"] = _normal(g, (w.vocab, w.d_model), 1.0 / math.sqrt(w.d_model), dt)
+        out["pos0"] = 0
     elif w.kind == "layer":
         if w.n_q != w.n_k:
             raise ValueError("an encoder layer attends to its own positions (n_q == n_k)")

@@ -13,7 +13,9 @@
  * around the block, one Post-LN encoder layer:
  *
  *   x1 = LayerNorm(X + MultiHead(X, X, X)),  Y = LayerNorm(x1 + FFN(x1)),
- *   FFN(x) = max(0, x W1 + b1) W2 + b2.
+ *   FFN(x) = max(0, x W1 + b1) W2 + b2,
+ *
+ * and the layer's input, X = E[tokens] * sqrt(d_model) + PE (sinusoidal).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -39,8 +41,8 @@
  *   exception crosses this interface.
  *
  * Supported on the GPU in this version: d_k = d_v = 64 for attention;
- * bf16 for every entry point; fp32 for sdpa_forward.  Other combinations
- * return MHA_ERR_UNSUPPORTED.
+ * bf16 for every entry point; fp32 for sdpa_forward and
+ * embed_positional_forward.  Other combinations return MHA_ERR_UNSUPPORTED.
  */
 #ifndef MHA_H
 #define MHA_H
@@ -340,6 +342,40 @@ int encoder_layer_forward_timed(const void* X, const void* Wq, const void* Wk, c
  * non-positive sizes.
  */
 int encoder_layer_launches(int n, int d_model);
+
+/*
+ * embed_positional_forward -- the model's input: token embedding scaled by
+ * sqrt(d_model) plus the sinusoidal positional encoding, fused:
+ *   out[b][p][j] = E[tokens[b][p]][j] * sqrt(d_model) + PE(pos0 + p, j)
+ *   PE(pos, 2i) = sin(pos / 10000^(2i/d_model)), PE(pos, 2i+1) = cos(same)
+ * Sources: devpress.csdn.net "【深度学习】Transformer", section 4 (equation
+ * (4.1), Table 4.1, the worked example scaling the input by sqrt(d_model)
+ * before the encoding is added); hex4c59.cc "读懂 Attention Is All You Need",
+ * section "没有循环，模型怎样知道词序？" (embedding row looked up by token id,
+ * times sqrt(d_model), plus the encoding of the same width).
+ *
+ *   tokens  DEVICE int32 [B][n], token ids; an id outside [0, vocab) gives
+ *           a row of NaN (nothing is read for it) -- ids are device data and
+ *           are not checked on the host.
+ *   E       [vocab][d_model] embedding table;  out [B][n][d_model]
+ *   pos0    position of each sequence's first token (>= 0; 0 for whole
+ *           sentences, the step index when one new token is embedded during
+ *           incremental decoding); positions are pos0 .. pos0 + n - 1.
+ *   dtype   MHA_DTYPE_BF16 or MHA_DTYPE_F32 (E and out).
+ *   d_model % 8 == 0 (else MHA_ERR_UNSUPPORTED); B <= 524280.
+ * Frequencies and angles are formed in double precision and reduced to one
+ * turn there; sine and cosine of the reduced angle are single precision
+ * (error ~2e-7 up to positions of 2^24); the sum is formed in fp32 and
+ * rounded once to the output type.  One launch.
+ */
+int embed_positional_forward(const int32_t* tokens, const void* E, void* out, int B, int n,
+                             int vocab, int d_model, int pos0, int dtype, hipStream_t stream);
+
+/* embed_positional_forward with launch events (one launch), as the other
+ * _timed variants. */
+int embed_positional_forward_timed(const int32_t* tokens, const void* E, void* out, int B, int n,
+                                   int vocab, int d_model, int pos0, int dtype, hipStream_t stream,
+                                   hipEvent_t* events, int capacity, int* n_launches);
 
 /* Text of a status code (static storage; never NULL). */
 const char* mha_status_str(int status);

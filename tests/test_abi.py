@@ -273,3 +273,23 @@ def test_encoder_layer_launch_plan(L):
     assert L.encoder_layer_launches(100, 512) == 6        # fused block plan + 4
     assert L.encoder_layer_launches(512, 512) == 7        # stacked projection plan + 4
     assert L.encoder_layer_launches(0, 512) == DIM
+
+
+def emb(L, T=FAKE, E=FAKE, O=FAKE2, B=2, n=8, vocab=100, d=512, pos0=0, dtype=BF16):
+    return L.embed_positional_forward(T, E, O, B, n, vocab, d, pos0, dtype, None)
+
+
+def test_embed_positional_rejections(L):
+    assert emb(L, T=None) == NULL
+    assert emb(L, O=None) == NULL
+    assert emb(L, B=0) == DIM
+    assert emb(L, vocab=0) == DIM
+    assert emb(L, pos0=-1) == DIM
+    assert emb(L, pos0=(1 << 31) - 4) == DIM              # last position overflows int32
+    assert emb(L, d=(1 << 20) + 8) == DIM
+    assert emb(L, d=500) == UNSUP
+    assert emb(L, dtype=7) == UNSUP
+    assert emb(L, E=MISALIGNED) == UNSUP
+    assert emb(L, T=ctypes.c_void_p(0x10002)) == UNSUP    # token ids not 4-byte aligned
+    assert L.embed_positional_forward_timed(FAKE, FAKE, FAKE2, 2, 8, 100, 512, 0, BF16, None,
+                                            None, 0, None) == -9
