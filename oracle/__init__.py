@@ -15,7 +15,9 @@ Two independent formulations are provided:
   ``oracle.layer`` -- the same for residual + LayerNorm and the
   position-wise feed-forward network of an encoder layer;
   ``oracle.embedding`` -- the scaled token embedding plus the sinusoidal
-  positional encoding.
+  positional encoding;
+  ``oracle.backward`` -- the gradients of attention (dQ, dK, dV) and the row
+  log-sum-exp a forward pass saves for them.
 * ``oracle.bruteforce`` -- pure-Python loops with ``math.exp``/``math.fsum``,
   one query row at a time, for tiny inputs; it cross-checks the matrix form.
 
@@ -43,6 +45,9 @@ computed):
 * For the input side (``oracle.embedding``): devpress.csdn.net section 4
   (equation (4.1), Table 4.1, the worked example, the shift identity);
   hex4c59.cc section "没有循环，模型怎样知道词序？".
+* For the backward pass (``oracle.backward``): hex4c59.cc sections
+  "训练能并行，不意味着一次生成整句话" and "参数是怎样学出来的？"; the
+  gradients are those of devpress.csdn.net section 2.1 equation (2.4).
 
 Parity status of every function is stated in its docstring.  All functions
 are pinned by ``tests/test_oracle.py`` (printed values from the pages,
@@ -72,5 +77,6 @@ from .bruteforce import (  # noqa: F401
     layer_norm_bruteforce,
     mha_bruteforce,
 )
+from .backward import row_logsumexp, sdpa_backward_ref  # noqa: F401
 from .embedding import embed_positional_ref, positional_encoding  # noqa: F401
 from .layer import add_layer_norm, encoder_layer_ref, ffn, layer_norm  # noqa: F401

@@ -715,3 +715,103 @@ ALL_EMBED_CHECKS = [
     check_pe_shift_identity,
     check_embedding_bruteforce,
 ]
+
+
+# ------------------------------------------------------------ backward pass pins
+# Implementation interface: sdpa_backward_ref(Q, K, V, dO, scale, mask_kind,
+# key_lengths) -> (dQ, dK, dV); row_logsumexp(Q, K, scale, mask_kind, key_lengths).
+
+def _bwd_inputs(seed, B, h, n_q, n_k, d):
+    r = _rng(seed)
+    return (r.standard_normal((B, h, n_q, d)), r.standard_normal((B, h, n_k, d)),
+            r.standard_normal((B, h, n_k, d)), r.standard_normal((B, h, n_q, d)))
+
+
+def check_bwd_finite_differences(impl):
+    """Every gradient element against the central difference of the loss
+    sum(dO * O) in float64 (step 1e-5: truncation ~1e-10, rounding ~1e-11),
+    for each mask kind.  The forward is the oracle's sdpa_ref, already
+    pinned on its own; the backward is never consulted for the reference."""
+    import oracle
+    cases = [(NONE, 3, 4, None), (CAUSAL, 4, 4, None), (PAD, 3, 5, [5, 2]), (BOTH, 4, 4, [3, 1])]
+    for kind, n_q, n_k, kl in cases:
+        Q, K, V, dO = _bwd_inputs(40 + kind, 2, 2, n_q, n_k, 3)
+        kl = None if kl is None else np.array(kl)
+        scale = 0.7
+        got = impl.sdpa_backward_ref(Q, K, V, dO, scale, kind, kl)
+        base = [Q, K, V]
+        for which in range(3):
+            want = np.zeros_like(base[which])
+            it = np.nditer(base[which], flags=["multi_index"])
+            for _ in it:
+                idx = it.multi_index
+                vals = []
+                for sgn in (1.0, -1.0):
+                    args = [t.copy() for t in base]
+                    args[which][idx] += sgn * 1e-5
+                    vals.append(float((dO * oracle.sdpa_ref(*args, scale, kind, kl)).sum()))
+                want[idx] = (vals[0] - vals[1]) / 2e-5
+            assert np.abs(got[which] - want).max() <= 1e-7, (kind, which, np.abs(got[which] - want).max())
+
+
+def check_bwd_invariants(impl):
+    """Shifting every key of a sequence by the same vector adds a constant to
+    each row of scores and leaves the softmax unchanged, so the key gradients
+    of each (batch, head) sum to zero; keys no query can see (padding) get
+    exactly zero dK and dV; under the causal mask the last key is seen by the
+    last query only."""
+    Q, K, V, dO = _bwd_inputs(45, 2, 3, 6, 6, 4)
+    for kind, kl in ((NONE, None), (CAUSAL, None), (PAD, np.array([4, 6])), (BOTH, np.array([2, 5]))):
+        dQ, dK, dV = impl.sdpa_backward_ref(Q, K, V, dO, 0.5, kind, kl)
+        assert np.abs(dK.sum(axis=2)).max() <= 1e-12
+        if kl is not None:
+            assert np.all(dK[0, :, kl[0]:] == 0) and np.all(dV[0, :, kl[0]:] == 0)
+    _, dK, dV = impl.sdpa_backward_ref(Q, K, V, dO, 0.5, CAUSAL, None)
+    dO2 = dO.copy()
+    dO2[:, :, :5] = _rng(46).standard_normal(dO2[:, :, :5].shape)
+    _, dK2, dV2 = impl.sdpa_backward_ref(Q, K, V, dO2, 0.5, CAUSAL, None)
+    assert np.array_equal(dK2[:, :, 5], dK[:, :, 5]) and np.array_equal(dV2[:, :, 5], dV[:, :, 5])
+    assert not np.allclose(dV2[:, :, 4], dV[:, :, 4])
+
+
+def check_bwd_uniform_weights(impl):
+    """Q = 0: every visible key has weight 1/n.  Then dV_j = (1/n) sum_i dO_i,
+    dK = 0 exactly, and dQ_i = (scale/n) sum_j (dO_i . (V_j - mean V)) K_j
+    (unmasked, written out with loops)."""
+    _, K, V, dO = _bwd_inputs(47, 1, 2, 3, 5, 4)
+    Q = np.zeros((1, 2, 3, 4))
+    scale = 0.8
+    dQ, dK, dV = impl.sdpa_backward_ref(Q, K, V, dO, scale, NONE, None)
+    n = 5
+    assert np.array_equal(dK, np.zeros_like(dK))
+    for hh in range(2):
+        vbar = V[0, hh].mean(axis=0)
+        for j in range(n):
+            assert np.allclose(dV[0, hh, j], dO[0, hh].sum(axis=0) / n, atol=1e-14)
+        for i in range(3):
+            want = sum((dO[0, hh, i] @ (V[0, hh, j] - vbar)) * K[0, hh, j] for j in range(n)) * scale / n
+            assert np.allclose(dQ[0, hh, i], want, atol=1e-13)
+
+
+def check_row_logsumexp(impl):
+    """Against a loop with math.fsum over the visible keys; exp(S - lse) rows
+    then sum to one."""
+    Q, K, _, _ = _bwd_inputs(48, 2, 2, 4, 4, 3)
+    kl = np.array([4, 2])
+    for kind in (NONE, CAUSAL, PAD, BOTH):
+        lse = impl.row_logsumexp(Q, K, 0.6, kind, kl if kind & PAD else None)
+        for b in range(2):
+            for hh in range(2):
+                for i in range(4):
+                    vis = [j for j in range(4) if not ((kind & CAUSAL and j > i) or (kind & PAD and j >= kl[b]))]
+                    s = [0.6 * float(Q[b, hh, i] @ K[b, hh, j]) for j in vis]
+                    want = math.log(math.fsum(math.exp(x) for x in s))
+                    assert abs(lse[b, hh, i] - want) <= 1e-13
+
+
+ALL_BWD_CHECKS = [
+    check_bwd_finite_differences,
+    check_bwd_invariants,
+    check_bwd_uniform_weights,
+    check_row_logsumexp,
+]

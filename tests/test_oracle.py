@@ -15,6 +15,11 @@ def test_sdpa_pin(check):
     check(oracle)
 
 
+@pytest.mark.parametrize("check", pins.ALL_BWD_CHECKS, ids=lambda f: f.__name__)
+def test_bwd_pin(check):
+    check(oracle)
+
+
 @pytest.mark.parametrize("check", pins.ALL_EMBED_CHECKS, ids=lambda f: f.__name__)
 def test_embed_pin(check):
     check(oracle)

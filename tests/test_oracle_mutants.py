@@ -284,3 +284,55 @@ def test_unmutated_embed_copy_passes_every_pin():
 def test_embed_mutant_is_caught(name):
     failed = _fails_some_embed_pin(EMBED_MUTANTS[name]())
     assert failed, f"planted mistake {name!r} passed every pin"
+
+
+# ------------------------------------------------------------ backward mutants
+
+def _bwd(variant):
+    def sdpa_backward_ref(Q, K, V, dO, scale, mask_kind=0, key_lengths=None):
+        P = oracle.attention_weights(Q, K, scale, mask_kind, key_lengths)
+        Pt = np.swapaxes(P, -1, -2)
+        dV = (P if variant == "dv_untransposed" else Pt) @ dO
+        dP = dO @ np.swapaxes(V, -1, -2)
+        if variant == "ds_no_centering":
+            dS = P * dP
+        elif variant == "ds_centered_by_mean":
+            dS = P * (dP - dP.mean(axis=-1, keepdims=True))
+        else:
+            dS = P * (dP - (P * dP).sum(axis=-1, keepdims=True))
+        sq = 1.0 if variant == "dq_unscaled" else scale
+        dQ = sq * (dS @ K)
+        dK = scale * ((dS if variant == "dk_untransposed" else np.swapaxes(dS, -1, -2)) @ Q)
+        return dQ, dK, dV
+
+    def row_logsumexp(Q, K, scale, mask_kind=0, key_lengths=None):
+        lse = oracle.row_logsumexp(Q, K, scale, mask_kind, key_lengths)
+        return lse / scale if variant == "lse_unscaled" else lse
+
+    return types.SimpleNamespace(sdpa_backward_ref=sdpa_backward_ref, row_logsumexp=row_logsumexp)
+
+
+BWD_MUTANTS = {v: (lambda v=v: _bwd(v)) for v in
+               ("dv_untransposed", "ds_no_centering", "ds_centered_by_mean", "dq_unscaled",
+                "dk_untransposed", "lse_unscaled")}
+
+
+def _fails_some_bwd_pin(impl):
+    failed = []
+    for check in pins.ALL_BWD_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check(impl)
+        except (AssertionError, ValueError, FloatingPointError, IndexError):
+            failed.append(check.__name__)
+    return failed
+
+
+def test_unmutated_bwd_copy_passes_every_pin():
+    assert _fails_some_bwd_pin(_bwd("none")) == []
+
+
+@pytest.mark.parametrize("name", sorted(BWD_MUTANTS))
+def test_bwd_mutant_is_caught(name):
+    failed = _fails_some_bwd_pin(BWD_MUTANTS[name]())
+    assert failed, f"planted mistake {name!r} passed every pin"
