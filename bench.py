@@ -6,8 +6,10 @@ A step is one pass of the whole path over one batch: for a multi-head block
 the input projection(s), the fused attention and the output projection; for
 bare attention the fused attention kernel; for an encoder layer the block,
 residual + LayerNorm, the two FFN GEMMs and residual + LayerNorm; for the
-input embedding the fused lookup x sqrt(d_model) + positional encoding
-(no attention: its line carries the roofline and a null metric value).  Inputs are seeded synthetic
+input embedding the fused lookup x sqrt(d_model) + positional encoding; for
+the backward pass its two kernels (dQ, then dK/dV) on resident Q, K, V, O,
+dO and row log-sum-exp.  The embedding and backward lines carry their
+roofline and a null forward-attention metric value.  Inputs are seeded synthetic
 tensors of the workload's shapes, resident in GPU memory before timing, and
 rotated through enough buffer sets that every step reads memory no earlier
 step left in the 256 MB Infinity Cache.
@@ -80,6 +82,8 @@ def layer_launches(w):
 def step_launches(w):
     if w.kind in ("sdpa", "embed"):
         return 1
+    if w.kind == "bwd":
+        return 2
     return layer_launches(w) if w.kind == "layer" else mha_launches(w)
 
 
@@ -105,6 +109,18 @@ def kernel_plan(w, n_launches=None):
     if w.kind == "sdpa":
         plan.append(dict(name="attention", flops=0.0, bytes=0.0,
                          peak_kind="mfma" if w.dtype == "bf16" else "fp32", has_attention=True))
+        return plan, None
+    if w.kind == "bwd":
+        # per visible (query, key) pair the dQ kernel runs three 2-d flop
+        # products (S, dP, dQ), the dK/dV kernel four (S, dP, dV, dK)
+        pairs = bwd_pairs(w)
+        rows_q, rows_k = B * h * nq, B * h * nk
+        plan.append(dict(name="backward_dq", flops=6.0 * pairs * dk,
+                         bytes=float(e * rows_q * dk * 4 + 4 * rows_q * 2 + e * rows_k * dk * 2),
+                         peak_kind="mfma", has_attention=False))
+        plan.append(dict(name="backward_dkdv", flops=8.0 * pairs * dk,
+                         bytes=float(e * rows_k * dk * 4 + e * rows_q * dk * 2 + 4 * rows_q * 2),
+                         peak_kind="mfma", has_attention=False))
         return plan, None
     if w.kind == "embed":
         # gather one table row per token, write one row per token, read the ids
@@ -137,6 +153,19 @@ def kernel_plan(w, n_launches=None):
         gemm("ffn_gemm_2", M, w.d_ff, w.d_model, bias=True)
         layernorm("residual_layernorm_2", M, w.d_model)
     return plan, None
+
+
+def bwd_pairs(w, key_lengths=None):
+    """Visible (query, key) pairs of all heads."""
+    L = [w.n_k] * w.B if key_lengths is None else [int(x) for x in key_lengths]
+    pairs = 0.0
+    for b in range(w.B):
+        if w.mask & 1:
+            full = min(L[b], w.n_q)
+            pairs += full * (full + 1) / 2.0 + max(0, w.n_q - full) * L[b]
+        else:
+            pairs += w.n_q * L[b]
+    return pairs * w.h
 
 
 def attention_accounting(w, key_lengths):
@@ -192,6 +221,25 @@ class Step:
                 self.sets.append((P(Q.data_ptr()), P(K.data_ptr()), P(V.data_ptr()), P(O.data_ptr()),
                                   w.B, w.h, w.n_q, w.n_k, w.d_k, w.d_v, float(x["scale"]), w.mask,
                                   self.kl, code))
+            elif w.kind == "bwd":
+                Q, K, V, dO = (x[k].to(dev) for k in ("Q", "K", "V", "dO"))
+                O = torch.empty_like(Q)
+                lse = torch.empty((w.B, w.h, w.n_q), dtype=torch.float32, device=dev)
+                st = self.lib.sdpa_forward_lse(P(Q.data_ptr()), P(K.data_ptr()), P(V.data_ptr()),
+                                               P(O.data_ptr()), P(lse.data_ptr()), w.B, w.h, w.n_q,
+                                               w.n_k, w.d_k, w.d_v, float(x["scale"]), w.mask, self.kl,
+                                               bnd.DTYPE_BF16, P(torch.cuda.current_stream().cuda_stream))
+                if st != 0:
+                    raise RuntimeError(f"sdpa_forward_lse failed with status {st}")
+                dQ, dK, dV = torch.empty_like(Q), torch.empty_like(K), torch.empty_like(V)
+                nbytes = int(self.lib.sdpa_backward_workspace_bytes(w.B, w.h, w.n_q))
+                ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+                self.keep.append((Q, K, V, dQ, dK, dV, O, lse, dO, ws))
+                self.sets.append((P(Q.data_ptr()), P(K.data_ptr()), P(V.data_ptr()), P(O.data_ptr()),
+                                  P(dO.data_ptr()), P(lse.data_ptr()), P(dQ.data_ptr()),
+                                  P(dK.data_ptr()), P(dV.data_ptr()), w.B, w.h, w.n_q, w.n_k, w.d_k,
+                                  w.d_v, float(x["scale"]), w.mask, self.kl, bnd.DTYPE_BF16,
+                                  P(ws.data_ptr()), nbytes))
             elif w.kind == "embed":
                 T = x["tokens"].to(dev)
                 E = x["E"].to(dev)
@@ -224,11 +272,14 @@ class Step:
                                   bnd.DTYPE_BF16, P(ws.data_ptr()), ws.numel()))
         self.n_launches = step_launches(w)
         names = {"sdpa": "sdpa_forward", "mha": "mha_forward", "layer": "encoder_layer_forward",
-                 "embed": "embed_positional_forward"}
+                 "embed": "embed_positional_forward", "bwd": "sdpa_backward"}
         self.entry = names[w.kind]
 
     def output(self, i):
         return self.keep[i][3]
+
+    def parity_output(self, i):
+        return self.keep[i][3:6] if self.w.kind == "bwd" else self.keep[i][3]
 
     def run(self, i, stream):
         st = getattr(self.lib, self.entry)(*self.sets[i], stream)
@@ -245,6 +296,8 @@ class Step:
 
 def set_bytes(w):
     e = 2 if w.dtype == "bf16" else 4
+    if w.kind == "bwd":
+        return e * w.B * w.h * (w.n_q * 64 * 4 + w.n_k * 64 * 4) + 8 * w.B * w.h * w.n_q
     if w.kind == "embed":
         return e * (w.vocab * w.d_model + w.B * w.n_q * w.d_model) + 4 * w.B * w.n_q
     if w.kind == "sdpa":
@@ -277,6 +330,24 @@ def parity_check(w, x, out):
     from head_attention_forward_amd.workloads import to_f64
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
     rows = "all"
+    if w.kind == "bwd":
+        # two sampled (batch, head) pairs, whole gradients; the test bar:
+        # rel-L2 <= 2u and every element within 4u max(max|want|, 1), u = 2^-8
+        u = 2.0 ** -8
+        worst, rel_max, max_abs = 0.0, 0.0, 0.0
+        picks = [(0, 0), (w.B - 1, w.h - 1)]
+        for b, hh in picks:
+            sl = lambda t: to_f64(t[b:b + 1, hh:hh + 1])  # noqa: E731
+            want = oracle.sdpa_backward_ref(sl(x["Q"]), sl(x["K"]), sl(x["V"]), sl(x["dO"]),
+                                            x["scale"], w.mask, None if kl is None else kl[b:b + 1])
+            for got_t, want_t in zip(out, want):
+                got = to_f64(got_t[b:b + 1, hh:hh + 1])
+                err = np.abs(got - want_t)
+                worst = max(worst, float(err.max()) / (4 * u * max(float(np.abs(want_t).max()), 1.0)))
+                rel_max = max(rel_max, float(np.linalg.norm(got - want_t) / np.linalg.norm(want_t)))
+                max_abs = max(max_abs, float(err.max()))
+        return dict(max_abs=max_abs, rel_l2=rel_max, worst_over_bound=worst,
+                    ok=bool(worst <= 1.0 and rel_max <= 2 * u), rows="2 sampled (batch, head) pairs")
     if w.kind == "embed":
         want = oracle.embed_positional_ref(x["tokens"].numpy(), to_f64(x["E"]), x["pos0"])
         got = to_f64(out)
@@ -342,6 +413,31 @@ def cpu_baseline(w, x, target_s):
         threads = 1
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
 
+    if w.kind == "bwd":
+        Q, K, V, dO = (to_f64(x[k]) for k in ("Q", "K", "V", "dO"))
+
+        def run_pairs(n):  # the first n (batch, head) pairs
+            done = 0
+            for b in range(w.B):
+                for hh in range(w.h):
+                    if done >= n:
+                        return
+                    oracle.sdpa_backward_ref(Q[b:b + 1, hh:hh + 1], K[b:b + 1, hh:hh + 1],
+                                             V[b:b + 1, hh:hh + 1], dO[b:b + 1, hh:hh + 1], x["scale"],
+                                             w.mask, None if kl is None else kl[b:b + 1])
+                    done += 1
+        t0 = time.perf_counter()
+        run_pairs(1)
+        t1 = max(time.perf_counter() - t0, 1e-6)
+        n = int(max(1, min(w.B * w.h, target_s / t1)))
+        t0 = time.perf_counter()
+        run_pairs(n)
+        t = time.perf_counter() - t0
+        flops = 10.0 * bwd_pairs(w) / (w.B * w.h) * w.d_k * n
+        return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                    sample=f"{n} of {w.B * w.h} (batch, head) pairs, backward; {t:.2f} s, numpy float64"
+                           " (algorithmic backward flops: 5 products per visible pair)",
+                    seconds=round(t, 3))
     if w.kind == "embed":
         tokens, E = x["tokens"].numpy(), to_f64(x["E"])
         e = 2 if w.dtype == "bf16" else 4
@@ -424,6 +520,8 @@ KERNEL_SOURCES = {
     "gemm_bf16_kernel": ("gemm_bf16.hip", "mha_api.hip"),
     "add_layernorm_bf16_kernel": ("add_layernorm_bf16.hip", "mha_api.hip"),
     "embed_positional_kernel": ("embed_positional.hip", "mha_api.hip"),
+    "attn_bwd_dq_kernel": ("attn_bwd_bf16.hip", "wave_attention.h", "mha_api.hip"),
+    "attn_bwd_dkdv_kernel": ("attn_bwd_bf16.hip", "wave_attention.h", "mha_api.hip"),
 }
 
 
@@ -501,7 +599,7 @@ def main():
     if not args.no_parity:
         step.run(0, sp)
         torch.cuda.synchronize()
-        parity = parity_check(w, x, step.output(0))
+        parity = parity_check(w, x, step.parity_output(0))
         log(f"parity vs oracle: {parity}")
         if not parity["ok"]:
             print(json.dumps(dict(metric=METRIC, value=None, error="parity failed", parity=parity)))
@@ -617,6 +715,7 @@ def main():
     kinds = {"mha": "multi-head block (projections + attention + output projection)",
              "sdpa": "bare attention",
              "embed": "token embedding x sqrt(d_model) + sinusoidal positional encoding",
+             "bwd": "attention backward (dQ, dK, dV from dO, O and the row log-sum-exp)",
              "layer": "encoder layer, Post-LN (block, residual + LayerNorm, FFN, residual + LayerNorm)"}
     cfg = dict(workload=w.name, B=w.B, n_q=w.n_q, n_k=w.n_k, h=w.h, d_k=w.d_k, d_v=w.d_v,
                mask={0: "none", 1: "causal", 2: "key_padding", 3: "causal+key_padding"}[w.mask],
@@ -664,6 +763,15 @@ def main():
     }
     if w.kind == "embed":
         out["data"] = "synthetic (seeded uniform token ids, N(0,1/d_model) embedding table)"
+    if w.kind == "bwd":
+        out["data"] = "synthetic (seeded N(0,1) Q, K, V and upstream gradient dO)"
+        bf = 10.0 * bwd_pairs(w, x["key_lengths"]) * w.d_k
+        out["backward"] = dict(algorithmic_flops_per_step=bf,
+                               algorithmic_tflops=round(bf / (ms_step * 1e-3) / 1e12, 2),
+                               pct_of_bf16_mfma_peak=round(100 * bf / (ms_step * 1e-3) / 1e12 /
+                                                           PEAK_BF16_TFLOPS, 2),
+                               note="5 products (S, dP, dV, dK, dQ) of 2 d flops per visible pair; "
+                                    "the kernels also recompute S and dP in both kernels")
     if w.kind == "layer":
         lf = layer_flops(w)
         out["layer"] = dict(matmul_flops_per_step=lf,

@@ -19,7 +19,9 @@ from ._binding import (  # noqa: F401
     mha_forward,
     mha_project_in,
     mha_project_out,
+    sdpa_backward,
     sdpa_forward,
+    sdpa_forward_lse,
     workspace_bytes,
     workspace_views,
 )

@@ -56,6 +56,12 @@ _SIG = {
     "encoder_layer_launches": (_I, [_I, _I]),
     "embed_positional_forward": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]),
     "embed_positional_forward_timed": (_I, [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _I, _P]),
+    "sdpa_forward_lse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _I,
+                              _P]),
+    "sdpa_backward_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "sdpa_backward": (_I, [_P] * 9 + [_I] * 6 + [ctypes.c_float, _I, _P, _I, _P, ctypes.c_size_t, _P]),
+    "sdpa_backward_timed": (_I, [_P] * 9 + [_I] * 6 + [ctypes.c_float, _I, _P, _I, _P,
+                                                      ctypes.c_size_t, _P, _P, _I, _P]),
 }
 
 _lib = None
@@ -349,3 +355,48 @@ def embed_positional_forward(tokens, E, pos0=0, out=None, stream=None):
                                         vocab, d_model, int(pos0), _dtype_code(E), _stream(stream))
     _check("embed_positional_forward", st)
     return out
+
+
+def sdpa_forward_lse(Q, K, V, scale=None, mask_kind=0, key_lengths=None, out=None, lse=None,
+                     stream=None):
+    """sdpa_forward (bf16) that also returns the row log-sum-exp [B][h][n_q]
+    (fp32) for the backward pass.  Returns (O, lse)."""
+    B, h, n_q, d_k = Q.shape
+    n_k, d_v = K.shape[2], V.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((B, h, n_q, d_v), dtype=Q.dtype, device=Q.device)
+    if lse is None:
+        lse = torch.empty((B, h, n_q), dtype=torch.float32, device=Q.device)
+    arr, kl = _key_lengths(mask_kind, key_lengths, B)
+    st = lib().sdpa_forward_lse(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(out, "out"),
+                                _dev(lse, "lse"), B, h, n_q, n_k, d_k, d_v, float(scale),
+                                int(mask_kind), kl, _dtype_code(Q), _stream(stream))
+    _check("sdpa_forward_lse", st)
+    return out, lse
+
+
+def sdpa_backward(Q, K, V, O, dO, lse, scale=None, mask_kind=0, key_lengths=None,
+                  workspace=None, stream=None):
+    """(dQ, dK, dV) of O = softmax(Q K^T * scale + M) V for the upstream
+    gradient dO (bf16, head-major, d = 64), given the forward's output O and
+    row log-sum-exp lse."""
+    B, h, n_q, d_k = Q.shape
+    n_k, d_v = K.shape[2], V.shape[3]
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    dQ = torch.empty_like(Q)
+    dK = torch.empty_like(K)
+    dV = torch.empty_like(V)
+    if workspace is None:
+        n = int(lib().sdpa_backward_workspace_bytes(B, h, n_q))
+        workspace = torch.empty(max(n, 1), dtype=torch.uint8, device=Q.device)
+    arr, kl = _key_lengths(mask_kind, key_lengths, B)
+    st = lib().sdpa_backward(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(O, "O"), _dev(dO, "dO"),
+                             _dev(lse, "lse"), _dev(dQ, "dQ"), _dev(dK, "dK"), _dev(dV, "dV"),
+                             B, h, n_q, n_k, d_k, d_v, float(scale), int(mask_kind), kl,
+                             _dtype_code(Q), _dev(workspace, "workspace"),
+                             workspace.numel() * workspace.element_size(), _stream(stream))
+    _check("sdpa_backward", st)
+    return dQ, dK, dV

@@ -137,6 +137,8 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
 
   const float inv = wa.inv_sum();
   if (my_q < a.n_q) wa.store(Op + (int64_t)my_q * a.o_sr, inv);
+  if (a.lse != nullptr && my_q < a.n_q && wa.g == 0)
+    a.lse[(int64_t)(b * a.h + hh) * a.n_q + my_q] = wa.row_lse(inv);
 }
 
 template <int NW, int NS, int WPE>

@@ -144,6 +144,8 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_bf16_d64_kernel(const Att
   }
   const float inv = wa.inv_sum();
   if (my_q < a.n_q) wa.store(Op + (int64_t)my_q * a.o_sr, inv);
+  if (a.lse != nullptr && my_q < a.n_q && wa.g == 0)
+    a.lse[(int64_t)(b * a.h + hh) * a.n_q + my_q] = wa.row_lse(inv);
 }
 
 }  // namespace

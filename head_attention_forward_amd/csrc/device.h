@@ -48,6 +48,19 @@ __device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsign
                : "memory", "m0");
 }
 
+// 4-byte global -> LDS copy per lane (same addressing as dma16_s; lane l
+// writes LDS byte address lds + 4 l): 64 consecutive floats per wave.
+__device__ __forceinline__ void dma4_s(const void* sbase, unsigned voff, unsigned lds) {
+  const unsigned long long p = (unsigned long long)(size_t)sbase;
+  const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
+  const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)p);
+  const unsigned long long sp = ((unsigned long long)hi << 32) | (unsigned long long)lo;
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+               :
+               : "s"(lds), "v"(voff), "s"((const void*)(size_t)sp)
+               : "memory", "m0");
+}
+
 // A wave-uniform pointer pinned to SGPRs (uniform 64-bit products are
 // otherwise formed, and kept, in VGPRs).
 template <typename T>

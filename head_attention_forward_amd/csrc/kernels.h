@@ -24,6 +24,31 @@ struct AttnArgs {
   float scale;        // multiplies q.k
   int causal;         // key j hidden from query i when j > i
   int padded;         // key j hidden in batch b when j >= key_len[b]
+  // Optional (bf16 kernels): row log-sum-exp, lse[(b*h + head)*n_q + i] =
+  // ln(sum over visible keys j of exp(scale * q_i . k_j)); null: not written.
+  float* lse;
+  int32_t key_len[MHA_MAX_PADDED_BATCH];
+};
+
+// Attention backward: dQ, dK, dV of O = softmax(Q K^T * scale + M) V from
+// the upstream gradient dO and the forward's row log-sum-exp.  Every tensor
+// is head-major [B][h][n][64] bf16; Dw is fp32 workspace [B][h][n_q] that
+// receives rowsum(dO * O).
+struct BwdArgs {
+  const void* Q;
+  const void* K;
+  const void* V;
+  const void* O;
+  const void* dO;
+  const float* lse;
+  void* dQ;
+  void* dK;
+  void* dV;
+  float* Dw;
+  int B, h, n_q, n_k;
+  float scale;
+  int causal;
+  int padded;
   int32_t key_len[MHA_MAX_PADDED_BATCH];
 };
 
@@ -108,6 +133,9 @@ hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents e
 hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev = {});
+// Backward: the dQ kernel (also writes Dw), then the dK/dV kernel (reads Dw).
+hipError_t launch_attn_bwd_dq(const BwdArgs& a, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_add_layernorm_bf16(const LnArgs& a, hipStream_t s, LaunchEvents ev = {});
 // f32 != 0: E and out are fp32, else bf16.
 hipError_t launch_embed_positional(const EmbedArgs& a, int f32, hipStream_t s, LaunchEvents ev = {});

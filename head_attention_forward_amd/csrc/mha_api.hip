@@ -626,4 +626,110 @@ int embed_positional_forward_timed(const int32_t* tokens, const void* E, void* o
   return st;
 }
 
+int sdpa_forward_lse(const void* Q, const void* K, const void* V, void* O, float* lse, int B,
+                     int h, int n_q, int n_k, int d_k, int d_v, float scale, int mask_kind,
+                     const int32_t* key_lengths, int dtype, hipStream_t stream) {
+  if (!Q || !K || !V || !O || !lse) return MHA_ERR_NULL;
+  int st = check_attn_dims(B, h, n_q, n_k, d_k, d_v);
+  if (st != MHA_OK) return st;
+  if (!(isfinite(scale) && scale > 0.f)) return MHA_ERR_SCALE;
+  st = check_mask(mask_kind, B, n_q, n_k, key_lengths);
+  if (st != MHA_OK) return st;
+  if (dtype != MHA_DTYPE_BF16) return MHA_ERR_UNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O) || ((uintptr_t)lse & 3u))
+    return MHA_ERR_UNSUPPORTED;
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.lse = lse;
+  set_head_major(a.q_sb, a.q_sh, a.q_sr, h, n_q, d_k);
+  set_head_major(a.k_sb, a.k_sh, a.k_sr, h, n_k, d_k);
+  set_head_major(a.v_sb, a.v_sh, a.v_sr, h, n_k, d_v);
+  set_head_major(a.o_sb, a.o_sh, a.o_sr, h, n_q, d_v);
+  a.B = B;
+  a.h = h;
+  a.n_q = n_q;
+  a.n_k = n_k;
+  a.scale = scale;
+  fill_mask(a, mask_kind, key_lengths);
+  return launch_status(launch_attn_bf16_d64(a, stream, {}));
+}
+
+size_t sdpa_backward_workspace_bytes(int B, int h, int n_q) {
+  if (B <= 0 || h <= 0 || n_q <= 0) return 0;
+  return round_up((size_t)4 * B * h * n_q);
+}
+
+static int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                    const float* lse, void* dQ, void* dK, void* dV, int B, int h, int n_q, int n_k,
+                    int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lengths,
+                    int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                    Timer* tm) {
+  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV) return MHA_ERR_NULL;
+  int st = check_attn_dims(B, h, n_q, n_k, d_k, d_v);
+  if (st != MHA_OK) return st;
+  if (!(isfinite(scale) && scale > 0.f)) return MHA_ERR_SCALE;
+  st = check_mask(mask_kind, B, n_q, n_k, key_lengths);
+  if (st != MHA_OK) return st;
+  if (dtype != MHA_DTYPE_BF16) return MHA_ERR_UNSUPPORTED;
+  const void* p16[] = {Q, K, V, O, dO, dQ, dK, dV};
+  for (const void* p : p16)
+    if (!aligned16(p)) return MHA_ERR_UNSUPPORTED;
+  if ((uintptr_t)lse & 3u) return MHA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0 ||
+      workspace_bytes < round_up((size_t)4 * B * h * n_q))
+    return MHA_ERR_WORKSPACE;
+  BwdArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  a.dO = dO;
+  a.lse = lse;
+  a.dQ = dQ;
+  a.dK = dK;
+  a.dV = dV;
+  a.Dw = (float*)workspace;
+  a.B = B;
+  a.h = h;
+  a.n_q = n_q;
+  a.n_k = n_k;
+  a.scale = scale;
+  a.causal = (mask_kind & MHA_MASK_CAUSAL) ? 1 : 0;
+  a.padded = (mask_kind & MHA_MASK_KEY_PADDING) ? 1 : 0;
+  if (a.padded)
+    for (int b = 0; b < B; ++b) a.key_len[b] = key_lengths[b];
+  st = launch_status(launch_attn_bwd_dq(a, stream, next_events(tm)));
+  if (st != MHA_OK) return st;
+  return launch_status(launch_attn_bwd_dkdv(a, stream, next_events(tm)));
+}
+
+int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                  const float* lse, void* dQ, void* dK, void* dV, int B, int h, int n_q, int n_k,
+                  int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lengths,
+                  int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(Q, K, V, O, dO, lse, dQ, dK, dV, B, h, n_q, n_k, d_k, d_v, scale, mask_kind,
+                  key_lengths, dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int sdpa_backward_timed(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* lse, void* dQ, void* dK, void* dV, int B,
+                        int h, int n_q, int n_k, int d_k, int d_v, float scale, int mask_kind,
+                        const int32_t* key_lengths, int dtype, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream, hipEvent_t* events,
+                        int capacity, int* n_launches) {
+  if (events == nullptr || capacity < 4) return MHA_ERR_EVENTS;
+  for (int i = 0; i < 4; ++i)
+    if (events[i] == nullptr) return MHA_ERR_EVENTS;
+  Timer tm{events, capacity, 0};
+  const int st = bwd_impl(Q, K, V, O, dO, lse, dQ, dK, dV, B, h, n_q, n_k, d_k, d_v, scale,
+                          mask_kind, key_lengths, dtype, workspace, workspace_bytes, stream, &tm);
+  if (n_launches) *n_launches = tm.used;
+  return st;
+}
+
 }  // extern "C"

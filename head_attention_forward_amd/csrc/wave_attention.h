@@ -222,6 +222,13 @@ struct WaveAttention {
   // 1 / (row sum of weights); a cross-lane exchange: call with all lanes active.
   __device__ __forceinline__ float inv_sum() const { return 1.f / sum_halves(l); }
 
+  // Natural log of the row's sum of exp(scale * s) over its visible keys,
+  // from inv = inv_sum(): the weights are exp(scale (s - m)), so the sum is
+  // exp(scale m) / inv.
+  __device__ __forceinline__ float row_lse(float inv) const {
+    return (m * c2 - __builtin_amdgcn_logf(inv)) * 0.6931471805599453f;
+  }
+
   // O row of this lane's query = acc * inv, rounded to bf16 (lane g writes d
   // 8i + 4g .. +3 of both 32-wide halves).
   __device__ __forceinline__ void store(__bf16* orow, float inv) const {

@@ -28,6 +28,9 @@ W1 has variance 1/d_model, W2 1/d_ff; biases and LayerNorm shifts are
 0.1 * N(0, 1), LayerNorm scales 1 + 0.1 * N(0, 1) (non-trivial values, so
 that every term of the layer shows in its output).
 
+Backward pass (kind "bwd"): Q, K, V as bare attention, then the upstream
+gradient dO ~ N(0, 1), then key lengths.
+
 Input embedding (kind "embed"): token ids uniform over the vocabulary, drawn
 first, then the table E [vocab][d_model] with variance 1/d_model (so that
 E * sqrt(d_model) has unit variance, the scale of the encoding); positions
@@ -100,6 +103,12 @@ WORKLOADS = {
         "long_causal_sdpa", "sdpa", "bf16", B=4, n_q=4096, n_k=4096, h=16, d_k=64, d_v=64,
         mask=MASK_CAUSAL,
         description="bare causal attention, bf16, B=4 h=16 n=4096 d=64"),
+    # Training's backward pass over the long causal shape: gradients of the
+    # attention for an upstream gradient dO ~ N(0, 1).
+    "long_causal_sdpa_bwd": Workload(
+        "long_causal_sdpa_bwd", "bwd", "bf16", B=4, n_q=4096, n_k=4096, h=16, d_k=64, d_v=64,
+        mask=MASK_CAUSAL,
+        description="attention backward (dQ, dK, dV), bf16, B=4 h=16 n=4096 d=64, causal"),
     # One generation step of incremental decoding: each sequence's newest
     # query against its cached keys and values (cache capacity 4096, current
     # lengths in [1024, 4096]); the pages give no decoding shapes, these are
@@ -143,6 +152,7 @@ def generate(w: Workload, seed: int = 0):
 
     sdpa: Q [B][h][n_q][d_k], K [B][h][n_k][d_k], V [B][h][n_k][d_v], scale,
           key_lengths (int32 [B] or None).
+    bwd:  as sdpa, then the upstream gradient dO [B][h][n_q][d_v].
     mha:  X_q [B][n_q][d_model], X_kv (the same tensor object for
           self-attention), Wq/Wk [d_model][h*d_k], Wv [d_model][h*d_v],
           Wo [h*d_v][d_model], key_lengths.
@@ -155,11 +165,13 @@ def generate(w: Workload, seed: int = 0):
     g.manual_seed(seed)
     dt = w.torch_dtype
     out = {}
-    if w.kind == "sdpa":
+    if w.kind in ("sdpa", "bwd"):
         out["Q"] = _normal(g, (w.B, w.h, w.n_q, w.d_k), 1.0, dt)
         out["K"] = _normal(g, (w.B, w.h, w.n_k, w.d_k), 1.0, dt)
         out["V"] = _normal(g, (w.B, w.h, w.n_k, w.d_v), 1.0, dt)
         out["scale"] = 1.0 / math.sqrt(w.d_k)
+        if w.kind == "bwd":
+            out["dO"] = _normal(g, (w.B, w.h, w.n_q, w.d_v), 1.0, dt)
     elif w.kind == "embed":
         out["tokens"] = torch.randint(0, w.vocab, (w.B, w.n_q), generator=g, dtype=torch.int32)
         out["E"] = _normal(g, (w.vocab, w.d_model), 1.0 / math.sqrt(w.d_model), dt)

@@ -229,6 +229,71 @@ int mha_forward_launches(int n_q, int n_k, int d_model, int self_attention);
 
 /*
  * ---------------------------------------------------------------------------
+ * Training: the forward with its row log-sum-exp, and the backward pass.
+ * ---------------------------------------------------------------------------
+ */
+
+/*
+ * sdpa_forward_lse -- sdpa_forward (bf16 only) that also writes, for every
+ * query row, the log-sum-exp the backward pass recomputes the weights from:
+ *   lse[(b*h + head)*n_q + i] = ln( sum over visible keys j of
+ *                                   exp(scale * q_i . k_j) )
+ * so that softmax weight P_ij = exp(scale * q_i . k_j - lse_i).
+ *   lse  DEVICE float [B][h][n_q], 4-byte aligned, caller-owned.
+ * Other arguments, results and errors as sdpa_forward (O is bit-identical).
+ * The sum is the one the forward normalises by (its weights rounded to bf16
+ * as they enter the second product).
+ */
+int sdpa_forward_lse(const void* Q, const void* K, const void* V, void* O, float* lse,
+                     int B, int h, int n_q, int n_k, int d_k, int d_v,
+                     float scale, int mask_kind, const int32_t* key_lengths,
+                     int dtype, hipStream_t stream);
+
+/*
+ * sdpa_backward_workspace_bytes -- scratch of sdpa_backward: the fp32 row
+ * terms D_i = sum_d dO_id O_id, [B][h][n_q], 256-byte rounded.  0 for
+ * invalid sizes.
+ */
+size_t sdpa_backward_workspace_bytes(int B, int h, int n_q);
+
+/*
+ * sdpa_backward -- gradients of O = softmax(Q K^T * scale + M) V:
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - rowsum(dO * O)),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q,   P = exp(S - lse)
+ * The gradient of the forward's definition (devpress.csdn.net
+ * "【深度学习】Transformer", section 2.1, equation (2.4)) through its steps in
+ * reverse order; training back-propagates the losses of all positions at
+ * once (hex4c59.cc "读懂 Attention Is All You Need", sections "训练能并行，
+ * 不意味着一次生成整句话" and "参数是怎样学出来的？").
+ *
+ *   Q, K, V, O  the forward's inputs and output; lse from sdpa_forward_lse
+ *   dO          upstream gradient [B][h][n_q][d_v]
+ *   dQ, dK, dV  outputs, shaped as Q, K, V; must not overlap any input.
+ *               Keys no query can see get zero dK and dV.
+ *   scale, mask_kind, key_lengths  as the forward (they must be the same)
+ *   workspace   >= sdpa_backward_workspace_bytes(B, h, n_q), 256-byte aligned
+ *   dtype       MHA_DTYPE_BF16 (d_k = d_v = 64), fp32 accumulation; P and
+ *               dS are rounded to bf16 as they enter the accumulating
+ *               products.
+ * Two launches, no atomics (results are deterministic): one kernel per
+ * 128-query block computes dQ and D; one per 128-key block computes dK, dV.
+ */
+int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                  const float* lse, void* dQ, void* dK, void* dV,
+                  int B, int h, int n_q, int n_k, int d_k, int d_v,
+                  float scale, int mask_kind, const int32_t* key_lengths, int dtype,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* sdpa_backward with launch events (2 launches), as the other _timed variants. */
+int sdpa_backward_timed(const void* Q, const void* K, const void* V, const void* O,
+                        const void* dO, const float* lse, void* dQ, void* dK, void* dV,
+                        int B, int h, int n_q, int n_k, int d_k, int d_v,
+                        float scale, int mask_kind, const int32_t* key_lengths, int dtype,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream,
+                        hipEvent_t* events, int capacity, int* n_launches);
+
+/*
+ * ---------------------------------------------------------------------------
  * The rest of an encoder layer around the attention block: residual +
  * LayerNorm (Post-LN) and the position-wise feed-forward network.  These
  * entry points DO take biases and per-feature scale/shift vectors, because

@@ -1,0 +1,144 @@
+"""GPU parity of the training entry points: sdpa_forward_lse (the forward
+with its row log-sum-exp) and sdpa_backward (dQ, dK, dV) against the fp64
+oracle, through the C ABI.
+
+Tolerances.  lse: the forward normalises by the sum of its weights rounded
+to bf16 (relative error of each weight <= u = 2^-8, of the sum at most the
+same), so |lse - exact| <= u + 1e-6 (ln(1 + u) < u).  Gradients: inputs and
+outputs bf16, fp32 accumulation, and one bf16 rounding of P (dV) or dS
+(dQ, dK) as it enters the accumulating product, plus the output rounding:
+each gradient within relative L2 error 2u = 7.8e-3 of the exact one, and
+every element within 4u * max(max|exact|, 1) of it (elements of a gradient
+are sums of terms of both signs, so the bar is set on the tensor's scale,
+at least the unit scale of the inputs).
+
+Each GPU step prints the case it runs (flushed) before launching it."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import head_attention_forward_amd as hafa
+from head_attention_forward_amd.workloads import to_f64
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -8
+
+
+def announce(*what):
+    print("[gpu case]", *what, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a ROCm GPU")
+    return torch.device("cuda")
+
+
+def inputs(B, h, n_q, n_k, seed):
+    g = torch.Generator("cpu")
+    g.manual_seed(seed)
+    mk = lambda n: torch.randn((B, h, n, 64), generator=g).to(torch.bfloat16)  # noqa: E731
+    return mk(n_q), mk(n_k), mk(n_k), mk(n_q)
+
+
+def check_grad(got, want, what):
+    """A gradient that is exactly zero (one visible key: the softmax is
+    constant) is held to the elementwise bar on the inputs' unit scale."""
+    g = to_f64(got)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite"
+    err = np.abs(g - want)
+    scale = max(float(np.abs(want).max()), 1.0)
+    worst = float(err.max()) / (4 * U * scale)
+    norm = float(np.linalg.norm(want))
+    rel = float(np.linalg.norm(g - want) / norm) if norm > 0 else 0.0
+    print(f"  {what}: rel_l2={rel:.2e} max_abs={float(err.max()):.2e} "
+          f"(max|want| {float(np.abs(want).max()):.2e}, worst/bound {worst:.3f})", flush=True)
+    assert rel <= 2 * U, f"{what}: rel-L2 {rel}"
+    assert worst <= 1.0, f"{what}: max-abs {float(err.max())}"
+
+
+CASES = [
+    # B, h, n_q, n_k, mask, key_lengths, label
+    (2, 4, 128, 128, 0, None, "one block each, unmasked"),
+    (2, 2, 256, 256, 1, None, "causal"),
+    (2, 3, 96, 160, 2, [160, 37], "key padding, cross shape"),
+    (3, 2, 100, 77, 0, None, "ragged query and key tiles"),
+    (2, 2, 200, 200, 3, [200, 150], "causal + key padding"),
+    (1, 1, 1, 1, 0, None, "one query, one key"),
+    (1, 2, 1, 300, 0, None, "one query over 300 keys"),
+    (4, 8, 100, 100, 0, None, "the encoder block's heads"),
+]
+
+
+@pytest.mark.parametrize("B,h,n_q,n_k,mask,kl,label", CASES)
+def test_backward(dev, B, h, n_q, n_k, mask, kl, label):
+    Q, K, V, dO = inputs(B, h, n_q, n_k, seed=B * 1000 + n_q + n_k + mask)
+    scale = 1.0 / 8.0
+    announce("backward", B, h, n_q, n_k, mask, kl, label)
+    Qd, Kd, Vd, dOd = (t.to(dev) for t in (Q, K, V, dO))
+    O, lse = hafa.sdpa_forward_lse(Qd, Kd, Vd, scale, mask, kl)
+    dQ, dK, dV = hafa.sdpa_backward(Qd, Kd, Vd, O, dOd, lse, scale, mask, kl)
+    torch.cuda.synchronize()
+    kla = None if kl is None else np.array(kl)
+    args = [to_f64(t) for t in (Q, K, V)]
+    want_lse = oracle.row_logsumexp(args[0], args[1], scale, mask, kla)
+    lerr = float(np.abs(to_f64(lse) - want_lse).max())
+    print(f"  lse max_abs={lerr:.2e}", flush=True)
+    assert lerr <= U + 1e-6
+    # The backward is checked against the oracle's gradients at the GPU's own
+    # forward output (the identity D = rowsum(dO * O) uses O; the oracle's
+    # gradient formula uses P only, so the exact gradients are what is compared).
+    wQ, wK, wV = oracle.sdpa_backward_ref(*args, to_f64(dO), scale, mask, kla)
+    check_grad(dQ, wQ, f"dQ {label}")
+    check_grad(dK, wK, f"dK {label}")
+    check_grad(dV, wV, f"dV {label}")
+    if kl is not None:
+        for b, L in enumerate(kl):
+            assert torch.count_nonzero(dK[b, :, L:]) == 0 and torch.count_nonzero(dV[b, :, L:]) == 0
+
+
+def test_forward_lse_leaves_output_unchanged(dev):
+    Q, K, V, _ = inputs(2, 4, 300, 300, seed=5)
+    Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
+    announce("forward with lse vs plain forward", 2, 4, 300)
+    O1 = hafa.sdpa_forward(Qd, Kd, Vd, 0.125, 1)
+    O2, _ = hafa.sdpa_forward_lse(Qd, Kd, Vd, 0.125, 1)
+    Qs = Qd[:, :, :1].contiguous()
+    # a decode shape (one query over many keys) takes the key-split kernel
+    O3 = hafa.sdpa_forward(Qs, Kd, Vd, 0.125, 0)
+    O4, l4 = hafa.sdpa_forward_lse(Qs, Kd, Vd, 0.125, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(O1, O2) and torch.equal(O3, O4)
+    want = oracle.row_logsumexp(to_f64(Q[:, :, :1]), to_f64(K), 0.125, 0, None)
+    assert float(np.abs(to_f64(l4) - want).max()) <= U + 1e-6
+
+
+def test_backward_deterministic(dev):
+    Q, K, V, dO = inputs(2, 2, 384, 384, seed=7)
+    Qd, Kd, Vd, dOd = (t.to(dev) for t in (Q, K, V, dO))
+    announce("backward determinism", 2, 2, 384)
+    O, lse = hafa.sdpa_forward_lse(Qd, Kd, Vd, 0.125, 1)
+    r1 = hafa.sdpa_backward(Qd, Kd, Vd, O, dOd, lse, 0.125, 1)
+    r2 = hafa.sdpa_backward(Qd, Kd, Vd, O, dOd, lse, 0.125, 1)
+    torch.cuda.synchronize()
+    for a, b in zip(r1, r2):
+        assert torch.equal(a, b)
+
+
+def test_backward_long_causal(dev):
+    """B = 1, h = 2, n = 2048, causal: the whole gradients against the
+    oracle (fp64 over 2 x 2048 x 2048 weights)."""
+    Q, K, V, dO = inputs(1, 2, 2048, 2048, seed=11)
+    Qd, Kd, Vd, dOd = (t.to(dev) for t in (Q, K, V, dO))
+    announce("backward long causal", 1, 2, 2048)
+    O, lse = hafa.sdpa_forward_lse(Qd, Kd, Vd, 0.125, 1)
+    dQ, dK, dV = hafa.sdpa_backward(Qd, Kd, Vd, O, dOd, lse, 0.125, 1)
+    torch.cuda.synchronize()
+    wQ, wK, wV = oracle.sdpa_backward_ref(*(to_f64(t) for t in (Q, K, V, dO)), 0.125, 1, None)
+    check_grad(dQ, wQ, "dQ long causal")
+    check_grad(dK, wK, "dK long causal")
+    check_grad(dV, wV, "dV long causal")
