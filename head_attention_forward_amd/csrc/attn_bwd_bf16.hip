@@ -212,12 +212,17 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(const BwdArgs a) {
             f32x16 dp = score32(Vs[u], kx, 32 * hk, dof);  // dP^T
             bf16x8 wa, wb;
             f32x8 w0, w1;
+            float p[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s[i], c2, -l2));
+            if (k0 + 32 * hk + 32 > lim_min) {  // wave-uniform: a tile on the mask's edge
+#pragma unroll
+              for (int i = 0; i < 16; ++i)
+                if (k0 + 32 * hk + 8 * (i >> 2) + 4 * g + (i & 3) >= lim) p[i] = 0.f;
+            }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const int key = k0 + 32 * hk + 8 * (i >> 2) + 4 * g + (i & 3);
-              float p = fast_exp2(fmaf(s[i], c2, -l2));
-              if (k0 + 32 * hk + 32 > lim_min && key >= lim) p = 0.f;
-              const float ds = p * (dp[i] - Dq);
+              const float ds = p[i] * (dp[i] - Dq);
               if (i < 8) w0[i] = ds;
               else w1[i - 8] = ds;
             }
@@ -312,6 +317,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(const BwdArgs a)
         const int q0 = t * BT;
         // the tile's last query sees some key of this wave (causal), or no causal mask
         if (wave_live && (!a.causal || q0 + BT - 1 >= kw0)) {
+          // every (query, key) pair of the tile and the wave visible: no per-element test
+          const bool full = kw0 + 32 <= L && q0 + BT <= a.n_q && (!a.causal || q0 >= kw0 + 31);
 #pragma unroll
           for (int hq = 0; hq < 2; ++hq) {
             f32x16 s = score32(Qs[u], qx, 32 * hq, kf);    // S: rows queries, lane = key
@@ -326,7 +333,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(const BwdArgs a)
               for (int r = 0; r < 4; ++r) {
                 const int i = 4 * i4 + r;
                 const int q = q0 + qr + r;
-                const bool vis = my_k < L && q < a.n_q && (!a.causal || my_k <= q);
+                const bool vis = full || (my_k < L && q < a.n_q && (!a.causal || my_k <= q));
                 const float p = vis ? fast_exp2(fmaf(s[i], c2, -l4[r] * kLog2e)) : 0.f;
                 const float ds = p * (dp[i] - d4[r]);
                 if (i < 8) {
