@@ -12,7 +12,11 @@
 // "训练能并行，不意味着一次生成整句话" and "参数是怎样学出来的？").  P is not
 // stored by the forward: it is recomputed from S and the row log-sum-exp
 // the forward saved, P = exp(S - lse), one exponential per entry, no row
-// reductions.
+// reductions.  The per-row constants enter the score products as their
+// initial accumulators (fp32, exact): the raw-score product starts at
+// -lse/scale, so it yields (S - lse)/scale and P = exp2(acc * scale log2 e);
+// the dP product starts at -D, so it yields dP - D and dS = P * acc.  The dQ
+// kernel writes both row constants, -lse/scale and -D, to the workspace.
 //
 // Two kernels, deterministic (no atomics):
 //   attn_bwd_dq_kernel    workgroup = 128 queries of one (batch, head), wave
@@ -82,10 +86,11 @@ __device__ __forceinline__ void load_row_operand(const __bf16* row, int g, bf16x
   for (int s = 0; s < 4; ++s) f[s] = ((const bf16x8*)row)[2 * s + g];
 }
 
-// 32 x 32 score-shaped product over d = 64: rows from an LDS tile in the
-// k_off layout (row offsets rx), columns from the lane's own operand f.
-__device__ __forceinline__ f32x16 score32(const __bf16* t, const int rx[4], int row0, const bf16x8 f[4]) {
-  f32x16 s = {};
+// 32 x 32 score-shaped product over d = 64 added to the accumulator init:
+// rows from an LDS tile in the k_off layout (row offsets rx), columns from
+// the lane's own operand f.
+__device__ __forceinline__ f32x16 score32(const __bf16* t, const int rx[4], int row0, const bf16x8 f[4],
+                                          f32x16 s) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
     const bf16x8 a = *(const bf16x8*)&t[rx[kk] + row0 * D];
@@ -169,9 +174,18 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(const BwdArgs a) {
     }
   }
   const float Dq = sum_halves(dpart);
-  if (g == 0 && my_q < a.n_q) a.Dw[(int64_t)bh * a.n_q + my_q] = Dq;
-  const float l2 = a.lse[(int64_t)bh * a.n_q + qc] * kLog2e;
+  const float ls = -a.lse[(int64_t)bh * a.n_q + qc] / a.scale;  // -lse / scale
+  if (g == 0 && my_q < a.n_q) {
+    a.Dw[(int64_t)bh * a.n_q + my_q] = -Dq;
+    a.Lw[(int64_t)bh * a.n_q + my_q] = ls;
+  }
   const float c2 = a.scale * kLog2e;
+  f32x16 s_init, dp_init;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    s_init[i] = ls;
+    dp_init[i] = -Dq;
+  }
 
   int kx[4], vx[2];
 #pragma unroll
@@ -208,13 +222,13 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(const BwdArgs a) {
         if (k0 < wv_keys) {
 #pragma unroll
           for (int hk = 0; hk < 2; ++hk) {
-            f32x16 s = score32(Ks[u], kx, 32 * hk, qf);   // S^T: rows keys, lane = query
-            f32x16 dp = score32(Vs[u], kx, 32 * hk, dof);  // dP^T
+            const f32x16 s = score32(Ks[u], kx, 32 * hk, qf, s_init);     // (S^T - lse) / scale
+            const f32x16 dp = score32(Vs[u], kx, 32 * hk, dof, dp_init);  // dP^T - D
             bf16x8 wa, wb;
             f32x8 w0, w1;
             float p[16];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) p[i] = fast_exp2(fmaf(s[i], c2, -l2));
+            for (int i = 0; i < 16; ++i) p[i] = fast_exp2(s[i] * c2);
             if (k0 + 32 * hk + 32 > lim_min) {  // wave-uniform: a tile on the mask's edge
 #pragma unroll
               for (int i = 0; i < 16; ++i)
@@ -222,7 +236,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(const BwdArgs a) {
             }
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-              const float ds = p[i] * (dp[i] - Dq);
+              const float ds = p[i] * dp[i];
               if (i < 8) w0[i] = ds;
               else w1[i - 8] = ds;
             }
@@ -245,8 +259,8 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(const BwdArgs a)
   __shared__ __attribute__((aligned(1024))) __bf16 Qt[2][BT * D];   // Q, v_off (dS^T Q)
   __shared__ __attribute__((aligned(1024))) __bf16 Os[2][BT * D];   // dO, k_off (dP rows)
   __shared__ __attribute__((aligned(1024))) __bf16 Ot[2][BT * D];   // dO, v_off (P^T dO)
-  __shared__ __attribute__((aligned(256))) float Ls[2][BT];          // lse * log2(e)
-  __shared__ __attribute__((aligned(256))) float Ds[2][BT];          // D
+  __shared__ __attribute__((aligned(256))) float Ls[2][BT];          // -lse / scale
+  __shared__ __attribute__((aligned(256))) float Ds[2][BT];          // -D
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -283,7 +297,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(const BwdArgs a)
   const unsigned qs_lds = lds_addr(&Qs[0][0]), qt_lds = lds_addr(&Qt[0][0]);
   const unsigned os_lds = lds_addr(&Os[0][0]), ot_lds = lds_addr(&Ot[0][0]);
   const unsigned ls_lds = lds_addr(&Ls[0][0]), ds_lds = lds_addr(&Ds[0][0]);
-  const char* Lp = wave_uniform((const char*)(a.lse + (int64_t)bh * a.n_q));
+  const char* Lp = wave_uniform((const char*)(a.Lw + (int64_t)bh * a.n_q));
   const char* Dp = wave_uniform((const char*)(a.Dw + (int64_t)bh * a.n_q));
   auto issue = [&](int tile, int buf) {
     const int q0 = tile * BT;
@@ -298,7 +312,7 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(const BwdArgs a)
       dma16_s(dOp, (unsigned)(q * D + kc) * 2u, os_lds + dst);
       dma16_s(dOp, (unsigned)(q * D + vc) * 2u, ot_lds + dst);
     }
-    // lse and D of the tile's 64 queries: one 4-byte copy per lane
+    // -lse/scale and -D of the tile's 64 queries: one 4-byte copy per lane
     const unsigned qo = (unsigned)min(q0 + lane, a.n_q - 1) * 4u;
     if (wave == 0) dma4_s(Lp, qo, ls_lds + (unsigned)(buf * BT * 4));
     if (wave == 1) dma4_s(Dp, qo, ds_lds + (unsigned)(buf * BT * 4));
@@ -321,29 +335,38 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(const BwdArgs a)
           const bool full = kw0 + 32 <= L && q0 + BT <= a.n_q && (!a.causal || q0 >= kw0 + 31);
 #pragma unroll
           for (int hq = 0; hq < 2; ++hq) {
-            f32x16 s = score32(Qs[u], qx, 32 * hq, kf);    // S: rows queries, lane = key
-            f32x16 dp = score32(Os[u], qx, 32 * hq, vf);   // dP
-            f32x8 p0, p1, w0, w1;
+            // element 4 i4 + r of a lane is query row 32 hq + 8 i4 + 4 g + r of the tile
+            f32x16 s_init, dp_init;
 #pragma unroll
             for (int i4 = 0; i4 < 4; ++i4) {
-              const int qr = 32 * hq + 8 * i4 + 4 * g;  // tile row of elements 4 i4 .. +3
+              const int qr = 32 * hq + 8 * i4 + 4 * g;
               const f32x4 l4 = *(const f32x4*)&Ls[u][qr];
               const f32x4 d4 = *(const f32x4*)&Ds[u][qr];
 #pragma unroll
               for (int r = 0; r < 4; ++r) {
-                const int i = 4 * i4 + r;
-                const int q = q0 + qr + r;
-                const bool vis = full || (my_k < L && q < a.n_q && (!a.causal || my_k <= q));
-                const float p = vis ? fast_exp2(fmaf(s[i], c2, -l4[r] * kLog2e)) : 0.f;
-                const float ds = p * (dp[i] - d4[r]);
-                if (i < 8) {
-                  p0[i] = p;
-                  w0[i] = ds;
-                } else {
-                  p1[i - 8] = p;
-                  w1[i - 8] = ds;
-                }
+                s_init[4 * i4 + r] = l4[r];
+                dp_init[4 * i4 + r] = d4[r];
               }
+            }
+            const f32x16 s = score32(Qs[u], qx, 32 * hq, kf, s_init);    // (S - lse) / scale
+            const f32x16 dp = score32(Os[u], qx, 32 * hq, vf, dp_init);  // dP - D
+            float p[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) p[i] = fast_exp2(s[i] * c2);
+            if (!full) {  // wave-uniform: a tile on the mask's edge
+#pragma unroll
+              for (int i = 0; i < 16; ++i) {
+                const int q = q0 + 32 * hq + 8 * (i >> 2) + 4 * g + (i & 3);
+                if (!(my_k < L && q < a.n_q && (!a.causal || my_k <= q))) p[i] = 0.f;
+              }
+            }
+            f32x8 p0, p1, w0, w1;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+              p0[i] = p[i];
+              p1[i] = p[8 + i];
+              w0[i] = p[i] * dp[i];
+              w1[i] = p[8 + i] * dp[8 + i];
             }
             const bf16x8 pa = __builtin_convertvector(p0, bf16x8), pb = __builtin_convertvector(p1, bf16x8);
             const bf16x8 wa = __builtin_convertvector(w0, bf16x8), wb = __builtin_convertvector(w1, bf16x8);

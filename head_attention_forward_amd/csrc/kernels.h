@@ -32,8 +32,8 @@ struct AttnArgs {
 
 // Attention backward: dQ, dK, dV of O = softmax(Q K^T * scale + M) V from
 // the upstream gradient dO and the forward's row log-sum-exp.  Every tensor
-// is head-major [B][h][n][64] bf16; Dw is fp32 workspace [B][h][n_q] that
-// receives rowsum(dO * O).
+// is head-major [B][h][n][64] bf16; Dw and Lw are fp32 workspace [B][h][n_q]
+// that receive -rowsum(dO * O) and -lse / scale.
 struct BwdArgs {
   const void* Q;
   const void* K;
@@ -45,6 +45,7 @@ struct BwdArgs {
   void* dK;
   void* dV;
   float* Dw;
+  float* Lw;
   int B, h, n_q, n_k;
   float scale;
   int causal;

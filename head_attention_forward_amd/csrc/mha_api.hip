@@ -660,7 +660,7 @@ int sdpa_forward_lse(const void* Q, const void* K, const void* V, void* O, float
 
 size_t sdpa_backward_workspace_bytes(int B, int h, int n_q) {
   if (B <= 0 || h <= 0 || n_q <= 0) return 0;
-  return round_up((size_t)4 * B * h * n_q);
+  return 2 * round_up((size_t)4 * B * h * n_q);
 }
 
 static int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -679,8 +679,9 @@ static int bwd_impl(const void* Q, const void* K, const void* V, const void* O, 
   for (const void* p : p16)
     if (!aligned16(p)) return MHA_ERR_UNSUPPORTED;
   if ((uintptr_t)lse & 3u) return MHA_ERR_UNSUPPORTED;
+  const size_t row_terms = round_up((size_t)4 * B * h * n_q);
   if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0 ||
-      workspace_bytes < round_up((size_t)4 * B * h * n_q))
+      workspace_bytes < 2 * row_terms)
     return MHA_ERR_WORKSPACE;
   BwdArgs a;
   memset(&a, 0, sizeof(a));
@@ -694,6 +695,7 @@ static int bwd_impl(const void* Q, const void* K, const void* V, const void* O, 
   a.dK = dK;
   a.dV = dV;
   a.Dw = (float*)workspace;
+  a.Lw = (float*)((char*)workspace + row_terms);
   a.B = B;
   a.h = h;
   a.n_q = n_q;

@@ -250,9 +250,9 @@ int sdpa_forward_lse(const void* Q, const void* K, const void* V, void* O, float
                      int dtype, hipStream_t stream);
 
 /*
- * sdpa_backward_workspace_bytes -- scratch of sdpa_backward: the fp32 row
- * terms D_i = sum_d dO_id O_id, [B][h][n_q], 256-byte rounded.  0 for
- * invalid sizes.
+ * sdpa_backward_workspace_bytes -- scratch of sdpa_backward: two fp32 row
+ * arrays [B][h][n_q], each 256-byte rounded: -D_i (D_i = sum_d dO_id O_id)
+ * and -lse_i / scale.  0 for invalid sizes.
  */
 size_t sdpa_backward_workspace_bytes(int B, int h, int n_q);
 

@@ -296,12 +296,12 @@ def test_embed_positional_rejections(L):
 
 
 def test_backward_rejections(L):
-    assert L.sdpa_backward_workspace_bytes(2, 3, 5) == 256
-    assert L.sdpa_backward_workspace_bytes(4, 16, 4096) == 4 * 4 * 16 * 4096
+    assert L.sdpa_backward_workspace_bytes(2, 3, 5) == 512
+    assert L.sdpa_backward_workspace_bytes(4, 16, 4096) == 2 * 4 * 4 * 16 * 4096
     assert L.sdpa_backward_workspace_bytes(0, 3, 5) == 0
 
     def bwd(Q=FAKE, lse=FAKE, dQ=FAKE2, B=2, h=2, n_q=8, n_k=8, d=64, scale=0.125, mask=0, kl=None,
-            dtype=BF16, ws=FAKE, ws_bytes=4096):
+            dtype=BF16, ws=FAKE, ws_bytes=8192):
         return L.sdpa_backward(Q, FAKE, FAKE, FAKE, FAKE, lse, dQ, FAKE2, FAKE2, B, h, n_q, n_k, d, d,
                                scale, mask, kl, dtype, ws, ws_bytes, None)
     assert bwd(Q=None) == NULL
@@ -315,7 +315,7 @@ def test_backward_rejections(L):
     assert bwd(dQ=MISALIGNED) == UNSUP
     assert bwd(lse=ctypes.c_void_p(0x10002)) == UNSUP
     assert bwd(ws=None) == WS
-    assert bwd(ws_bytes=100) == WS
+    assert bwd(ws_bytes=300) == WS
     assert L.sdpa_forward_lse(FAKE, FAKE, FAKE, FAKE2, None, 2, 2, 8, 8, 64, 64, 0.125, 0, None, BF16,
                               None) == NULL
     assert L.sdpa_forward_lse(FAKE, FAKE, FAKE, FAKE2, FAKE, 2, 2, 8, 8, 64, 64, 0.125, 0, None, F32,
