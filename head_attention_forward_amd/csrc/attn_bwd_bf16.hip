@@ -124,7 +124,10 @@ __device__ __forceinline__ void swz(int q, int& row, int& kc, int& vc) {
 
 // ---------------------------------------------------------------------- dQ
 
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(const BwdArgs a) {
+// Three waves per SIMD (48 KB of LDS: three workgroups per compute unit):
+// at most 168 registers per lane, accumulators included.
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(3, 3)))
+void attn_bwd_dq_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 Ks[2][BT * D];  // K, k_off (score rows)
   __shared__ __attribute__((aligned(1024))) __bf16 Kt[2][BT * D];  // K, v_off (dS K)
   __shared__ __attribute__((aligned(1024))) __bf16 Vs[2][BT * D];  // V, k_off (dP rows)
@@ -254,7 +257,10 @@ __global__ __launch_bounds__(NW * 64) void attn_bwd_dq_kernel(const BwdArgs a) {
 
 // ---------------------------------------------------------------- dK and dV
 
-__global__ __launch_bounds__(NW * 64) void attn_bwd_dkdv_kernel(const BwdArgs a) {
+// Two waves per SIMD (65 KB of LDS: two workgroups per compute unit): at
+// most 256 registers per lane, accumulators included.
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_bwd_dkdv_kernel(const BwdArgs a) {
   __shared__ __attribute__((aligned(1024))) __bf16 Qs[2][BT * D];   // Q, k_off (score rows)
   __shared__ __attribute__((aligned(1024))) __bf16 Qt[2][BT * D];   // Q, v_off (dS^T Q)
   __shared__ __attribute__((aligned(1024))) __bf16 Os[2][BT * D];   // dO, k_off (dP rows)
