@@ -16,7 +16,8 @@ Two independent formulations are provided:
   position-wise feed-forward network of an encoder layer;
   ``oracle.embedding`` -- the scaled token embedding plus the sinusoidal
   positional encoding;
-  ``oracle.backward`` -- the gradients of attention (dQ, dK, dV) and the row
+  ``oracle.backward`` -- the gradients of attention (dQ, dK, dV), of the
+  multi-head block (inputs and the four projection weights) and the row
   log-sum-exp a forward pass saves for them.
 * ``oracle.bruteforce`` -- pure-Python loops with ``math.exp``/``math.fsum``,
   one query row at a time, for tiny inputs; it cross-checks the matrix form.
@@ -77,6 +78,6 @@ from .bruteforce import (  # noqa: F401
     layer_norm_bruteforce,
     mha_bruteforce,
 )
-from .backward import row_logsumexp, sdpa_backward_ref  # noqa: F401
+from .backward import mha_backward_ref, row_logsumexp, sdpa_backward_ref  # noqa: F401
 from .embedding import embed_positional_ref, positional_encoding  # noqa: F401
 from .layer import add_layer_norm, encoder_layer_ref, ffn, layer_norm  # noqa: F401

@@ -63,3 +63,38 @@ def sdpa_backward_ref(Q, K, V, dO, scale, mask_kind=0, key_lengths=None):
     dQ = scale * (dS @ K)
     dK = scale * (np.swapaxes(dS, -1, -2) @ Q)
     return dQ, dK, dV
+
+
+def mha_backward_ref(X_q, X_kv, Wq, Wk, Wv, Wo, h, dY, mask_kind=0, key_lengths=None):
+    """Gradients of the multi-head block Y = Concat(head_1..head_h) W^O,
+    head_i = Attention(X_q W_i^Q, X_kv W_i^K, X_kv W_i^V) (devpress.csdn.net
+    section 2.2), for the upstream gradient dY [B][n_q][d_model], taken
+    through the block's steps in reverse:
+
+        Y = C W^O            ->  dC = dY W^O^T,   dW^O = sum over rows C^T dY
+        C = concat(heads)    ->  dO = split(dC)
+        O = attention        ->  dQ, dK, dV (sdpa_backward_ref)
+        Q = X_q W^Q, ...     ->  dW^Q = X_q^T dQ_c,  dX_q = dQ_c W^Q^T
+                                 dX_kv = dK_c W^K^T + dV_c W^V^T, ...
+
+    (_c: heads concatenated back into [rows][h*d]).  Returns dX_q, dX_kv,
+    dWq, dWk, dWv, dWo; for self-attention (X_kv the same array as X_q) the
+    gradient with respect to the shared input is dX_q + dX_kv.
+    Parity: pinned by finite differences of sum(dY * Y)."""
+    from .attention import concat_heads, mha_ref, split_heads
+    X_q, X_kv, Wq, Wk, Wv, Wo, dY = (_f64(t) for t in (X_q, X_kv, Wq, Wk, Wv, Wo, dY))
+    _, it = mha_ref(X_q, X_kv, Wq, Wk, Wv, Wo, h, mask_kind, key_lengths, return_intermediates=True)
+    d_k = Wq.shape[1] // h
+    C = it["concat"]
+    dWo = np.einsum("bni,bnj->ij", C, dY)
+    dC = dY @ Wo.T
+    dO = split_heads(dC, h)
+    dQ, dK, dV = sdpa_backward_ref(it["Q"], it["K"], it["V"], dO, 1.0 / np.sqrt(d_k), mask_kind,
+                                   key_lengths)
+    dQc, dKc, dVc = concat_heads(dQ), concat_heads(dK), concat_heads(dV)
+    dWq = np.einsum("bni,bnj->ij", X_q, dQc)
+    dWk = np.einsum("bni,bnj->ij", X_kv, dKc)
+    dWv = np.einsum("bni,bnj->ij", X_kv, dVc)
+    dX_q = dQc @ Wq.T
+    dX_kv = dKc @ Wk.T + dVc @ Wv.T
+    return dX_q, dX_kv, dWq, dWk, dWv, dWo

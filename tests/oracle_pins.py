@@ -809,8 +809,52 @@ def check_row_logsumexp(impl):
                     assert abs(lse[b, hh, i] - want) <= 1e-13
 
 
+def check_mha_bwd_finite_differences(impl):
+    """Block gradients against central differences of sum(dY * Y), cross-
+    attention with padding and self-attention with the causal mask (there the
+    shared input's gradient is dX_q + dX_kv), every element of every input
+    and weight.  The forward is the oracle's mha_ref, pinned on its own."""
+    import oracle
+    r = _rng(49)
+    for self_attn, kind, kl in ((False, PAD, np.array([3, 2])), (True, CAUSAL, None)):
+        B, n_q, n_k, dm, h, d = 2, 3, (3 if self_attn else 4), 4, 2, 2
+        X_q = r.standard_normal((B, n_q, dm))
+        X_kv = X_q if self_attn else r.standard_normal((B, n_k, dm))
+        W = [r.standard_normal((dm, h * d)) for _ in range(3)] + [r.standard_normal((h * d, dm))]
+        dY = r.standard_normal((B, n_q, dm))
+        got = impl.mha_backward_ref(X_q, X_kv, *W, h, dY, kind, kl)
+        dX_want = got[0] + got[1] if self_attn else None
+
+        def loss(Xq, Xkv, Ws):
+            return float((dY * oracle.mha_ref(Xq, Xkv, *Ws, h, kind, kl)).sum())
+
+        def fd(arr, setter):
+            g = np.zeros_like(arr)
+            it = np.nditer(arr, flags=["multi_index"])
+            for _ in it:
+                vals = []
+                for sgn in (1.0, -1.0):
+                    a2 = arr.copy()
+                    a2[it.multi_index] += sgn * 1e-5
+                    vals.append(setter(a2))
+                g[it.multi_index] = (vals[0] - vals[1]) / 2e-5
+            return g
+        if self_attn:
+            assert np.abs(fd(X_q, lambda a: loss(a, a, W)) - dX_want).max() <= 1e-7
+        else:
+            assert np.abs(fd(X_q, lambda a: loss(a, X_kv, W)) - got[0]).max() <= 1e-7
+            assert np.abs(fd(X_kv, lambda a: loss(X_q, a, W)) - got[1]).max() <= 1e-7
+        for j in range(4):
+            def set_w(a, j=j):
+                W2 = list(W)
+                W2[j] = a
+                return loss(X_q, X_kv, W2)
+            assert np.abs(fd(W[j], set_w) - got[2 + j]).max() <= 1e-7, (self_attn, j)
+
+
 ALL_BWD_CHECKS = [
     check_bwd_finite_differences,
+    check_mha_bwd_finite_differences,
     check_bwd_invariants,
     check_bwd_uniform_weights,
     check_row_logsumexp,

@@ -309,12 +309,27 @@ def _bwd(variant):
         lse = oracle.row_logsumexp(Q, K, scale, mask_kind, key_lengths)
         return lse / scale if variant == "lse_unscaled" else lse
 
-    return types.SimpleNamespace(sdpa_backward_ref=sdpa_backward_ref, row_logsumexp=row_logsumexp)
+    def mha_backward_ref(X_q, X_kv, Wq, Wk, Wv, Wo, h, dY, mask_kind=0, key_lengths=None):
+        g = list(oracle.mha_backward_ref(X_q, X_kv, Wq, Wk, Wv, Wo, h, dY, mask_kind, key_lengths))
+        if variant == "dwo_transposed" and g[5].shape[0] == g[5].shape[1]:
+            g[5] = g[5].T.copy()
+        if variant == "dx_kv_missing_value_path":
+            from oracle.attention import concat_heads, mha_ref, split_heads
+            _, it = mha_ref(X_q, X_kv, Wq, Wk, Wv, Wo, h, mask_kind, key_lengths, return_intermediates=True)
+            dO = split_heads(dY @ Wo.T, h)
+            d = Wq.shape[1] // h
+            _, dK, _ = oracle.sdpa_backward_ref(it["Q"], it["K"], it["V"], dO, 1.0 / np.sqrt(d), mask_kind,
+                                                key_lengths)
+            g[1] = concat_heads(dK) @ Wk.T
+        return tuple(g)
+
+    return types.SimpleNamespace(sdpa_backward_ref=sdpa_backward_ref, row_logsumexp=row_logsumexp,
+                                 mha_backward_ref=mha_backward_ref)
 
 
 BWD_MUTANTS = {v: (lambda v=v: _bwd(v)) for v in
                ("dv_untransposed", "ds_no_centering", "ds_centered_by_mean", "dq_unscaled",
-                "dk_untransposed", "lse_unscaled")}
+                "dk_untransposed", "lse_unscaled", "dwo_transposed", "dx_kv_missing_value_path")}
 
 
 def _fails_some_bwd_pin(impl):
