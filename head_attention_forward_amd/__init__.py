@@ -16,7 +16,9 @@ from ._binding import (  # noqa: F401
     alloc_workspace,
     lib,
     mha_attend,
+    mha_backward,
     mha_forward,
+    mha_forward_train,
     mha_project_in,
     mha_project_out,
     sdpa_backward,

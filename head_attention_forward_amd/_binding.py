@@ -62,6 +62,14 @@ _SIG = {
     "sdpa_backward": (_I, [_P] * 9 + [_I] * 6 + [ctypes.c_float, _I, _P, _I, _P, ctypes.c_size_t, _P]),
     "sdpa_backward_timed": (_I, [_P] * 9 + [_I] * 6 + [ctypes.c_float, _I, _P, _I, _P,
                                                       ctypes.c_size_t, _P, _P, _I, _P]),
+    "mha_train_workspace_bytes": (ctypes.c_size_t, [_I] * 7),
+    "mha_forward_train": (_I, [_P] * 7 + [_I] * 8 + [_P, _I, _P, ctypes.c_size_t, _P]),
+    "mha_backward_workspace_bytes": (ctypes.c_size_t, [_I] * 9),
+    "mha_backward": (_I, [_P] * 13 + [_I] * 8 + [_P, _I, _P, ctypes.c_size_t, _P, ctypes.c_size_t,
+                                                 _P]),
+    "mha_backward_timed": (_I, [_P] * 13 + [_I] * 8 + [_P, _I, _P, ctypes.c_size_t, _P,
+                                                       ctypes.c_size_t, _P, _P, _I, _P]),
+    "mha_backward_launches": (_I, [_I]),
 }
 
 _lib = None
@@ -400,3 +408,44 @@ def sdpa_backward(Q, K, V, O, dO, lse, scale=None, mask_kind=0, key_lengths=None
                              workspace.numel() * workspace.element_size(), _stream(stream))
     _check("sdpa_backward", st)
     return dQ, dK, dV
+
+
+def mha_forward_train(X_q, X_kv, Wq, Wk, Wv, Wo, h, mask_kind=0, key_lengths=None, stream=None):
+    """mha_forward that keeps its state for mha_backward.  Returns (Y, state)
+    where state is the training workspace (uint8 tensor)."""
+    B, n_q, n_k, d_model, d_k, d_v = _mha_dims(X_q, X_kv, Wq, Wk, Wv, Wo, h)
+    Y = torch.empty((B, n_q, d_model), dtype=X_q.dtype, device=X_q.device)
+    nbytes = int(lib().mha_train_workspace_bytes(B, n_q, n_k, h, d_k, d_v, _dtype_code(X_q)))
+    state = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X_q.device)
+    arr, kl = _key_lengths(mask_kind, key_lengths, B)
+    st = lib().mha_forward_train(_dev(X_q, "X_q"), _dev(X_kv, "X_kv"), _dev(Wq, "Wq"), _dev(Wk, "Wk"),
+                                 _dev(Wv, "Wv"), _dev(Wo, "Wo"), _dev(Y, "Y"), B, n_q, n_k, d_model, h,
+                                 d_k, d_v, int(mask_kind), kl, _dtype_code(X_q), _dev(state, "state"),
+                                 state.numel(), _stream(stream))
+    _check("mha_forward_train", st)
+    return Y, state
+
+
+def mha_backward(X_q, X_kv, Wq, Wk, Wv, Wo, h, dY, state, mask_kind=0, key_lengths=None,
+                 stream=None):
+    """Gradients of the multi-head block: returns (dX_q, dX_kv, dWq, dWk, dWv, dWo);
+    for self-attention (X_kv is X_q) dX_kv is None and dX_q is the gradient of
+    the shared input."""
+    B, n_q, n_k, d_model, d_k, d_v = _mha_dims(X_q, X_kv, Wq, Wk, Wv, Wo, h)
+    self_attn = X_q.data_ptr() == X_kv.data_ptr() and n_q == n_k
+    dX_q = torch.empty_like(X_q)
+    dX_kv = None if self_attn else torch.empty_like(X_kv)
+    dWq, dWk, dWv, dWo = (torch.empty_like(t) for t in (Wq, Wk, Wv, Wo))
+    code = _dtype_code(X_q)
+    nbytes = int(lib().mha_backward_workspace_bytes(B, n_q, n_k, d_model, h, d_k, d_v,
+                                                    1 if self_attn else 0, code))
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=X_q.device)
+    arr, kl = _key_lengths(mask_kind, key_lengths, B)
+    st = lib().mha_backward(_dev(X_q, "X_q"), _dev(X_kv, "X_kv"), _dev(Wq, "Wq"), _dev(Wk, "Wk"),
+                            _dev(Wv, "Wv"), _dev(Wo, "Wo"), _dev(dY, "dY"), _dev(dX_q, "dX_q"),
+                            None if dX_kv is None else _dev(dX_kv, "dX_kv"), _dev(dWq, "dWq"),
+                            _dev(dWk, "dWk"), _dev(dWv, "dWv"), _dev(dWo, "dWo"), B, n_q, n_k, d_model,
+                            h, d_k, d_v, int(mask_kind), kl, code, _dev(state, "state"),
+                            state.numel(), _dev(ws, "workspace"), ws.numel(), _stream(stream))
+    _check("mha_backward", st)
+    return dX_q, dX_kv, dWq, dWk, dWv, dWo

@@ -167,7 +167,7 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   load_row_operand(dorow, g, dof);
   float dpart = 0.f;
   {
-    const __bf16* orow = (const __bf16*)a.O + qbase + (int64_t)qc * D;
+    const __bf16* orow = (const __bf16*)a.O + b * a.o_sb + (int64_t)(bh - b * a.h) * a.o_sh + (int64_t)qc * a.o_sr;
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
       const bf16x8 o8 = ((const bf16x8*)orow)[4 * g + c];
@@ -252,7 +252,9 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
     }
   }
   wait_vmcnt<0>();
-  if (my_q < a.n_q) store_row((__bf16*)a.dQ + qbase + (int64_t)my_q * D, g, dq0, dq1, a.scale);
+  if (my_q < a.n_q)
+    store_row((__bf16*)a.dQ + b * a.dq_sb + (int64_t)(bh - b * a.h) * a.dq_sh + (int64_t)my_q * a.dq_sr, g,
+              dq0, dq1, a.scale);
 }
 
 // ---------------------------------------------------------------- dK and dV
@@ -385,9 +387,9 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   }
   wait_vmcnt<0>();
   if (my_k < a.n_k) {
-    const int64_t off = kbase + (int64_t)my_k * D;
-    store_row((__bf16*)a.dK + off, g, dk0, dk1, a.scale);
-    store_row((__bf16*)a.dV + off, g, dv0, dv1, 1.0f);
+    const int64_t hh = bh - b * a.h;
+    store_row((__bf16*)a.dK + b * a.dk_sb + hh * a.dk_sh + (int64_t)my_k * a.dk_sr, g, dk0, dk1, a.scale);
+    store_row((__bf16*)a.dV + b * a.dv_sb + hh * a.dv_sh + (int64_t)my_k * a.dv_sr, g, dv0, dv1, 1.0f);
   }
 }
 

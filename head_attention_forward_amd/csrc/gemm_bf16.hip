@@ -128,7 +128,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
 
   // The tile's columns lie in one segment (segment starts are multiples of BN).
   const int sg = seg_of(g, n0);
-  const int wstride = seg_field(g, sg, &GemmSeg::width);
+  const int wwidth = seg_field(g, sg, &GemmSeg::width);
+  const int ldw_s = seg_field(g, sg, &GemmSeg::ldw);
+  const int wstride = ldw_s > 0 ? ldw_s : wwidth;  // row stride of the segment's weight
   const int ncol0 = n0 - seg_start(g, sg);  // first tile column within the segment
   const char* a_tile = (const char*)g.A + (int64_t)m0 * g.K * 2;
   const char* w_seg = (const char*)seg_ptr(g, sg);
@@ -151,7 +153,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
   for (int r = 0; r < BL; ++r) {
     const int row = (wave * BL + r) * (1024 / (2 * BN)) + lane / BROW;
     w_row[r] = row;
-    w_col[r] = min(ncol0 + 8 * b_pos<BN>(row, lane % BROW), wstride - 8);
+    w_col[r] = min(ncol0 + 8 * b_pos<BN>(row, lane % BROW), wwidth - 8);
     w_voff[r] = (unsigned)(row * wstride + w_col[r]) * 2u;
   }
   // LDS byte addresses of the two rings (wave-uniform, computed once).

@@ -46,6 +46,12 @@ struct BwdArgs {
   void* dV;
   float* Dw;
   float* Lw;
+  // batch, head, row strides (elements) of O, dQ, dK, dV; Q, K, V, dO are
+  // head-major and dense
+  int64_t o_sb, o_sh, o_sr;
+  int64_t dq_sb, dq_sh, dq_sr;
+  int64_t dk_sb, dk_sh, dk_sr;
+  int64_t dv_sb, dv_sh, dv_sr;
   int B, h, n_q, n_k;
   float scale;
   int causal;
@@ -54,7 +60,7 @@ struct BwdArgs {
 };
 
 // One column segment of a projection GEMM: columns [0, width) of weight W
-// (row stride = width) and the per-head scatter of the result:
+// (row stride ldw, or width) and the per-head scatter of the result:
 //   out element (row m, column c) -> dst[((b*heads + c/hd)*rows + pos)*hd + c%hd]
 // with b = m / rows, pos = m % rows, hd = head width.  A plain row-major
 // [M][width] output is heads = 1, hd = width, rows = M.
@@ -65,6 +71,7 @@ struct GemmSeg {
   int hd;
   int heads;
   int rows;
+  int ldw;   // row stride of W in elements (0: width); a multiple of 8
 };
 
 struct GemmArgs {
@@ -138,6 +145,8 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev = 
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_add_layernorm_bf16(const LnArgs& a, hipStream_t s, LaunchEvents ev = {});
+// dst[c][r] = src[r][c] for a dense bf16 [R][C] matrix (R, C multiples of 8).
+hipError_t launch_transpose_bf16(const void* src, void* dst, int R, int C, hipStream_t s, LaunchEvents ev = {});
 // f32 != 0: E and out are fp32, else bf16.
 hipError_t launch_embed_positional(const EmbedArgs& a, int f32, hipStream_t s, LaunchEvents ev = {});
 bool proj_attn_supported(int n_q, int n_k, int d_model);

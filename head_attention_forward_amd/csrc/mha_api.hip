@@ -179,7 +179,8 @@ int do_project_in(const void* X_q, const void* X_kv, const void* Wq, const void*
 }
 
 int do_attend(int B, int n_q, int n_k, int h, int d_k, int d_v, int mask_kind,
-              const int32_t* key_lengths, const Workspace& w, hipStream_t stream, Timer* tm) {
+              const int32_t* key_lengths, const Workspace& w, hipStream_t stream, Timer* tm,
+              float* lse = nullptr) {
   AttnArgs a;
   memset(&a, 0, sizeof(a));
   a.Q = w.Q;
@@ -198,6 +199,7 @@ int do_attend(int B, int n_q, int n_k, int h, int d_k, int d_v, int mask_kind,
   a.n_q = n_q;
   a.n_k = n_k;
   a.scale = 1.0f / sqrtf((float)d_k);
+  a.lse = lse;
   fill_mask(a, mask_kind, key_lengths);
   return launch_status(launch_attn_bf16_d64(a, stream, next_events(tm)));
 }
@@ -291,6 +293,99 @@ LayerWorkspace carve_layer(void* base, int B, int n, int d_model, int h, int d_k
 int layer_launch_count(int n, int d_model) {
   return (use_fused(n, n, d_model) ? 2 : 3) + 4;
 }
+
+// ---- training: the block's forward with its saved state, and its backward
+
+// Forward state kept for the backward: the block workspace (Q, K, V
+// head-major, O concatenated) and the row log-sum-exp [B][h][n_q].
+struct TrainWs {
+  Workspace blk;
+  float* lse;
+  size_t bytes;
+};
+
+TrainWs carve_train(void* base, int B, int n_q, int n_k, int h, int d_k, int d_v) {
+  TrainWs t;
+  t.blk = carve(base, B, n_q, n_k, h, d_k, d_v, MHA_DTYPE_BF16);
+  t.lse = (float*)((char*)base + t.blk.bytes);
+  t.bytes = t.blk.bytes + round_up((size_t)4 * B * h * n_q);
+  return t;
+}
+
+// Backward scratch.  Self-attention (shared input): dQ | dK | dV side by side
+// in one [M][3hd] buffer and [W^Q | W^K | W^V]^T stacked as one [3hd][d_model]
+// matrix, so dX is one GEMM; cross-attention: dQ [M_q][hd] and dK | dV
+// [M_k][2hd], with their transposed weights.
+struct BwdWs {
+  void* WoT;    // [h d_v][d_model]
+  void* dO;     // [B][h][n_q][d_v]
+  void* OcT;    // [h d_v][M_q]
+  void* dQKV;   // self: [M][3hd]; cross: dQ [M_q][hd]
+  void* dKV;    // cross: [M_k][2hd]
+  float* rows;  // sdpa_backward row terms (two arrays)
+  void* WT;     // self: [3hd][d_model]; cross: W^Q^T [hd][d_model]
+  void* WkvT;   // cross: [2hd][d_model]
+  void* XqT;    // [d_model][M_q]
+  void* XkvT;   // cross: [d_model][M_k]
+  size_t rows_each;
+  size_t bytes;
+};
+
+BwdWs carve_bwd(void* base, bool self_attn, int B, int n_q, int n_k, int d_model, int h, int d) {
+  BwdWs w{};
+  const size_t hd = (size_t)h * d, Mq = (size_t)B * n_q, Mk = (size_t)B * n_k, dm = d_model;
+  char* p = (char*)base;
+  auto take = [&](size_t bytes) {
+    char* r = p;
+    p += round_up(bytes);
+    return (void*)r;
+  };
+  w.WoT = take(2 * hd * dm);
+  w.dO = take(2 * Mq * hd);
+  w.OcT = take(2 * hd * Mq);
+  w.rows_each = round_up((size_t)4 * B * h * n_q);
+  if (self_attn) {
+    w.dQKV = take(2 * Mq * 3 * hd);
+    w.rows = (float*)take(2 * w.rows_each);
+    w.WT = take(2 * 3 * hd * dm);
+    w.XqT = take(2 * dm * Mq);
+  } else {
+    w.dQKV = take(2 * Mq * hd);
+    w.dKV = take(2 * Mk * 2 * hd);
+    w.rows = (float*)take(2 * w.rows_each);
+    w.WT = take(2 * hd * dm);
+    w.WkvT = take(2 * 2 * hd * dm);
+    w.XqT = take(2 * dm * Mq);
+    w.XkvT = take(2 * dm * Mk);
+  }
+  w.bytes = (size_t)(p - (char*)base);
+  return w;
+}
+
+// C = A . [segments], A [M][K] row-major; each segment a row-major weight
+// (row stride ldw) written as a plain row-major [M][width] matrix.
+int do_gemm_rm(const void* A, int M, int K, int nseg, const void* const* W, void* const* dst,
+               const int* width, int ldw, hipStream_t stream, Timer* tm) {
+  GemmArgs g{};
+  g.A = A;
+  g.M = M;
+  g.K = K;
+  g.nseg = nseg;
+  int c = 0;
+  for (int s = 0; s < nseg; ++s) {
+    g.seg[s] = GemmSeg{W[s], dst[s], width[s], width[s], 1, M, ldw};
+    g.col_start[s] = c;
+    c += width[s];
+  }
+  g.col_start[nseg] = c;
+  return launch_status(launch_gemm_bf16(g, stream, next_events(tm)));
+}
+
+int do_transpose(const void* src, void* dst, int R, int C, hipStream_t stream, Timer* tm) {
+  return launch_status(launch_transpose_bf16(src, dst, R, C, stream, next_events(tm)));
+}
+
+int mha_bwd_launch_count(bool self_attn) { return self_attn ? 12 : 15; }
 
 }  // namespace
 }  // namespace mha
@@ -696,6 +791,10 @@ static int bwd_impl(const void* Q, const void* K, const void* V, const void* O, 
   a.dV = dV;
   a.Dw = (float*)workspace;
   a.Lw = (float*)((char*)workspace + row_terms);
+  set_head_major(a.o_sb, a.o_sh, a.o_sr, h, n_q, d_v);
+  set_head_major(a.dq_sb, a.dq_sh, a.dq_sr, h, n_q, d_k);
+  set_head_major(a.dk_sb, a.dk_sh, a.dk_sr, h, n_k, d_k);
+  set_head_major(a.dv_sb, a.dv_sh, a.dv_sr, h, n_k, d_v);
   a.B = B;
   a.h = h;
   a.n_q = n_q;
@@ -732,6 +831,228 @@ int sdpa_backward_timed(const void* Q, const void* K, const void* V, const void*
                           mask_kind, key_lengths, dtype, workspace, workspace_bytes, stream, &tm);
   if (n_launches) *n_launches = tm.used;
   return st;
+}
+
+size_t mha_train_workspace_bytes(int B, int n_q, int n_k, int h, int d_k, int d_v, int dtype) {
+  if (B <= 0 || n_q <= 0 || n_k <= 0 || h <= 0 || d_k <= 0 || d_v <= 0) return 0;
+  if (dtype != MHA_DTYPE_BF16) return 0;
+  return carve_train(nullptr, B, n_q, n_k, h, d_k, d_v).bytes;
+}
+
+int mha_forward_train(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
+                      const void* Wv, const void* Wo, void* Y, int B, int n_q, int n_k,
+                      int d_model, int h, int d_k, int d_v, int mask_kind,
+                      const int32_t* key_lengths, int dtype, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream) {
+  if (!X_q || !X_kv || !Wq || !Wk || !Wv || !Wo || !Y) return MHA_ERR_NULL;
+  int st = check_mha(workspace, workspace_bytes, B, n_q, n_k, d_model, h, d_k, d_v, dtype);
+  if (st != MHA_OK) return st;
+  if (workspace_bytes < carve_train(nullptr, B, n_q, n_k, h, d_k, d_v).bytes) return MHA_ERR_WORKSPACE;
+  st = check_mask(mask_kind, B, n_q, n_k, key_lengths);
+  if (st != MHA_OK) return st;
+  if (!aligned16(X_q) || !aligned16(X_kv) || !aligned16(Wq) || !aligned16(Wk) ||
+      !aligned16(Wv) || !aligned16(Wo) || !aligned16(Y))
+    return MHA_ERR_UNSUPPORTED;
+  const TrainWs t = carve_train(workspace, B, n_q, n_k, h, d_k, d_v);
+  st = do_project_in(X_q, X_kv, Wq, Wk, Wv, B, n_q, n_k, d_model, h, d_k, d_v, t.blk, stream, nullptr);
+  if (st != MHA_OK) return st;
+  st = do_attend(B, n_q, n_k, h, d_k, d_v, mask_kind, key_lengths, t.blk, stream, nullptr, t.lse);
+  if (st != MHA_OK) return st;
+  return do_project_out(Wo, Y, B, n_q, d_model, h, d_v, t.blk, stream, nullptr);
+}
+
+size_t mha_backward_workspace_bytes(int B, int n_q, int n_k, int d_model, int h, int d_k, int d_v,
+                                    int self_attention, int dtype) {
+  if (B <= 0 || n_q <= 0 || n_k <= 0 || d_model <= 0 || h <= 0 || d_k <= 0 || d_v <= 0) return 0;
+  if (dtype != MHA_DTYPE_BF16 || d_k != d_v) return 0;
+  return carve_bwd(nullptr, self_attention && n_q == n_k, B, n_q, n_k, d_model, h, d_k).bytes;
+}
+
+static int mha_bwd_impl(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
+                        const void* Wv, const void* Wo, const void* dY, void* dX_q, void* dX_kv,
+                        void* dWq, void* dWk, void* dWv, void* dWo, int B, int n_q, int n_k,
+                        int d_model, int h, int d_k, int d_v, int mask_kind,
+                        const int32_t* key_lengths, int dtype, const void* train_ws,
+                        size_t train_ws_bytes, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream, Timer* tm) {
+  const bool self_attn = X_q == X_kv && n_q == n_k;
+  if (!X_q || !X_kv || !Wq || !Wk || !Wv || !Wo || !dY || !dX_q || !dWq || !dWk || !dWv || !dWo)
+    return MHA_ERR_NULL;
+  if (!self_attn && !dX_kv) return MHA_ERR_NULL;
+  int st = check_mha(train_ws, train_ws_bytes, B, n_q, n_k, d_model, h, d_k, d_v, dtype);
+  if (st != MHA_OK) return st == MHA_ERR_WORKSPACE ? MHA_ERR_WORKSPACE : st;
+  if (train_ws_bytes < carve_train(nullptr, B, n_q, n_k, h, d_k, d_v).bytes) return MHA_ERR_WORKSPACE;
+  st = check_mask(mask_kind, B, n_q, n_k, key_lengths);
+  if (st != MHA_OK) return st;
+  const int64_t Mq = (int64_t)B * n_q, Mk = (int64_t)B * n_k;
+  // The transposed activations are GEMM operands with Mq (Mk) columns.
+  if (Mq % 8 != 0 || Mk % 8 != 0) return MHA_ERR_UNSUPPORTED;
+  if (Mq > (int64_t)65535 * 64 || Mk > (int64_t)65535 * 64) return MHA_ERR_DIM;
+  if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0 ||
+      workspace_bytes < carve_bwd(nullptr, self_attn, B, n_q, n_k, d_model, h, d_k).bytes)
+    return MHA_ERR_WORKSPACE;
+  const void* p16[] = {X_q, X_kv, Wq, Wk, Wv, Wo, dY, dX_q, dWq, dWk, dWv, dWo};
+  for (const void* p : p16)
+    if (!aligned16(p)) return MHA_ERR_UNSUPPORTED;
+  if (!self_attn && !aligned16(dX_kv)) return MHA_ERR_UNSUPPORTED;
+
+  const TrainWs t = carve_train((void*)train_ws, B, n_q, n_k, h, d_k, d_v);
+  const BwdWs w = carve_bwd(workspace, self_attn, B, n_q, n_k, d_model, h, d_k);
+  const int hd = h * d_k, dm = d_model;
+  // dC = dY W^O^T, scattered per head into dO [B][h][n_q][d]
+  st = do_transpose(Wo, w.WoT, hd, dm, stream, tm);
+  if (st != MHA_OK) return st;
+  {
+    GemmArgs g{};
+    g.A = dY;
+    g.M = (int)Mq;
+    g.K = dm;
+    g.nseg = 1;
+    g.seg[0] = GemmSeg{w.WoT, w.dO, hd, d_v, h, n_q, 0};
+    g.col_start[0] = 0;
+    g.col_start[1] = hd;
+    st = launch_status(launch_gemm_bf16(g, stream, next_events(tm)));
+    if (st != MHA_OK) return st;
+  }
+  // dW^O = C^T dY
+  st = do_transpose(t.blk.O, w.OcT, (int)Mq, hd, stream, tm);
+  if (st != MHA_OK) return st;
+  {
+    const void* W[1] = {dY};
+    void* D[1] = {dWo};
+    const int wd[1] = {dm};
+    st = do_gemm_rm(w.OcT, hd, (int)Mq, 1, W, D, wd, 0, stream, tm);
+    if (st != MHA_OK) return st;
+  }
+  // attention gradients, written with the heads concatenated
+  {
+    BwdArgs a;
+    memset(&a, 0, sizeof(a));
+    a.Q = t.blk.Q;
+    a.K = t.blk.K;
+    a.V = t.blk.V;
+    a.O = t.blk.O;
+    a.dO = w.dO;
+    a.lse = t.lse;
+    a.Dw = w.rows;
+    a.Lw = (float*)((char*)w.rows + w.rows_each);
+    a.o_sb = (int64_t)n_q * hd;
+    a.o_sh = d_v;
+    a.o_sr = hd;
+    const int ldq = self_attn ? 3 * hd : hd;  // row stride of the dQ buffer
+    const int ldkv = self_attn ? 3 * hd : 2 * hd;
+    __bf16* dq = (__bf16*)w.dQKV;
+    __bf16* dk = self_attn ? dq + hd : (__bf16*)w.dKV;
+    __bf16* dv = dk + hd;
+    a.dQ = dq;
+    a.dK = dk;
+    a.dV = dv;
+    a.dq_sb = (int64_t)n_q * ldq;
+    a.dq_sh = d_k;
+    a.dq_sr = ldq;
+    a.dk_sb = a.dv_sb = (int64_t)n_k * ldkv;
+    a.dk_sh = a.dv_sh = d_k;
+    a.dk_sr = a.dv_sr = ldkv;
+    a.B = B;
+    a.h = h;
+    a.n_q = n_q;
+    a.n_k = n_k;
+    a.scale = 1.0f / sqrtf((float)d_k);
+    a.causal = (mask_kind & MHA_MASK_CAUSAL) ? 1 : 0;
+    a.padded = (mask_kind & MHA_MASK_KEY_PADDING) ? 1 : 0;
+    if (a.padded)
+      for (int b = 0; b < B; ++b) a.key_len[b] = key_lengths[b];
+    st = launch_status(launch_attn_bwd_dq(a, stream, next_events(tm)));
+    if (st != MHA_OK) return st;
+    st = launch_status(launch_attn_bwd_dkdv(a, stream, next_events(tm)));
+    if (st != MHA_OK) return st;
+  }
+  const size_t wblock = (size_t)hd * dm;  // elements of one transposed weight
+  if (self_attn) {
+    // dX = [dQ | dK | dV] [W^Q | W^K | W^V]^T
+    st = do_transpose(Wq, w.WT, dm, hd, stream, tm);
+    if (st == MHA_OK) st = do_transpose(Wk, (__bf16*)w.WT + wblock, dm, hd, stream, tm);
+    if (st == MHA_OK) st = do_transpose(Wv, (__bf16*)w.WT + 2 * wblock, dm, hd, stream, tm);
+    if (st != MHA_OK) return st;
+    const void* W[1] = {w.WT};
+    void* D[1] = {dX_q};
+    const int wd[1] = {dm};
+    st = do_gemm_rm(w.dQKV, (int)Mq, 3 * hd, 1, W, D, wd, 0, stream, tm);
+    if (st != MHA_OK) return st;
+    // [dW^Q | dW^K | dW^V] = X^T [dQ | dK | dV]
+    st = do_transpose(X_q, w.XqT, (int)Mq, dm, stream, tm);
+    if (st != MHA_OK) return st;
+    const void* W3[3] = {w.dQKV, (__bf16*)w.dQKV + hd, (__bf16*)w.dQKV + 2 * hd};
+    void* D3[3] = {dWq, dWk, dWv};
+    const int wd3[3] = {hd, hd, hd};
+    return do_gemm_rm(w.XqT, dm, (int)Mq, 3, W3, D3, wd3, 3 * hd, stream, tm);
+  }
+  // cross-attention: dX_q = dQ W^Q^T, dX_kv = [dK | dV] [W^K | W^V]^T
+  st = do_transpose(Wq, w.WT, dm, hd, stream, tm);
+  if (st == MHA_OK) st = do_transpose(Wk, w.WkvT, dm, hd, stream, tm);
+  if (st == MHA_OK) st = do_transpose(Wv, (__bf16*)w.WkvT + wblock, dm, hd, stream, tm);
+  if (st != MHA_OK) return st;
+  {
+    const void* W[1] = {w.WT};
+    void* D[1] = {dX_q};
+    const int wd[1] = {dm};
+    st = do_gemm_rm(w.dQKV, (int)Mq, hd, 1, W, D, wd, 0, stream, tm);
+    if (st != MHA_OK) return st;
+    const void* W2[1] = {w.WkvT};
+    void* D2[1] = {dX_kv};
+    st = do_gemm_rm(w.dKV, (int)Mk, 2 * hd, 1, W2, D2, wd, 0, stream, tm);
+    if (st != MHA_OK) return st;
+  }
+  // dW^Q = X_q^T dQ, [dW^K | dW^V] = X_kv^T [dK | dV]
+  st = do_transpose(X_q, w.XqT, (int)Mq, dm, stream, tm);
+  if (st == MHA_OK) st = do_transpose(X_kv, w.XkvT, (int)Mk, dm, stream, tm);
+  if (st != MHA_OK) return st;
+  {
+    const void* W[1] = {w.dQKV};
+    void* D[1] = {dWq};
+    const int wd[1] = {hd};
+    st = do_gemm_rm(w.XqT, dm, (int)Mq, 1, W, D, wd, 0, stream, tm);
+    if (st != MHA_OK) return st;
+    const void* W2[2] = {w.dKV, (__bf16*)w.dKV + hd};
+    void* D2[2] = {dWk, dWv};
+    const int wd2[2] = {hd, hd};
+    return do_gemm_rm(w.XkvT, dm, (int)Mk, 2, W2, D2, wd2, 2 * hd, stream, tm);
+  }
+}
+
+int mha_backward(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
+                 const void* Wv, const void* Wo, const void* dY, void* dX_q, void* dX_kv,
+                 void* dWq, void* dWk, void* dWv, void* dWo, int B, int n_q, int n_k,
+                 int d_model, int h, int d_k, int d_v, int mask_kind, const int32_t* key_lengths,
+                 int dtype, const void* train_workspace, size_t train_workspace_bytes,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return mha_bwd_impl(X_q, X_kv, Wq, Wk, Wv, Wo, dY, dX_q, dX_kv, dWq, dWk, dWv, dWo, B, n_q, n_k,
+                      d_model, h, d_k, d_v, mask_kind, key_lengths, dtype, train_workspace,
+                      train_workspace_bytes, workspace, workspace_bytes, stream, nullptr);
+}
+
+int mha_backward_timed(const void* X_q, const void* X_kv, const void* Wq, const void* Wk,
+                       const void* Wv, const void* Wo, const void* dY, void* dX_q, void* dX_kv,
+                       void* dWq, void* dWk, void* dWv, void* dWo, int B, int n_q, int n_k,
+                       int d_model, int h, int d_k, int d_v, int mask_kind,
+                       const int32_t* key_lengths, int dtype, const void* train_workspace,
+                       size_t train_workspace_bytes, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, hipEvent_t* events, int capacity, int* n_launches) {
+  const int need = 2 * mha_bwd_launch_count(X_q == X_kv && n_q == n_k);
+  if (events == nullptr || capacity < need) return MHA_ERR_EVENTS;
+  for (int i = 0; i < need; ++i)
+    if (events[i] == nullptr) return MHA_ERR_EVENTS;
+  Timer tm{events, capacity, 0};
+  const int st = mha_bwd_impl(X_q, X_kv, Wq, Wk, Wv, Wo, dY, dX_q, dX_kv, dWq, dWk, dWv, dWo, B, n_q,
+                              n_k, d_model, h, d_k, d_v, mask_kind, key_lengths, dtype,
+                              train_workspace, train_workspace_bytes, workspace, workspace_bytes,
+                              stream, &tm);
+  if (n_launches) *n_launches = tm.used;
+  return st;
+}
+
+int mha_backward_launches(int self_attention) {
+  return mha_bwd_launch_count(self_attention != 0);
 }
 
 }  // extern "C"

@@ -293,6 +293,91 @@ int sdpa_backward_timed(const void* Q, const void* K, const void* V, const void*
                         hipEvent_t* events, int capacity, int* n_launches);
 
 /*
+ * mha_train_workspace_bytes -- state mha_forward_train keeps for
+ * mha_backward: the block workspace of mha_workspace_bytes (Q, K, V
+ * head-major, the concatenated heads) followed by the row log-sum-exp
+ * [B][h][n_q] (fp32), 256-byte aligned.  0 for invalid sizes; bf16 only.
+ */
+size_t mha_train_workspace_bytes(int B, int n_q, int n_k, int h, int d_k, int d_v, int dtype);
+
+/*
+ * mha_forward_train -- mha_forward for training: the same Y (same kernels
+ * as the staged plan: stacked or split input projections, attention,
+ * output projection), keeping in the workspace everything mha_backward
+ * needs.  Arguments as mha_forward; workspace >=
+ * mha_train_workspace_bytes(...).
+ */
+int mha_forward_train(const void* X_q, const void* X_kv,
+                      const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                      void* Y,
+                      int B, int n_q, int n_k, int d_model, int h, int d_k, int d_v,
+                      int mask_kind, const int32_t* key_lengths, int dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * mha_backward_workspace_bytes -- scratch of mha_backward (transposed
+ * operands, the per-head upstream gradient, the attention gradients with
+ * their heads concatenated, row terms).  self_attention nonzero when X_kv
+ * will be the same pointer as X_q (and n_q == n_k).  0 for invalid sizes.
+ */
+size_t mha_backward_workspace_bytes(int B, int n_q, int n_k, int d_model, int h, int d_k,
+                                    int d_v, int self_attention, int dtype);
+
+/*
+ * mha_backward -- gradients of the multi-head block Y = Concat(head_1..h) W^O
+ * (devpress.csdn.net "【深度学习】Transformer", section 2.2) for the upstream
+ * gradient dY [B][n_q][d_model], through the block's steps in reverse:
+ *   dC = dY W^O^T,  dW^O = C^T dY            (C: concatenated heads)
+ *   dQ, dK, dV of each head                  (as sdpa_backward)
+ *   dW^Q = X_q^T dQ_c,  dW^K = X_kv^T dK_c,  dW^V = X_kv^T dV_c
+ *   dX_q = dQ_c W^Q^T,  dX_kv = dK_c W^K^T + dV_c W^V^T
+ * (_c: heads concatenated, [rows][h*d]).  Training back-propagates through
+ * every part (hex4c59.cc "读懂 Attention Is All You Need", section
+ * "参数是怎样学出来的？").
+ *
+ *   X_q, X_kv, Wq, Wk, Wv, Wo, B ... key_lengths, dtype: exactly as the
+ *       mha_forward_train call whose workspace is passed as train_workspace
+ *       (read only).
+ *   dY  [B][n_q][d_model];  outputs dWq, dWk [d_model][h*d_k], dWv
+ *       [d_model][h*d_v], dWo [h*d_v][d_model], dX_q [B][n_q][d_model] and,
+ *       for cross-attention, dX_kv [B][n_k][d_model].  Self-attention (X_kv
+ *       the same pointer as X_q, n_q == n_k): dX_q receives the gradient
+ *       with respect to the shared input (both paths summed) and dX_kv is
+ *       ignored.  Outputs must not overlap inputs or workspaces.
+ *   workspace >= mha_backward_workspace_bytes(...), 256-byte aligned.
+ *   B*n_q and B*n_k must be multiples of 8 (MHA_ERR_UNSUPPORTED): the
+ *   transposed activations are GEMM operands of that width.
+ * Launches (mha_backward_launches): transposes of W^O, C, the stacked input
+ * weights and the inputs (bandwidth-bound copies that let the projection
+ * GEMM take every product as A . B with row-major operands), four or six
+ * GEMMs and the two attention-backward kernels.  bf16 in and out, fp32
+ * accumulation.
+ */
+int mha_backward(const void* X_q, const void* X_kv,
+                 const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                 const void* dY, void* dX_q, void* dX_kv,
+                 void* dWq, void* dWk, void* dWv, void* dWo,
+                 int B, int n_q, int n_k, int d_model, int h, int d_k, int d_v,
+                 int mask_kind, const int32_t* key_lengths, int dtype,
+                 const void* train_workspace, size_t train_workspace_bytes,
+                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* mha_backward with launch events, as the other _timed variants. */
+int mha_backward_timed(const void* X_q, const void* X_kv,
+                       const void* Wq, const void* Wk, const void* Wv, const void* Wo,
+                       const void* dY, void* dX_q, void* dX_kv,
+                       void* dWq, void* dWk, void* dWv, void* dWo,
+                       int B, int n_q, int n_k, int d_model, int h, int d_k, int d_v,
+                       int mask_kind, const int32_t* key_lengths, int dtype,
+                       const void* train_workspace, size_t train_workspace_bytes,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream,
+                       hipEvent_t* events, int capacity, int* n_launches);
+
+/* mha_backward_launches -- kernels mha_backward launches: 12 for
+ * self-attention, 15 for cross-attention.  Host-only. */
+int mha_backward_launches(int self_attention);
+
+/*
  * ---------------------------------------------------------------------------
  * The rest of an encoder layer around the attention block: residual +
  * LayerNorm (Post-LN) and the position-wise feed-forward network.  These

@@ -320,3 +320,29 @@ def test_backward_rejections(L):
                               None) == NULL
     assert L.sdpa_forward_lse(FAKE, FAKE, FAKE, FAKE2, FAKE, 2, 2, 8, 8, 64, 64, 0.125, 0, None, F32,
                               None) == UNSUP
+
+
+def test_mha_backward_rejections(L):
+    B, n, dm, h = 2, 8, 64, 2
+    tws = L.mha_train_workspace_bytes(B, n, n, h, 64, 64, BF16)
+    assert tws == L.mha_workspace_bytes(B, n, n, h, 64, 64, BF16) + 256
+    bws = L.mha_backward_workspace_bytes(B, n, n, dm, h, 64, 64, 1, BF16)
+    assert bws > 0 and L.mha_backward_workspace_bytes(B, n, n, dm, h, 64, 64, 1, F32) == 0
+    assert L.mha_backward_launches(1) == 12 and L.mha_backward_launches(0) == 15
+
+    def bwd(Xq=FAKE, Xkv=FAKE, dXkv=None, B=B, n_q=n, n_k=n, mask=0, kl=None, dtype=BF16, tw=FAKE,
+            tw_bytes=tws, ws=FAKE2, ws_bytes=bws):
+        return L.mha_backward(Xq, Xkv, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, dXkv, FAKE2, FAKE2, FAKE2,
+                              FAKE2, B, n_q, n_k, dm, h, 64, 64, mask, kl, dtype, tw, tw_bytes, ws,
+                              ws_bytes, None)
+    assert bwd(Xq=None) == NULL
+    assert bwd(Xkv=FAKE2) == NULL                 # cross-attention needs dX_kv
+    assert bwd(tw=None) == WS
+    assert bwd(tw_bytes=tws - 256) == WS          # no room for the log-sum-exp
+    assert bwd(ws=None) == WS
+    assert bwd(ws_bytes=bws - 1) == WS
+    assert bwd(B=1, n_q=5, n_k=5, tw_bytes=1 << 30) == UNSUP   # B*n not a multiple of 8
+    assert bwd(mask=2) == KEYLEN
+    assert bwd(dtype=F32) == UNSUP
+    assert L.mha_forward_train(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, B, n, n, dm, h, 64, 64, 0,
+                               None, BF16, FAKE, tws - 256, None) == WS

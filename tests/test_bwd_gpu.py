@@ -142,3 +142,60 @@ def test_backward_long_causal(dev):
     check_grad(dQ, wQ, "dQ long causal")
     check_grad(dK, wK, "dK long causal")
     check_grad(dV, wV, "dV long causal")
+
+
+# ------------------------------------------------------------------ the block's gradients
+
+def check_block_grad(got, want, what):
+    """Block gradients pass through more bf16 roundings (the per-head upstream
+    gradient, the concatenated dQ/dK/dV, the GEMM outputs): relative L2 <= 4u
+    and every element within 8u * max|exact|."""
+    g = to_f64(got)
+    assert np.all(np.isfinite(g)), f"{what}: non-finite"
+    err = np.abs(g - want)
+    scale = max(float(np.abs(want).max()), 1e-30)
+    rel = float(np.linalg.norm(g - want) / max(np.linalg.norm(want), 1e-300))
+    worst = float(err.max()) / (8 * U * scale)
+    print(f"  {what}: rel_l2={rel:.2e} worst/bound {worst:.3f}", flush=True)
+    assert rel <= 4 * U, f"{what}: rel-L2 {rel}"
+    assert worst <= 1.0, f"{what}: max-abs {float(err.max())}"
+
+
+BLOCK_CASES = [
+    # B, n_q, n_k, d_model, h, self_attn, mask, key_lengths, label
+    (4, 100, 100, 512, 8, True, 0, None, "encoder self-attention (fused forward shape)"),
+    (2, 256, 256, 512, 8, True, 1, None, "causal self-attention"),
+    (4, 96, 128, 256, 4, False, 2, [128, 64, 100, 1], "cross-attention, key padding"),
+    (8, 7, 9, 128, 2, False, 0, None, "tiny ragged cross-attention (B n multiples of 8)"),
+]
+
+
+@pytest.mark.parametrize("B,n_q,n_k,dm,h,self_attn,mask,kl,label", BLOCK_CASES)
+def test_mha_backward(dev, B, n_q, n_k, dm, h, self_attn, mask, kl, label):
+    g = torch.Generator("cpu")
+    g.manual_seed(B + n_q + dm)
+    Xq = torch.randn((B, n_q, dm), generator=g).to(torch.bfloat16)
+    Xkv = Xq if self_attn else torch.randn((B, n_k, dm), generator=g).to(torch.bfloat16)
+    Ws = [(torch.randn((dm, h * 64), generator=g) / dm ** 0.5).to(torch.bfloat16) for _ in range(3)]
+    Ws.append((torch.randn((h * 64, dm), generator=g) / (h * 64) ** 0.5).to(torch.bfloat16))
+    dY = torch.randn((B, n_q, dm), generator=g).to(torch.bfloat16)
+    announce("mha backward", B, n_q, n_k, dm, h, self_attn, mask, kl, label)
+    Xqd = Xq.to(dev)
+    Xkvd = Xqd if self_attn else Xkv.to(dev)
+    Wd = [w.to(dev) for w in Ws]
+    Y, state = hafa.mha_forward_train(Xqd, Xkvd, *Wd, h, mask, kl)
+    Y0 = hafa.mha_forward(Xqd, Xkvd, *Wd, h, mask, kl)
+    grads = hafa.mha_backward(Xqd, Xkvd, *Wd, h, dY.to(dev), state, mask, kl)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y0)  # the training forward gives the same output
+    kla = None if kl is None else np.array(kl)
+    want = oracle.mha_backward_ref(to_f64(Xq), to_f64(Xkv), *[to_f64(w) for w in Ws], h, to_f64(dY),
+                                   mask, kla)
+    if self_attn:
+        assert grads[1] is None
+        check_block_grad(grads[0], want[0] + want[1], f"dX {label}")
+    else:
+        check_block_grad(grads[0], want[0], f"dX_q {label}")
+        check_block_grad(grads[1], want[1], f"dX_kv {label}")
+    for name, gt, wt in zip(("dWq", "dWk", "dWv", "dWo"), grads[2:], want[2:]):
+        check_block_grad(gt, wt, f"{name} {label}")
