@@ -84,6 +84,9 @@ def step_launches(w):
         return 1
     if w.kind == "bwd":
         return 2
+    if w.kind == "mha_bwd":
+        from head_attention_forward_amd import _binding as bnd
+        return int(bnd.lib().mha_backward_launches(1 if w.self_attn else 0))
     return layer_launches(w) if w.kind == "layer" else mha_launches(w)
 
 
@@ -121,6 +124,32 @@ def kernel_plan(w, n_launches=None):
         plan.append(dict(name="backward_dkdv", flops=8.0 * pairs * dk,
                          bytes=float(e * rows_k * dk * 4 + e * rows_q * dk * 2 + 4 * rows_q * 2),
                          peak_kind="mfma", has_attention=False))
+        return plan, None
+    if w.kind == "mha_bwd":
+        if not w.self_attn:
+            raise ValueError("the block-backward bench covers self-attention")
+        M, dm, hd = B * nq, w.d_model, h * dk
+        pairs = bwd_pairs(w)
+
+        def tr(name, R, C):
+            plan.append(dict(name=name, flops=0.0, bytes=float(2 * e * R * C), peak_kind="hbm",
+                             has_attention=False))
+        tr("transpose_wo", hd, dm)
+        gemm("do_gemm", M, dm, hd)
+        tr("transpose_concat", M, hd)
+        gemm("dwo_gemm", hd, M, dm)
+        plan.append(dict(name="backward_dq", flops=6.0 * pairs * dk,
+                         bytes=float(e * B * h * nq * dk * 4 + 8 * B * h * nq + e * B * h * nk * dk * 2),
+                         peak_kind="mfma", has_attention=False))
+        plan.append(dict(name="backward_dkdv", flops=8.0 * pairs * dk,
+                         bytes=float(e * B * h * nk * dk * 4 + e * B * h * nq * dk * 2 + 8 * B * h * nq),
+                         peak_kind="mfma", has_attention=False))
+        tr("transpose_wq", dm, hd)
+        tr("transpose_wk", dm, hd)
+        tr("transpose_wv", dm, hd)
+        gemm("dx_gemm", M, 3 * hd, dm)
+        tr("transpose_x", M, dm)
+        gemm("dw_gemm", dm, M, 3 * hd)
         return plan, None
     if w.kind == "embed":
         # gather one table row per token, write one row per token, read the ids
@@ -166,6 +195,14 @@ def bwd_pairs(w, key_lengths=None):
         else:
             pairs += w.n_q * L[b]
     return pairs * w.h
+
+
+def block_bwd_flops(w, key_lengths=None):
+    """Algorithmic flops of the block's backward: two products per forward
+    projection (dX and dW for each of W^Q, W^K, W^V, W^O) and five per
+    visible pair of the attention."""
+    M, dm, hd = w.B * w.n_q, w.d_model, w.h * w.d_k
+    return 2.0 * (2.0 * M * dm * hd * 4) + 10.0 * bwd_pairs(w, key_lengths) * w.d_k
 
 
 def attention_accounting(w, key_lengths):
@@ -240,6 +277,32 @@ class Step:
                                   P(dK.data_ptr()), P(dV.data_ptr()), w.B, w.h, w.n_q, w.n_k, w.d_k,
                                   w.d_v, float(x["scale"]), w.mask, self.kl, bnd.DTYPE_BF16,
                                   P(ws.data_ptr()), nbytes))
+            elif w.kind == "mha_bwd":
+                Xq = x["X_q"].to(dev)
+                Ws = [x[k].to(dev) for k in ("Wq", "Wk", "Wv", "Wo")]
+                dY = x["dY"].to(dev)
+                Y = torch.empty((w.B, w.n_q, w.d_model), dtype=Xq.dtype, device=dev)
+                tb = int(self.lib.mha_train_workspace_bytes(w.B, w.n_q, w.n_k, w.h, w.d_k, w.d_v,
+                                                            bnd.DTYPE_BF16))
+                state = torch.empty(tb, dtype=torch.uint8, device=dev)
+                sp0 = P(torch.cuda.current_stream().cuda_stream)
+                st = self.lib.mha_forward_train(P(Xq.data_ptr()), P(Xq.data_ptr()),
+                                                *[P(t.data_ptr()) for t in Ws], P(Y.data_ptr()), w.B,
+                                                w.n_q, w.n_k, w.d_model, w.h, w.d_k, w.d_v, w.mask,
+                                                self.kl, bnd.DTYPE_BF16, P(state.data_ptr()), tb, sp0)
+                if st != 0:
+                    raise RuntimeError(f"mha_forward_train failed with status {st}")
+                dX = torch.empty_like(Xq)
+                dW = [torch.empty_like(t) for t in Ws]
+                bb = int(self.lib.mha_backward_workspace_bytes(w.B, w.n_q, w.n_k, w.d_model, w.h,
+                                                               w.d_k, w.d_v, 1, bnd.DTYPE_BF16))
+                ws = torch.empty(bb, dtype=torch.uint8, device=dev)
+                self.keep.append((Xq, Ws, dY, dX, *dW, state, ws, Y))
+                self.sets.append((P(Xq.data_ptr()), P(Xq.data_ptr()), *[P(t.data_ptr()) for t in Ws],
+                                  P(dY.data_ptr()), P(dX.data_ptr()), None,
+                                  *[P(t.data_ptr()) for t in dW], w.B, w.n_q, w.n_k, w.d_model, w.h,
+                                  w.d_k, w.d_v, w.mask, self.kl, bnd.DTYPE_BF16, P(state.data_ptr()),
+                                  tb, P(ws.data_ptr()), bb))
             elif w.kind == "embed":
                 T = x["tokens"].to(dev)
                 E = x["E"].to(dev)
@@ -272,14 +335,19 @@ class Step:
                                   bnd.DTYPE_BF16, P(ws.data_ptr()), ws.numel()))
         self.n_launches = step_launches(w)
         names = {"sdpa": "sdpa_forward", "mha": "mha_forward", "layer": "encoder_layer_forward",
-                 "embed": "embed_positional_forward", "bwd": "sdpa_backward"}
+                 "embed": "embed_positional_forward", "bwd": "sdpa_backward",
+                 "mha_bwd": "mha_backward"}
         self.entry = names[w.kind]
 
     def output(self, i):
         return self.keep[i][3]
 
     def parity_output(self, i):
-        return self.keep[i][3:6] if self.w.kind == "bwd" else self.keep[i][3]
+        if self.w.kind == "bwd":
+            return self.keep[i][3:6]
+        if self.w.kind == "mha_bwd":
+            return self.keep[i][3:8]  # dX, dWq, dWk, dWv, dWo
+        return self.keep[i][3]
 
     def run(self, i, stream):
         st = getattr(self.lib, self.entry)(*self.sets[i], stream)
@@ -296,6 +364,10 @@ class Step:
 
 def set_bytes(w):
     e = 2 if w.dtype == "bf16" else 4
+    if w.kind == "mha_bwd":
+        M, dm, hd = w.B * w.n_q, w.d_model, w.h * w.d_k
+        return e * (3 * M * dm + 8 * dm * hd + 4 * M * hd + 2 * M * 3 * hd + 3 * M * hd + hd * M +
+                    3 * hd * dm + dm * M)
     if w.kind == "bwd":
         return e * w.B * w.h * (w.n_q * 64 * 4 + w.n_k * 64 * 4) + 8 * w.B * w.h * w.n_q
     if w.kind == "embed":
@@ -330,6 +402,23 @@ def parity_check(w, x, out):
     from head_attention_forward_amd.workloads import to_f64
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
     rows = "all"
+    if w.kind == "mha_bwd":
+        # whole gradients; bar of the block-gradient tests: rel-L2 <= 4u and
+        # every element within 8u max|want|, u = 2^-8
+        u = 2.0 ** -8
+        want = oracle.mha_backward_ref(to_f64(x["X_q"]), to_f64(x["X_q"]),
+                                       *[to_f64(x[k]) for k in ("Wq", "Wk", "Wv", "Wo")], w.h,
+                                       to_f64(x["dY"]), w.mask, kl)
+        wants = [want[0] + want[1]] + list(want[2:])
+        worst, rel_max, max_abs = 0.0, 0.0, 0.0
+        for got_t, want_t in zip(out, wants):
+            got = to_f64(got_t)
+            err = np.abs(got - want_t)
+            worst = max(worst, float(err.max()) / (8 * u * float(np.abs(want_t).max())))
+            rel_max = max(rel_max, float(np.linalg.norm(got - want_t) / np.linalg.norm(want_t)))
+            max_abs = max(max_abs, float(err.max()))
+        return dict(max_abs=max_abs, rel_l2=rel_max, worst_over_bound=worst,
+                    ok=bool(worst <= 1.0 and rel_max <= 4 * u), rows="all (dX, dWq, dWk, dWv, dWo)")
     if w.kind == "bwd":
         # two sampled (batch, head) pairs, whole gradients; the test bar:
         # rel-L2 <= 2u and every element within 4u max(max|want|, 1), u = 2^-8
@@ -413,6 +502,26 @@ def cpu_baseline(w, x, target_s):
         threads = 1
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
 
+    if w.kind == "mha_bwd":
+        Xq = to_f64(x["X_q"])
+        Ws = [to_f64(x[k]) for k in ("Wq", "Wk", "Wv", "Wo")]
+        dY = to_f64(x["dY"])
+
+        def run(b):
+            oracle.mha_backward_ref(Xq[:b], Xq[:b], *Ws, w.h, dY[:b], w.mask,
+                                    None if kl is None else kl[:b])
+        run(1)
+        t0 = time.perf_counter()
+        run(1)
+        t1 = max(time.perf_counter() - t0, 1e-6)
+        n = int(max(1, min(w.B, target_s / t1)))
+        t0 = time.perf_counter()
+        run(n)
+        t = time.perf_counter() - t0
+        flops = block_bwd_flops(w) / w.B * n
+        return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                    sample=f"{n} of {w.B} sequences, block backward; {t:.2f} s, numpy float64"
+                           " (algorithmic flops of the block's backward)", seconds=round(t, 3))
     if w.kind == "bwd":
         Q, K, V, dO = (to_f64(x[k]) for k in ("Q", "K", "V", "dO"))
 
@@ -522,6 +631,7 @@ KERNEL_SOURCES = {
     "embed_positional_kernel": ("embed_positional.hip", "mha_api.hip"),
     "attn_bwd_dq_kernel": ("attn_bwd_bf16.hip", "wave_attention.h", "mha_api.hip"),
     "attn_bwd_dkdv_kernel": ("attn_bwd_bf16.hip", "wave_attention.h", "mha_api.hip"),
+    "transpose_bf16_kernel": ("transpose_bf16.hip", "mha_api.hip"),
 }
 
 
@@ -716,11 +826,12 @@ def main():
              "sdpa": "bare attention",
              "embed": "token embedding x sqrt(d_model) + sinusoidal positional encoding",
              "bwd": "attention backward (dQ, dK, dV from dO, O and the row log-sum-exp)",
+             "mha_bwd": "multi-head block backward (dX, dW^Q, dW^K, dW^V, dW^O)",
              "layer": "encoder layer, Post-LN (block, residual + LayerNorm, FFN, residual + LayerNorm)"}
     cfg = dict(workload=w.name, B=w.B, n_q=w.n_q, n_k=w.n_k, h=w.h, d_k=w.d_k, d_v=w.d_v,
                mask={0: "none", 1: "causal", 2: "key_padding", 3: "causal+key_padding"}[w.mask],
                kind=kinds[w.kind], buffer_sets=sets)
-    if w.kind in ("mha", "layer"):
+    if w.kind in ("mha", "layer", "mha_bwd"):
         cfg.update(d_model=w.d_model, self_attention=w.self_attn)
     if w.kind == "layer":
         cfg.update(d_ff=w.d_ff, eps=w.eps)
@@ -763,6 +874,15 @@ def main():
     }
     if w.kind == "embed":
         out["data"] = "synthetic (seeded uniform token ids, N(0,1/d_model) embedding table)"
+    if w.kind == "mha_bwd":
+        out["data"] = "synthetic (seeded N(0,1) X and dY, N(0,1/d_model) weights)"
+        bf = block_bwd_flops(w, x["key_lengths"])
+        out["backward"] = dict(algorithmic_flops_per_step=bf,
+                               algorithmic_tflops=round(bf / (ms_step * 1e-3) / 1e12, 2),
+                               pct_of_bf16_mfma_peak=round(100 * bf / (ms_step * 1e-3) / 1e12 /
+                                                           PEAK_BF16_TFLOPS, 2),
+                               note="dX and dW of the four projections, five products per visible "
+                                    "attention pair; the transposes are copies")
     if w.kind == "bwd":
         out["data"] = "synthetic (seeded N(0,1) Q, K, V and upstream gradient dO)"
         bf = 10.0 * bwd_pairs(w, x["key_lengths"]) * w.d_k

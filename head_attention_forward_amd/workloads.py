@@ -29,7 +29,8 @@ W1 has variance 1/d_model, W2 1/d_ff; biases and LayerNorm shifts are
 that every term of the layer shows in its output).
 
 Backward pass (kind "bwd"): Q, K, V as bare attention, then the upstream
-gradient dO ~ N(0, 1), then key lengths.
+gradient dO ~ N(0, 1), then key lengths.  Block backward (kind "mha_bwd"):
+the block's inputs and weights, then dY ~ N(0, 1), then key lengths.
 
 Input embedding (kind "embed"): token ids uniform over the vocabulary, drawn
 first, then the table E [vocab][d_model] with variance 1/d_model (so that
@@ -109,6 +110,13 @@ WORKLOADS = {
         "long_causal_sdpa_bwd", "bwd", "bf16", B=4, n_q=4096, n_k=4096, h=16, d_k=64, d_v=64,
         mask=MASK_CAUSAL,
         description="attention backward (dQ, dK, dV), bf16, B=4 h=16 n=4096 d=64, causal"),
+    # The encoder block's backward pass (training): all gradients of the
+    # multi-head block for an upstream gradient dY ~ N(0, 1).
+    "encoder_self_base_bwd": Workload(
+        "encoder_self_base_bwd", "mha_bwd", "bf16", B=32, n_q=100, n_k=100, h=8, d_k=64, d_v=64,
+        mask=MASK_NONE, d_model=512, self_attn=True,
+        description="encoder self-attention block backward (dX, dW^Q, dW^K, dW^V, dW^O), bf16, "
+                    "B=32 n=100 d_model=512 h=8"),
     # One generation step of incremental decoding: each sequence's newest
     # query against its cached keys and values (cache capacity 4096, current
     # lengths in [1024, 4096]); the pages give no decoding shapes, these are
@@ -153,6 +161,7 @@ def generate(w: Workload, seed: int = 0):
     sdpa: Q [B][h][n_q][d_k], K [B][h][n_k][d_k], V [B][h][n_k][d_v], scale,
           key_lengths (int32 [B] or None).
     bwd:  as sdpa, then the upstream gradient dO [B][h][n_q][d_v].
+    mha_bwd: as mha, then the upstream gradient dY [B][n_q][d_model].
     mha:  X_q [B][n_q][d_model], X_kv (the same tensor object for
           self-attention), Wq/Wk [d_model][h*d_k], Wv [d_model][h*d_v],
           Wo [h*d_v][d_model], key_lengths.
@@ -194,7 +203,7 @@ def generate(w: Workload, seed: int = 0):
         out["b2"] = _normal(g, (D,), 0.1, dt)
         out["ln2_gamma"] = (1.0 + 0.1 * torch.randn((D,), generator=g)).to(dt)
         out["ln2_beta"] = _normal(g, (D,), 0.1, dt)
-    else:
+    else:  # "mha" and "mha_bwd"
         std = 1.0 / math.sqrt(w.d_model)
         out["X_q"] = _normal(g, (w.B, w.n_q, w.d_model), 1.0, dt)
         if w.self_attn:
@@ -207,6 +216,8 @@ def generate(w: Workload, seed: int = 0):
         out["Wk"] = _normal(g, (w.d_model, w.h * w.d_k), std, dt)
         out["Wv"] = _normal(g, (w.d_model, w.h * w.d_v), std, dt)
         out["Wo"] = _normal(g, (w.h * w.d_v, w.d_model), std, dt)
+        if w.kind == "mha_bwd":
+            out["dY"] = _normal(g, (w.B, w.n_q, w.d_model), 1.0, dt)
     if w.mask & MASK_KEY_PADDING:
         lo, hi = w.key_len_range if w.key_len_range else (1, w.n_k)
         out["key_lengths"] = torch.randint(lo, hi + 1, (w.B,), generator=g, dtype=torch.int32)
