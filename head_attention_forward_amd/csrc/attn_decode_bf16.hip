@@ -21,7 +21,8 @@
 // split only reorders the sum over keys.  (Measured on MI355X: 6% faster
 // than four waves with two slots each.)
 //
-// Grid: batch * heads workgroups; a head's K/V rows are read once.  The
+// Grid: batch * heads workgroups, longest sequences first (padded); a
+// head's K/V rows are read once.  The
 // shape is bandwidth-bound: per key 256 bytes of K and V against 4 * 64 *
 // n_q flops.
 #include "wave_attention.h"
@@ -44,9 +45,10 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_bf16_d64_kernel(const Att
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
 
-  const int bh = blockIdx.x;
-  const int b = __builtin_amdgcn_readfirstlane(bh / a.h);
-  const int hh = bh - b * a.h;
+  // Workgroups in dispatch order take the longest sequences first.
+  const int slot = __builtin_amdgcn_readfirstlane((int)blockIdx.x / a.h);
+  const int hh = (int)blockIdx.x - slot * a.h;
+  const int b = __builtin_amdgcn_readfirstlane(a.padded ? (int)a.order[slot] : slot);
   const __bf16* Qp = wave_uniform((const __bf16*)a.Q + b * a.q_sb + hh * a.q_sh);
   const char* Kp = wave_uniform((const char*)((const __bf16*)a.K + b * a.k_sb + hh * a.k_sh));
   const char* Vp = wave_uniform((const char*)((const __bf16*)a.V + b * a.v_sb + hh * a.v_sh));

@@ -28,6 +28,10 @@ struct AttnArgs {
   // ln(sum over visible keys j of exp(scale * q_i . k_j)); null: not written.
   float* lse;
   int32_t key_len[MHA_MAX_PADDED_BATCH];
+  // Batches by decreasing key length (padded only; the few-query kernel
+  // takes the longest sequences first, so the last workgroups to start are
+  // short ones).
+  uint8_t order[MHA_MAX_PADDED_BATCH];
 };
 
 // Attention backward: dQ, dK, dV of O = softmax(Q K^T * scale + M) V from

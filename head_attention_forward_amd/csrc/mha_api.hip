@@ -48,8 +48,22 @@ int check_attn_dims(int B, int h, int n_q, int n_k, int d_k, int d_v) {
 void fill_mask(AttnArgs& a, int mask_kind, const int32_t* key_lengths) {
   a.causal = (mask_kind & MHA_MASK_CAUSAL) ? 1 : 0;
   a.padded = (mask_kind & MHA_MASK_KEY_PADDING) ? 1 : 0;
-  if (a.padded)
-    for (int b = 0; b < a.B; ++b) a.key_len[b] = key_lengths[b];
+  if (a.padded) {
+    for (int b = 0; b < a.B; ++b) {
+      a.key_len[b] = key_lengths[b];
+      a.order[b] = (uint8_t)b;
+    }
+    // stable insertion sort by decreasing length (B <= 256)
+    for (int i = 1; i < a.B; ++i) {
+      const uint8_t v = a.order[i];
+      int j = i;
+      while (j > 0 && key_lengths[a.order[j - 1]] < key_lengths[v]) {
+        a.order[j] = a.order[j - 1];
+        --j;
+      }
+      a.order[j] = v;
+    }
+  }
 }
 
 struct Workspace {
