@@ -130,26 +130,27 @@ def kernel_plan(w, n_launches=None):
             raise ValueError("the block-backward bench covers self-attention")
         M, dm, hd = B * nq, w.d_model, h * dk
         pairs = bwd_pairs(w)
-
-        def tr(name, R, C):
-            plan.append(dict(name=name, flops=0.0, bytes=float(2 * e * R * C), peak_kind="hbm",
-                             has_attention=False))
-        tr("transpose_wo", hd, dm)
+        # one batched transpose: W^O, C, W^Q, W^K, W^V, X
+        plan.append(dict(name="transposes", flops=0.0, bytes=float(2 * e * (4 * hd * dm + 2 * M * dm)),
+                         peak_kind="hbm", has_attention=False))
         gemm("do_gemm", M, dm, hd)
-        tr("transpose_concat", M, hd)
-        gemm("dwo_gemm", hd, M, dm)
+        def splits(Mo, No, Ko):  # the library's split-K factor for a weight gradient
+            return 8
+
+        def reduce(name, Mo, No):  # read the fp32 partials, write the bf16 result
+            plan.append(dict(name=name, flops=0.0, bytes=float(4 * splits(Mo, No, M) * Mo * No + e * Mo * No),
+                             peak_kind="hbm", has_attention=False))
+        gemm("dwo_gemm", hd, M, dm)   # split over K: fp32 partial sums
+        reduce("dwo_reduce", hd, dm)
         plan.append(dict(name="backward_dq", flops=6.0 * pairs * dk,
                          bytes=float(e * B * h * nq * dk * 4 + 8 * B * h * nq + e * B * h * nk * dk * 2),
                          peak_kind="mfma", has_attention=False))
         plan.append(dict(name="backward_dkdv", flops=8.0 * pairs * dk,
                          bytes=float(e * B * h * nk * dk * 4 + e * B * h * nq * dk * 2 + 8 * B * h * nq),
                          peak_kind="mfma", has_attention=False))
-        tr("transpose_wq", dm, hd)
-        tr("transpose_wk", dm, hd)
-        tr("transpose_wv", dm, hd)
         gemm("dx_gemm", M, 3 * hd, dm)
-        tr("transpose_x", M, dm)
-        gemm("dw_gemm", dm, M, 3 * hd)
+        gemm("dw_gemm", dm, M, 3 * hd)  # split over K: fp32 partial sums
+        reduce("dw_reduce", dm, 3 * hd)
         return plan, None
     if w.kind == "embed":
         # gather one table row per token, write one row per token, read the ids
@@ -632,6 +633,7 @@ KERNEL_SOURCES = {
     "attn_bwd_dq_kernel": ("attn_bwd_bf16.hip", "wave_attention.h", "mha_api.hip"),
     "attn_bwd_dkdv_kernel": ("attn_bwd_bf16.hip", "wave_attention.h", "mha_api.hip"),
     "transpose_bf16_kernel": ("transpose_bf16.hip", "mha_api.hip"),
+    "gemm_splitk_reduce_kernel": ("gemm_bf16.hip", "mha_api.hip"),
 }
 
 

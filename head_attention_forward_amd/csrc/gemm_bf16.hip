@@ -111,9 +111,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
   const int N = g.col_start[g.nseg];
   const int MT = (g.M + BM - 1) / BM;
   const int NT = (N + BN - 1) / BN;
-  // XCD-aware tile order (see the file comment).
-  int tile;
-  {
+  // XCD-aware tile order (see the file comment).  Split-K launches are 1-D
+  // over (tile, split) with the split fastest: workgroups are dealt to the
+  // XCDs round-robin, so with 8 splits each XCD owns one k range of both
+  // operands for every tile, a slice its L2 holds.
+  int tile, split = 0;
+  if (g.splits > 1) {
+    tile = (int)blockIdx.x / g.splits;
+    split = (int)blockIdx.x - tile * g.splits;
+  } else {
     const int T = MT * NT;
     const int bid = blockIdx.x;
     const int x = bid % kXcds;
@@ -123,7 +129,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
   }
   const int m0 = (tile / NT) * BM;
   const int n0 = (tile % NT) * BN;
-  const int nsteps = (g.K + BK - 1) / BK;
+  // Split-K (g.splits > 1): the workgroup of split z takes k stages
+  // [s_first, s_first + nsteps) of the total and writes fp32 partial sums.
+  const int total_steps = (g.K + BK - 1) / BK;
+  int s_first = 0, nsteps = total_steps;
+  if (g.splits > 1) {
+    const int per = (total_steps + g.splits - 1) / g.splits;
+    s_first = min(split * per, total_steps);
+    nsteps = min(per, total_steps - s_first);
+  }
   const bool ktail = (g.K % BK) != 0;  // the last stage reaches past K
 
   // The tile's columns lie in one segment (segment starts are multiples of BN).
@@ -160,7 +174,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
   const unsigned as_lds = lds_addr(&As[0][0]);
   const unsigned bs_lds = lds_addr(&Bs[0][0]);
   auto issue = [&](int step, int buf) {
-    const int k0 = step * BK;
+    const int k0 = (s_first + step) * BK;
     const unsigned a_dst = as_lds + (unsigned)(buf * BM * BK + wave * AL * 512) * 2u;
     const unsigned b_dst = bs_lds + (unsigned)(buf * BK * BN + wave * BL * 512) * 2u;
     if (!ktail || k0 + BK <= g.K) {
@@ -188,7 +202,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
   // addresses past K; once it has landed, every lane clears the 16-byte
   // chunks it loaded there, so those k contribute exact zeros.
   auto zero_past_k = [&](int step, int buf) {
-    const int k0 = step * BK;
+    const int k0 = (s_first + step) * BK;
 #pragma unroll
     for (int r = 0; r < AL; ++r)
       if (k0 + a_kc[r] >= g.K) *(u32x4*)&As[buf][(wave * AL + r) * 512 + 8 * lane] = u32x4{};
@@ -260,7 +274,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
       const int t = t0 + u;
       if (t < nsteps) {
         wait_stage<LPS, NS>(min(NS - 2, nsteps - 1 - t));
-        if (ktail && t == nsteps - 1) zero_past_k(t, u);
+        if (ktail && s_first + t == total_steps - 1) zero_past_k(t, u);
         __syncthreads();
         if (t + NS - 1 < nsteps) issue(t + NS - 1, (u + NS - 1) % NS);
         compute(As[u], Bs[u]);
@@ -270,6 +284,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
 
   // acc[i][j][e] = C[m][n], m = m0 + wm*BM/2 + 32i + col,
   //                         n = n0 + wn*BN/2 + 32j + 8(e/4) + 4grp + e%4.
+  if (g.splits > 1) {  // fp32 partial sums of this k range: partial[z][m][n]
+    float* part = g.partial + (int64_t)split * g.M * N;
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int nb = n0 + wn * (BN / WN) + 32 * j;
+      if (nb >= N) continue;
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        const int m = m0 + wm * (BM / WM) + 32 * i + col;
+        if (m >= g.M) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (nb + 8 * q >= N) continue;
+          f32x4 v;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) v[r] = acc[i][j][4 * q + r];
+          *(f32x4*)(part + (int64_t)m * N + nb + 8 * q + 4 * grp) = v;
+        }
+      }
+    }
+    return;
+  }
   // A 32-column block lies in one segment and one head (segment widths and
   // head widths are multiples of 32 unless there is a single segment with a
   // single head), so its destination is fixed per block; N is a multiple of 8.
@@ -327,8 +363,36 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
   const int N = g.col_start[g.nseg];
   const int tiles = ((N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
   void* args[] = {(void*)&g};
-  return hipExtLaunchKernel((const void*)gemm_bf16_kernel<BM, BN, NS, WM, WN>, dim3(tiles),
-                            dim3(64 * WM * WN), args, 0, s, ev.start, ev.stop, 0);
+  return hipExtLaunchKernel((const void*)gemm_bf16_kernel<BM, BN, NS, WM, WN>,
+                            dim3(tiles * (g.splits > 1 ? g.splits : 1)), dim3(64 * WM * WN), args, 0, s,
+                            ev.start, ev.stop, 0);
+}
+
+// Sum of the split-K partials, rounded once to bf16 and written to the
+// segments (plain row-major outputs).  One thread per 8 columns.
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const GemmArgs g) {
+  const int N = g.col_start[g.nseg];
+  const int chunks = N / 8;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= (int64_t)g.M * chunks) return;
+  const int m = (int)(idx / chunks);
+  const int n = (int)(idx - (int64_t)m * chunks) * 8;
+  f32x4 a = {}, b = {};
+  for (int z = 0; z < g.splits; ++z) {
+    const float* p = g.partial + ((int64_t)z * g.M + m) * N + n;
+    a += *(const f32x4*)p;
+    b += *(const f32x4*)(p + 4);
+  }
+  f32x8 v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    v[r] = a[r];
+    v[4 + r] = b[r];
+  }
+  const int sg = seg_of(g, n);
+  const int width = seg_field(g, sg, &GemmSeg::width);
+  __bf16* dst = (__bf16*)seg_field(g, sg, &GemmSeg::dst) + (int64_t)m * width + (n - seg_start(g, sg));
+  *(bf16x8*)dst = __builtin_convertvector(v, bf16x8);
 }
 
 // Every segment must start on a multiple of the tile width (a tile's columns
@@ -359,6 +423,22 @@ hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, Launc
     case 11: return launch_tile<64, 128, 2, 2, 4>(g, s, ev);
     default: return launch_tile<128, 64, 2, 4, 2>(g, s, ev);
   }
+}
+
+hipError_t launch_gemm_bf16_splitk(const GemmArgs& g, hipStream_t s, LaunchEvents ev_gemm,
+                                   LaunchEvents ev_reduce) {
+  // 64 x 64 tiles, 3-stage ring: the split-K shapes are small outputs.
+  if (g.splits < 2 || g.partial == nullptr || g.bias != nullptr || g.relu || !tiles_fit(g, 64))
+    return hipErrorInvalidValue;
+  for (int sg = 0; sg < g.nseg; ++sg)
+    if (g.seg[sg].heads != 1 || g.seg[sg].width % 8 != 0) return hipErrorInvalidValue;
+  hipError_t e = launch_tile<64, 64, 3>(g, s, ev_gemm);
+  if (e != hipSuccess) return e;
+  const int N = g.col_start[g.nseg];
+  const int64_t threads = (int64_t)g.M * (N / 8);
+  void* args[] = {(void*)&g};
+  return hipExtLaunchKernel((const void*)gemm_splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)),
+                            dim3(256), args, 0, s, ev_reduce.start, ev_reduce.stop, 0);
 }
 
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {

@@ -88,6 +88,11 @@ struct GemmArgs {
   // added to every row before rounding, then max(0, .) when relu != 0.
   const void* bias;
   int relu;
+  // Split-K (launch_gemm_bf16_splitk only): the k stages are shared out over
+  // `splits` workgroups per tile, each writing fp32 partial sums
+  // partial[z][M][N]; a second kernel adds them and rounds once.
+  int splits;
+  float* partial;
 };
 
 // Residual + LayerNorm over rows of d features (bf16):
@@ -145,12 +150,23 @@ hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents e
 hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev = {});
+hipError_t launch_gemm_bf16_splitk(const GemmArgs& g, hipStream_t s, LaunchEvents ev_gemm = {},
+                                   LaunchEvents ev_reduce = {});
 // Backward: the dQ kernel (also writes Dw), then the dK/dV kernel (reads Dw).
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_add_layernorm_bf16(const LnArgs& a, hipStream_t s, LaunchEvents ev = {});
-// dst[c][r] = src[r][c] for a dense bf16 [R][C] matrix (R, C multiples of 8).
-hipError_t launch_transpose_bf16(const void* src, void* dst, int R, int C, hipStream_t s, LaunchEvents ev = {});
+// dst_i[c][r] = src_i[r][c] for up to eight dense bf16 [R_i][C_i] matrices
+// in one launch (R_i, C_i multiples of 8).
+constexpr int kMaxTransposeBatch = 8;
+struct TransposeBatch {
+  const void* src[kMaxTransposeBatch];
+  void* dst[kMaxTransposeBatch];
+  int R[kMaxTransposeBatch];
+  int C[kMaxTransposeBatch];
+  int n;
+};
+hipError_t launch_transpose_bf16(const TransposeBatch& tb, hipStream_t s, LaunchEvents ev = {});
 // f32 != 0: E and out are fp32, else bf16.
 hipError_t launch_embed_positional(const EmbedArgs& a, int f32, hipStream_t s, LaunchEvents ev = {});
 bool proj_attn_supported(int n_q, int n_k, int d_model);

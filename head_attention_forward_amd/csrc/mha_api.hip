@@ -341,9 +341,15 @@ struct BwdWs {
   void* WkvT;   // cross: [2hd][d_model]
   void* XqT;    // [d_model][M_q]
   void* XkvT;   // cross: [d_model][M_k]
+  float* partial;  // split-K partial sums of the weight-gradient GEMMs
   size_t rows_each;
   size_t bytes;
 };
+
+// Split-K factor of a weight-gradient GEMM (small output, depth K = rows):
+// one k range per XCD (the GEMM deals the splits to the 8 XCDs, so each L2
+// holds one slice of both operands).
+int wgrad_splits(int, int, int) { return 8; }
 
 BwdWs carve_bwd(void* base, bool self_attn, int B, int n_q, int n_k, int d_model, int h, int d) {
   BwdWs w{};
@@ -358,6 +364,17 @@ BwdWs carve_bwd(void* base, bool self_attn, int B, int n_q, int n_k, int d_model
   w.dO = take(2 * Mq * hd);
   w.OcT = take(2 * hd * Mq);
   w.rows_each = round_up((size_t)4 * B * h * n_q);
+  {
+    // the largest of the weight-gradient GEMMs' partial sums
+    size_t part = (size_t)wgrad_splits((int)hd, d_model, (int)Mq) * hd * dm;
+    if (self_attn) {
+      part = max(part, (size_t)wgrad_splits(d_model, 3 * (int)hd, (int)Mq) * dm * 3 * hd);
+    } else {
+      part = max(part, (size_t)wgrad_splits(d_model, (int)hd, (int)Mq) * dm * hd);
+      part = max(part, (size_t)wgrad_splits(d_model, 2 * (int)hd, (int)Mk) * dm * 2 * hd);
+    }
+    w.partial = (float*)take(4 * part);
+  }
   if (self_attn) {
     w.dQKV = take(2 * Mq * 3 * hd);
     w.rows = (float*)take(2 * w.rows_each);
@@ -378,8 +395,9 @@ BwdWs carve_bwd(void* base, bool self_attn, int B, int n_q, int n_k, int d_model
 
 // C = A . [segments], A [M][K] row-major; each segment a row-major weight
 // (row stride ldw) written as a plain row-major [M][width] matrix.
+// partial != null: split-K (a weight gradient: small output, K = rows).
 int do_gemm_rm(const void* A, int M, int K, int nseg, const void* const* W, void* const* dst,
-               const int* width, int ldw, hipStream_t stream, Timer* tm) {
+               const int* width, int ldw, hipStream_t stream, Timer* tm, float* partial = nullptr) {
   GemmArgs g{};
   g.A = A;
   g.M = M;
@@ -392,14 +410,32 @@ int do_gemm_rm(const void* A, int M, int K, int nseg, const void* const* W, void
     c += width[s];
   }
   g.col_start[nseg] = c;
+  if (partial != nullptr) {
+    g.splits = wgrad_splits(M, c, K);
+    g.partial = partial;
+    const LaunchEvents e1 = next_events(tm);
+    const LaunchEvents e2 = next_events(tm);
+    return launch_status(launch_gemm_bf16_splitk(g, stream, e1, e2));
+  }
   return launch_status(launch_gemm_bf16(g, stream, next_events(tm)));
 }
 
-int do_transpose(const void* src, void* dst, int R, int C, hipStream_t stream, Timer* tm) {
-  return launch_status(launch_transpose_bf16(src, dst, R, C, stream, next_events(tm)));
-}
+// One batched transpose launch.
+struct Transposes {
+  TransposeBatch tb{};
+  void add(const void* src, void* dst, int R, int C) {
+    tb.src[tb.n] = src;
+    tb.dst[tb.n] = dst;
+    tb.R[tb.n] = R;
+    tb.C[tb.n] = C;
+    ++tb.n;
+  }
+  int launch(hipStream_t stream, Timer* tm) const {
+    return launch_status(launch_transpose_bf16(tb, stream, next_events(tm)));
+  }
+};
 
-int mha_bwd_launch_count(bool self_attn) { return self_attn ? 12 : 15; }
+int mha_bwd_launch_count(bool self_attn) { return self_attn ? 9 : 12; }
 
 }  // namespace
 }  // namespace mha
@@ -913,9 +949,29 @@ static int mha_bwd_impl(const void* X_q, const void* X_kv, const void* Wq, const
   const TrainWs t = carve_train((void*)train_ws, B, n_q, n_k, h, d_k, d_v);
   const BwdWs w = carve_bwd(workspace, self_attn, B, n_q, n_k, d_model, h, d_k);
   const int hd = h * d_k, dm = d_model;
+  const size_t wblock = (size_t)hd * dm;  // elements of one transposed weight
+  // Every transposed operand in one launch: W^O^T, C^T, the input weights'
+  // transposes (stacked for self-attention) and the inputs' transposes.
+  {
+    Transposes tr;
+    tr.add(Wo, w.WoT, hd, dm);
+    tr.add(t.blk.O, w.OcT, (int)Mq, hd);
+    if (self_attn) {
+      tr.add(Wq, w.WT, dm, hd);
+      tr.add(Wk, (__bf16*)w.WT + wblock, dm, hd);
+      tr.add(Wv, (__bf16*)w.WT + 2 * wblock, dm, hd);
+      tr.add(X_q, w.XqT, (int)Mq, dm);
+    } else {
+      tr.add(Wq, w.WT, dm, hd);
+      tr.add(Wk, w.WkvT, dm, hd);
+      tr.add(Wv, (__bf16*)w.WkvT + wblock, dm, hd);
+      tr.add(X_q, w.XqT, (int)Mq, dm);
+      tr.add(X_kv, w.XkvT, (int)Mk, dm);
+    }
+    st = tr.launch(stream, tm);
+    if (st != MHA_OK) return st;
+  }
   // dC = dY W^O^T, scattered per head into dO [B][h][n_q][d]
-  st = do_transpose(Wo, w.WoT, hd, dm, stream, tm);
-  if (st != MHA_OK) return st;
   {
     GemmArgs g{};
     g.A = dY;
@@ -929,13 +985,11 @@ static int mha_bwd_impl(const void* X_q, const void* X_kv, const void* Wq, const
     if (st != MHA_OK) return st;
   }
   // dW^O = C^T dY
-  st = do_transpose(t.blk.O, w.OcT, (int)Mq, hd, stream, tm);
-  if (st != MHA_OK) return st;
   {
     const void* W[1] = {dY};
     void* D[1] = {dWo};
     const int wd[1] = {dm};
-    st = do_gemm_rm(w.OcT, hd, (int)Mq, 1, W, D, wd, 0, stream, tm);
+    st = do_gemm_rm(w.OcT, hd, (int)Mq, 1, W, D, wd, 0, stream, tm, w.partial);
     if (st != MHA_OK) return st;
   }
   // attention gradients, written with the heads concatenated
@@ -981,31 +1035,20 @@ static int mha_bwd_impl(const void* X_q, const void* X_kv, const void* Wq, const
     st = launch_status(launch_attn_bwd_dkdv(a, stream, next_events(tm)));
     if (st != MHA_OK) return st;
   }
-  const size_t wblock = (size_t)hd * dm;  // elements of one transposed weight
   if (self_attn) {
     // dX = [dQ | dK | dV] [W^Q | W^K | W^V]^T
-    st = do_transpose(Wq, w.WT, dm, hd, stream, tm);
-    if (st == MHA_OK) st = do_transpose(Wk, (__bf16*)w.WT + wblock, dm, hd, stream, tm);
-    if (st == MHA_OK) st = do_transpose(Wv, (__bf16*)w.WT + 2 * wblock, dm, hd, stream, tm);
-    if (st != MHA_OK) return st;
     const void* W[1] = {w.WT};
     void* D[1] = {dX_q};
     const int wd[1] = {dm};
     st = do_gemm_rm(w.dQKV, (int)Mq, 3 * hd, 1, W, D, wd, 0, stream, tm);
     if (st != MHA_OK) return st;
     // [dW^Q | dW^K | dW^V] = X^T [dQ | dK | dV]
-    st = do_transpose(X_q, w.XqT, (int)Mq, dm, stream, tm);
-    if (st != MHA_OK) return st;
     const void* W3[3] = {w.dQKV, (__bf16*)w.dQKV + hd, (__bf16*)w.dQKV + 2 * hd};
     void* D3[3] = {dWq, dWk, dWv};
     const int wd3[3] = {hd, hd, hd};
-    return do_gemm_rm(w.XqT, dm, (int)Mq, 3, W3, D3, wd3, 3 * hd, stream, tm);
+    return do_gemm_rm(w.XqT, dm, (int)Mq, 3, W3, D3, wd3, 3 * hd, stream, tm, w.partial);
   }
   // cross-attention: dX_q = dQ W^Q^T, dX_kv = [dK | dV] [W^K | W^V]^T
-  st = do_transpose(Wq, w.WT, dm, hd, stream, tm);
-  if (st == MHA_OK) st = do_transpose(Wk, w.WkvT, dm, hd, stream, tm);
-  if (st == MHA_OK) st = do_transpose(Wv, (__bf16*)w.WkvT + wblock, dm, hd, stream, tm);
-  if (st != MHA_OK) return st;
   {
     const void* W[1] = {w.WT};
     void* D[1] = {dX_q};
@@ -1018,19 +1061,16 @@ static int mha_bwd_impl(const void* X_q, const void* X_kv, const void* Wq, const
     if (st != MHA_OK) return st;
   }
   // dW^Q = X_q^T dQ, [dW^K | dW^V] = X_kv^T [dK | dV]
-  st = do_transpose(X_q, w.XqT, (int)Mq, dm, stream, tm);
-  if (st == MHA_OK) st = do_transpose(X_kv, w.XkvT, (int)Mk, dm, stream, tm);
-  if (st != MHA_OK) return st;
   {
     const void* W[1] = {w.dQKV};
     void* D[1] = {dWq};
     const int wd[1] = {hd};
-    st = do_gemm_rm(w.XqT, dm, (int)Mq, 1, W, D, wd, 0, stream, tm);
+    st = do_gemm_rm(w.XqT, dm, (int)Mq, 1, W, D, wd, 0, stream, tm, w.partial);
     if (st != MHA_OK) return st;
     const void* W2[2] = {w.dKV, (__bf16*)w.dKV + hd};
     void* D2[2] = {dWk, dWv};
     const int wd2[2] = {hd, hd};
-    return do_gemm_rm(w.XkvT, dm, (int)Mk, 2, W2, D2, wd2, 2 * hd, stream, tm);
+    return do_gemm_rm(w.XkvT, dm, (int)Mk, 2, W2, D2, wd2, 2 * hd, stream, tm, w.partial);
   }
 }
 

@@ -3,10 +3,11 @@
 // the projection GEMM (dW = X^T dY, dX = dY W^T); this kernel materialises
 // them.
 //
-// One workgroup per 64 x 64 tile: 256 threads read the tile as 16-byte row
-// chunks (rows 32 apart per thread), store it in LDS with the row padded by
-// one element pair, and write the transposed tile as 16-byte chunks of
-// eight consecutive source rows.  Bandwidth-bound; R and C multiples of 8.
+// Up to eight matrices per launch (grid.z).  One workgroup per 64 x 64
+// tile: 256 threads read the tile as 16-byte row chunks (rows 32 apart per
+// thread), store it in LDS with the row padded by one element pair, and
+// write the transposed tile as 16-byte chunks of eight consecutive source
+// rows.  Bandwidth-bound; R and C multiples of 8.
 #include "device.h"
 
 namespace mha {
@@ -17,11 +18,28 @@ using namespace dev;
 constexpr int TB = 64;          // tile rows and columns
 constexpr int LD = TB + 2;      // LDS row length (elements): 132 bytes, odd word count
 
-__global__ __launch_bounds__(256) void transpose_bf16_kernel(const __bf16* __restrict__ src,
-                                                             __bf16* __restrict__ dst, int R, int C) {
+// Matrix z of a batched launch: blockIdx.z selects it (by selects on the
+// uniform z, so the argument block is never indexed dynamically); workgroups
+// past its tiles return at once (the grid covers the largest matrix).
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const TransposeBatch tb) {
   __shared__ __bf16 t[TB * LD];
+  const int z = blockIdx.z;
+  const void* sp = tb.src[0];
+  void* dp = tb.dst[0];
+  int R = tb.R[0], C = tb.C[0];
+#pragma unroll
+  for (int i = 1; i < kMaxTransposeBatch; ++i)
+    if (z == i) {
+      sp = tb.src[i];
+      dp = tb.dst[i];
+      R = tb.R[i];
+      C = tb.C[i];
+    }
+  const __bf16* __restrict__ src = (const __bf16*)sp;
+  __bf16* __restrict__ dst = (__bf16*)dp;
   const int tid = threadIdx.x;
   const int r0 = blockIdx.y * TB, c0 = blockIdx.x * TB;
+  if (r0 >= R || c0 >= C) return;  // whole workgroup: no barrier is skipped by part of it
   const int cc = (tid & 7) * 8;  // chunk column within the tile
   // read: thread covers rows (tid >> 3) and (tid >> 3) + 32, 8 columns each
 #pragma unroll
@@ -49,13 +67,17 @@ __global__ __launch_bounds__(256) void transpose_bf16_kernel(const __bf16* __res
 
 }  // namespace
 
-hipError_t launch_transpose_bf16(const void* src, void* dst, int R, int C, hipStream_t s, LaunchEvents ev) {
-  if (R <= 0 || C <= 0 || R % 8 != 0 || C % 8 != 0) return hipErrorInvalidValue;
-  const __bf16* sp = (const __bf16*)src;
-  __bf16* dp = (__bf16*)dst;
-  void* args[] = {(void*)&sp, (void*)&dp, (void*)&R, (void*)&C};
-  dim3 grid((C + TB - 1) / TB, (R + TB - 1) / TB);
+hipError_t launch_transpose_bf16(const TransposeBatch& tb, hipStream_t s, LaunchEvents ev) {
+  if (tb.n < 1 || tb.n > kMaxTransposeBatch) return hipErrorInvalidValue;
+  int maxR = 0, maxC = 0;
+  for (int i = 0; i < tb.n; ++i) {
+    if (tb.R[i] <= 0 || tb.C[i] <= 0 || tb.R[i] % 8 != 0 || tb.C[i] % 8 != 0) return hipErrorInvalidValue;
+    maxR = max(maxR, tb.R[i]);
+    maxC = max(maxC, tb.C[i]);
+  }
+  dim3 grid((maxC + TB - 1) / TB, (maxR + TB - 1) / TB, tb.n);
   if (grid.y > 65535) return hipErrorInvalidValue;
+  void* args[] = {(void*)&tb};
   return hipExtLaunchKernel((const void*)transpose_bf16_kernel, grid, dim3(256), args, 0, s, ev.start,
                             ev.stop, 0);
 }

@@ -347,11 +347,13 @@ size_t mha_backward_workspace_bytes(int B, int n_q, int n_k, int d_model, int h,
  *   workspace >= mha_backward_workspace_bytes(...), 256-byte aligned.
  *   B*n_q and B*n_k must be multiples of 8 (MHA_ERR_UNSUPPORTED): the
  *   transposed activations are GEMM operands of that width.
- * Launches (mha_backward_launches): transposes of W^O, C, the stacked input
- * weights and the inputs (bandwidth-bound copies that let the projection
- * GEMM take every product as A . B with row-major operands), four or six
- * GEMMs and the two attention-backward kernels.  bf16 in and out, fp32
- * accumulation.
+ * Launches (mha_backward_launches): one batched transpose of W^O, C, the
+ * input weights (stacked for self-attention) and the inputs (bandwidth-bound
+ * copies that let the projection GEMM take every product as A . B with
+ * row-major operands), the GEMMs for dC and dX, the weight-gradient GEMMs
+ * split over K (fp32 partial sums in the workspace, then one kernel that
+ * adds them and rounds once), and the two attention-backward kernels.
+ * bf16 in and out, fp32 accumulation.
  */
 int mha_backward(const void* X_q, const void* X_kv,
                  const void* Wq, const void* Wk, const void* Wv, const void* Wo,
@@ -373,8 +375,8 @@ int mha_backward_timed(const void* X_q, const void* X_kv,
                        void* workspace, size_t workspace_bytes, hipStream_t stream,
                        hipEvent_t* events, int capacity, int* n_launches);
 
-/* mha_backward_launches -- kernels mha_backward launches: 12 for
- * self-attention, 15 for cross-attention.  Host-only. */
+/* mha_backward_launches -- kernels mha_backward launches: 9 for
+ * self-attention, 12 for cross-attention.  Host-only. */
 int mha_backward_launches(int self_attention);
 
 /*
