@@ -100,6 +100,14 @@ WORKLOADS = {
         mask=MASK_KEY_PADDING, d_model=1024, self_attn=False, key_len_range=(64, 128),
         description="cross-attention block, bf16, B=32 n_q=96 n_k=128 d_model=1024 h=16, "
                     "key padding with lengths in [64,128]"),
+    # The encoder block's attention alone (the staged path's middle stage):
+    # per (batch, head) 100 queries over 100 keys, moving Q, K, V and O
+    # through HBM -- the short, bandwidth-bound attention shape.
+    "encoder_self_base_sdpa": Workload(
+        "encoder_self_base_sdpa", "sdpa", "bf16", B=32, n_q=100, n_k=100, h=8, d_k=64, d_v=64,
+        mask=MASK_NONE,
+        description="bare attention at the encoder block's shape, bf16, B=32 h=8 n=100 d=64, "
+                    "unmasked"),
     "long_causal_sdpa": Workload(
         "long_causal_sdpa", "sdpa", "bf16", B=4, n_q=4096, n_k=4096, h=16, d_k=64, d_v=64,
         mask=MASK_CAUSAL,

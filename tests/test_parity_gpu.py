@@ -172,6 +172,12 @@ EDGE = [
     (4, 2, 96, 128, 2, [1, 64, 127, 128]),
     (3, 1, 130, 130, 3, [1, 65, 130]),
     (2, 2, 257, 257, 3, [200, 257]),
+    # key ranges of at most 128 (at most two key tiles)
+    (2, 2, 300, 96, 0, None),         # three query tiles over 96 keys
+    (3, 2, 40, 33, 0, None),          # the second key group holds one key
+    (1, 2, 129, 1, 0, None),          # one key, two query tiles
+    (2, 2, 130, 128, 2, [128, 31]),
+    (2, 1, 100, 100, 3, [1, 100]),    # causal + padding, one visible key in batch 0
 ]
 
 
@@ -355,6 +361,50 @@ def test_deterministic_and_in_bounds(dev):
     torch.cuda.synchronize()
     assert torch.equal(first, out)
     assert bool((buf[:pad] == -12345.0).all()) and bool((buf[pad + numel:] == -12345.0).all())
+
+
+def test_short_key_ranges_masking_saturation_canary(dev):
+    """Key ranges of at most 128 keys (at most two key tiles):
+    hidden keys have exactly zero weight, large scores stay accurate, two
+    runs agree bit for bit and nothing is written past the output."""
+    B, h, n = 2, 2, 100
+    Q, K, V = sdpa_inputs(B, h, n, n, torch.bfloat16, seed=12)
+    announce("short causal perturbation")
+    O = run_sdpa(dev, Q, K, V, 0.125, 1, None).cpu()
+    for i in (0, 31, 32, 63, 95):
+        K2, V2 = K.clone(), V.clone()
+        K2[:, :, i + 1:] = K2[:, :, i + 1:] * -7
+        V2[:, :, i + 1:] = V2[:, :, i + 1:] * 5 + 3
+        O2 = run_sdpa(dev, Q, K2, V2, 0.125, 1, None).cpu()
+        assert torch.equal(O2[:, :, : i + 1], O[:, :, : i + 1]), i
+    announce("short padding perturbation")
+    kl = [37, 100]
+    O = run_sdpa(dev, Q, K, V, 0.125, 2, kl).cpu()
+    K2, V2 = K.clone(), V.clone()
+    K2[0, :, 37:] = 50.0
+    V2[0, :, 37:] = -80.0
+    assert torch.equal(O, run_sdpa(dev, Q, K2, V2, 0.125, 2, kl).cpu())
+    announce("short saturated")
+    Qs, Ks, Vs = sdpa_inputs(2, 2, 120, 120, torch.bfloat16, seed=4, q_scale=30.0)
+    for mask in (0, 1):
+        Os = run_sdpa(dev, Qs, Ks, Vs, 0.125, mask, None)
+        torch.cuda.synchronize()
+        assert_bf16_close(Os, ref_sdpa(Qs, Ks, Vs, 0.125, mask, None), f"short saturated mask {mask}")
+    announce("short determinism + canary")
+    B, h, n_q, n_k = 3, 2, 131, 100
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.bfloat16, seed=6)
+    Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
+    numel = B * h * n_q * 64
+    pad = 4096
+    buf = torch.full((numel + 2 * pad,), -12345.0, dtype=torch.bfloat16, device=dev)
+    out = buf[pad:pad + numel].view(B, h, n_q, 64)
+    hafa.sdpa_forward(Qd, Kd, Vd, 0.125, 2, [100, 17, 64], out=out)
+    first = out.clone()
+    hafa.sdpa_forward(Qd, Kd, Vd, 0.125, 2, [100, 17, 64], out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out)
+    assert bool((buf[:pad] == -12345.0).all()) and bool((buf[pad + numel:] == -12345.0).all())
+    assert_bf16_close(out, ref_sdpa(Q, K, V, 0.125, 2, [100, 17, 64]), "short padding, two query tiles")
 
 
 def test_mha_small_shapes(dev):
