@@ -11,9 +11,9 @@
 // walks every key tile alone.  Here the eight waves of a workgroup split the
 // keys instead: wave w takes key tiles w, w + 8, w + 16, ... and streams
 // them through its own 16 KB LDS slot (it issues, waits for and reads its own
-// copies -- the next tile's copies go out as soon as the current one has
-// been read -- so the loop has no workgroup barrier; two waves per SIMD
-// cover each other's waits).  Each wave ends with a partial state of the
+// copies, so the loop has no workgroup barrier).  A wave reads its tile out
+// of the slot into registers and issues the next tile's copy before it
+// multiplies, so a copy is in flight while it computes.  Each wave ends with a partial state of the
 // softmax over its keys -- a reference value m, a sum l and an accumulator --
 // for the same 32 query rows; the eight are merged as one streaming step
 // would merge them (common reference m* = max m_w; l and the accumulator
@@ -104,10 +104,14 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_bf16_d64_kernel(const Att
   for (int t = wave; t < ntiles; t += NW) {
     wait_vmcnt<0>();
     const __bf16* ks = &ring[wave][0];
-    wa.tile(ks, ks + KT * D, t * KT, L, L);
-    // every read of the slot has been consumed by the tile's products; the
-    // copy (after the tile in program order) may overwrite it
+    // The tile moves into registers; once those reads have returned, the
+    // slot takes the next tile's copy, which is in flight while this tile
+    // is multiplied.
+    WaveAttention::TileRegs r;
+    wa.read_tile(ks, ks + KT * D, r);
+    wait_lgkmcnt0();
     if (t + NW < ntiles) issue(t + NW);
+    wa.tile_regs(r, t * KT, L, L);
   }
   wait_vmcnt<0>();
   __syncthreads();  // every wave is done with its ring

@@ -30,6 +30,9 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// s_waitcnt lgkmcnt(0): every LDS read this wave issued has returned its data.
+__device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14)); }
+
 // 16-byte global -> LDS copy per lane from a wave-uniform 64-bit base plus a
 // per-lane 32-bit byte offset (no vector address arithmetic); lane l writes
 // LDS byte address lds + 16 l.  Inline assembly, so that the compiler does

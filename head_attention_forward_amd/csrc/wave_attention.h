@@ -219,6 +219,62 @@ struct WaveAttention {
     pv_half(vs, 1, p[2], p[3]);
   }
 
+  // ---- a tile held in registers ------------------------------------------
+  // The operands of one 64-key tile, read out of LDS in one go, so that the
+  // LDS slot can take the next tile's copy while this one is multiplied.
+  struct TileRegs {
+    bf16x8 k[8];  // K operand: key blocks 0..3 of the first 32 keys, then of the second
+    bf16x8 v[8];  // V^T operand of key block kk (0..3) and d block db at 2 kk + db
+  };
+  __device__ __forceinline__ void read_tile(const __bf16* ks, const __bf16* vs, TileRegs& r) const {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      r.k[kk] = *(const bf16x8*)&ks[kx[kk]];
+      r.k[4 + kk] = *(const bf16x8*)&ks[kx[kk] + 32 * D];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int db = 0; db < 2; ++db) {
+        const i16x4 lo = tr_read(&vs[vx[db] + 16 * kk * D]);
+        const i16x4 hi = tr_read(&vs[vx[db] + (16 * kk + 8) * D]);
+        r.v[2 * kk + db] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+  }
+  // tile() on a tile held in registers (same products, same order).
+  __device__ __forceinline__ void tile_regs(const TileRegs& r, int k0, int lim, int lim_min) {
+    f32x16 s0 = {}, s1 = {};
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.k[0], qf[0], s0, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.k[1], qf[1], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.k[4], qf[0], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.k[2], qf[2], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.k[5], qf[1], s1, 0, 0, 0);
+    s0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.k[3], qf[3], s0, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.k[6], qf[2], s1, 0, 0, 0);
+    s1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.k[7], qf[3], s1, 0, 0, 0);
+    if (k0 + KT > lim_min) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 8 * (i >> 2) + 4 * g + (i & 3);
+        if (key >= lim) s0[i] = -INFINITY;
+        if (key + 32 >= lim) s1[i] = -INFINITY;
+      }
+    }
+    bf16x8 p[4];
+    half(s0, p[0], p[1]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.v[2 * j], p[j], o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.v[2 * j + 1], p[j], o1, 0, 0, 0);
+    }
+    half(s1, p[2], p[3]);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      o0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.v[4 + 2 * j], p[2 + j], o0, 0, 0, 0);
+      o1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(r.v[4 + 2 * j + 1], p[2 + j], o1, 0, 0, 0);
+    }
+  }
+
   // 1 / (row sum of weights); a cross-lane exchange: call with all lanes active.
   __device__ __forceinline__ float inv_sum() const { return 1.f / sum_halves(l); }
 
