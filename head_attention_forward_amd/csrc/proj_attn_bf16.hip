@@ -162,11 +162,11 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
   const int tr_k = (lane & 15) >> 2;
   const int tr_n = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
 
-  auto compute = [&](const __bf16* st) {
+  auto compute = [&](const __bf16* st, const int ks_lo, const int ks_hi) {
     const __bf16* xs_q = st;
     const __bf16* xs_kv = CROSS ? st + XT : st;
 #pragma unroll
-    for (int ks = 0; ks < BKP / 16; ++ks) {
+    for (int ks = ks_lo; ks < ks_hi; ++ks) {
       const int xo = xrow * BKP + 8 * x_pos(xrow, 2 * ks + grp);
       const bf16x8 fq = *(const bf16x8*)&xs_q[xo];
       const bf16x8 fkv = CROSS ? *(const bf16x8*)&xs_kv[xo] : fq;
@@ -187,11 +187,19 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nsteps) issue(s, s);
+  // The copies of a stage are issued by half of the waves (0-3) before the
+  // stage's products and by the other half (4-7, the second wave of each
+  // SIMD) halfway through them, so that the address unit drains one half's
+  // copies while the other half multiplies.
   for (int t = 0; t < nsteps; ++t) {
     wait_stage<NS, LPS>(min(NS - 2, nsteps - 1 - t));
     __syncthreads();
-    if (t + NS - 1 < nsteps) issue(t + NS - 1, (t + NS - 1) % NS);
-    compute(&ring[(t % NS) * STAGE]);
+    const bool more = t + NS - 1 < nsteps;
+    const __bf16* st = &ring[(t % NS) * STAGE];
+    if (more && wave < 4) issue(t + NS - 1, (t + NS - 1) % NS);
+    compute(st, 0, BKP / 32);
+    if (more && wave >= 4) issue(t + NS - 1, (t + NS - 1) % NS);
+    compute(st, BKP / 32, BKP / 16);
   }
   wait_vmcnt<0>();
   __syncthreads();  // every wave is done with the ring
