@@ -103,9 +103,9 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
       for (int r = 0; r < CHW; ++r) {
         int row, kc, vc;
         chunk_of(r, row, kc, vc);
-        const int key = min(k0 + row, a.n_k - 1);
-        dma16_s(Kp, (unsigned)(key * a.k_sr + kc) * 2u, kd + 1024u * r);
-        dma16_s(Vp, (unsigned)(key * a.v_sr + vc) * 2u, vd + 1024u * r);
+        const int rr = min(row, a.n_k - 1 - k0);  // offsets from the tile's own row
+        dma16_s(kb, (unsigned)(rr * a.k_sr + kc) * 2u, kd + 1024u * r);
+        dma16_s(vb, (unsigned)(rr * a.v_sr + vc) * 2u, vd + 1024u * r);
       }
     }
     kb += kstep;

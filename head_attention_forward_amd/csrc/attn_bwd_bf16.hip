@@ -199,15 +199,18 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
   const unsigned ks_lds = lds_addr(&Ks[0][0]), kt_lds = lds_addr(&Kt[0][0]), vs_lds = lds_addr(&Vs[0][0]);
   auto issue = [&](int tile, int buf) {
     const int k0 = tile * BT;
+    // 64-bit base of the tile's first row; per-lane offsets stay small
+    const char* kb = wave_uniform(Kp + (int64_t)k0 * D * 2);
+    const char* vb = wave_uniform(Vp + (int64_t)k0 * D * 2);
 #pragma unroll
     for (int r = 0; r < CHW; ++r) {
       int row, kc, vc;
       swz((wave * CHW + r) * 64 + lane, row, kc, vc);
-      const int key = min(k0 + row, a.n_k - 1);  // rows past n_k repeat the last (masked)
+      const int rr = min(row, a.n_k - 1 - k0);  // rows past n_k repeat the last (masked)
       const unsigned dst = (unsigned)(buf * BT * D * 2 + (wave * CHW + r) * 1024);
-      dma16_s(Kp, (unsigned)(key * D + kc) * 2u, ks_lds + dst);
-      dma16_s(Kp, (unsigned)(key * D + vc) * 2u, kt_lds + dst);
-      dma16_s(Vp, (unsigned)(key * D + kc) * 2u, vs_lds + dst);
+      dma16_s(kb, (unsigned)(rr * D + kc) * 2u, ks_lds + dst);
+      dma16_s(kb, (unsigned)(rr * D + vc) * 2u, kt_lds + dst);
+      dma16_s(vb, (unsigned)(rr * D + kc) * 2u, vs_lds + dst);
     }
   };
 
@@ -309,21 +312,24 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
   const char* Dp = wave_uniform((const char*)(a.Dw + (int64_t)bh * a.n_q));
   auto issue = [&](int tile, int buf) {
     const int q0 = tile * BT;
+    // 64-bit bases of the tile's first row; per-lane offsets stay small
+    const char* qb = wave_uniform(Qp + (int64_t)q0 * D * 2);
+    const char* ob = wave_uniform(dOp + (int64_t)q0 * D * 2);
 #pragma unroll
     for (int r = 0; r < CHW; ++r) {
       int row, kc, vc;
       swz((wave * CHW + r) * 64 + lane, row, kc, vc);
-      const int q = min(q0 + row, a.n_q - 1);  // rows past n_q repeat the last (masked)
+      const int rr = min(row, a.n_q - 1 - q0);  // rows past n_q repeat the last (masked)
       const unsigned dst = (unsigned)(buf * BT * D * 2 + (wave * CHW + r) * 1024);
-      dma16_s(Qp, (unsigned)(q * D + kc) * 2u, qs_lds + dst);
-      dma16_s(Qp, (unsigned)(q * D + vc) * 2u, qt_lds + dst);
-      dma16_s(dOp, (unsigned)(q * D + kc) * 2u, os_lds + dst);
-      dma16_s(dOp, (unsigned)(q * D + vc) * 2u, ot_lds + dst);
+      dma16_s(qb, (unsigned)(rr * D + kc) * 2u, qs_lds + dst);
+      dma16_s(qb, (unsigned)(rr * D + vc) * 2u, qt_lds + dst);
+      dma16_s(ob, (unsigned)(rr * D + kc) * 2u, os_lds + dst);
+      dma16_s(ob, (unsigned)(rr * D + vc) * 2u, ot_lds + dst);
     }
     // -lse/scale and -D of the tile's 64 queries: one 4-byte copy per lane
-    const unsigned qo = (unsigned)min(q0 + lane, a.n_q - 1) * 4u;
-    if (wave == 0) dma4_s(Lp, qo, ls_lds + (unsigned)(buf * BT * 4));
-    if (wave == 1) dma4_s(Dp, qo, ds_lds + (unsigned)(buf * BT * 4));
+    const unsigned qo = (unsigned)min(lane, a.n_q - 1 - q0) * 4u;
+    if (wave == 0) dma4_s(Lp + (int64_t)q0 * 4, qo, ls_lds + (unsigned)(buf * BT * 4));
+    if (wave == 1) dma4_s(Dp + (int64_t)q0 * 4, qo, ds_lds + (unsigned)(buf * BT * 4));
   };
 
   f32x16 dk0 = {}, dk1 = {}, dv0 = {}, dv1 = {};

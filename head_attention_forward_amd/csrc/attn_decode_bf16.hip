@@ -75,9 +75,9 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_bf16_d64_kernel(const Att
     const unsigned kd = ring_lds;
     const unsigned vd = kd + (unsigned)TILE_BYTES;
     const int k0 = tile * KT;
+    const char* kb = wave_uniform(Kp + (int64_t)k0 * a.k_sr * 2);  // the tile's first row (64-bit)
+    const char* vb = wave_uniform(Vp + (int64_t)k0 * a.v_sr * 2);
     if (k0 + KT <= a.n_k) {
-      const char* kb = Kp + (int64_t)k0 * a.k_sr * 2;
-      const char* vb = Vp + (int64_t)k0 * a.v_sr * 2;
 #pragma unroll
       for (int r = 0; r < 8; ++r) {
         int row, kc, vc;
@@ -90,9 +90,9 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_bf16_d64_kernel(const Att
       for (int r = 0; r < 8; ++r) {
         int row, kc, vc;
         chunk_of(r, row, kc, vc);
-        const int key = min(k0 + row, a.n_k - 1);
-        dma16_s(Kp, (unsigned)(key * a.k_sr + kc) * 2u, kd + 1024u * r);
-        dma16_s(Vp, (unsigned)(key * a.v_sr + vc) * 2u, vd + 1024u * r);
+        const int rr = min(row, a.n_k - 1 - k0);  // offsets from the tile's own row
+        dma16_s(kb, (unsigned)(rr * a.k_sr + kc) * 2u, kd + 1024u * r);
+        dma16_s(vb, (unsigned)(rr * a.v_sr + vc) * 2u, vd + 1024u * r);
       }
     }
   };

@@ -190,10 +190,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
         const unsigned o = a_voff[r] + 2u * (unsigned)(min(k0 + a_kc[r], g.K - 8) - a_kc[r]);
         dma16_s(a_tile, o, a_dst + 1024u * r);
       }
+      const char* wb = w_seg + (int64_t)k0 * wstride * 2;  // the stage's first weight row
 #pragma unroll
       for (int r = 0; r < BL; ++r) {
-        const unsigned o = (unsigned)(min(k0 + w_row[r], g.K - 1) * wstride + w_col[r]) * 2u;
-        dma16_s(w_seg, o, b_dst + 1024u * r);
+        const unsigned o = (unsigned)((min(k0 + w_row[r], g.K - 1) - k0) * wstride + w_col[r]) * 2u;
+        dma16_s(wb, o, b_dst + 1024u * r);
       }
     }
   };

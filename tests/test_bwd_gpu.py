@@ -199,3 +199,55 @@ def test_mha_backward(dev, B, n_q, n_k, dm, h, self_attn, mask, kl, label):
         check_block_grad(grads[1], want[1], f"dX_kv {label}")
     for name, gt, wt in zip(("dWq", "dWk", "dWv", "dWo"), grads[2:], want[2:]):
         check_block_grad(gt, wt, f"{name} {label}")
+
+
+def test_key_range_past_32bit_byte_offsets(dev):
+    """One head with 2^25 + 37 keys (4.3 GB of K): the last, ragged key tile
+    starts at byte 2^32 of the head's K and V.  Every query has q[0] = 64;
+    the first 2^25 keys are (-64, 0, ..., 0), score -512, so their weights
+    are below e^-500 and exactly zero in fp32; the last 37 keys are ordinary
+    (N(0,1), first component 0).  The forward output, the forward's lse and
+    the gradients therefore equal the oracle's on those 37 keys alone, and
+    every other key's gradient is exactly zero.  Copies addressed with 32-bit
+    byte offsets from the head's first row would read the first rows of the
+    buffer for the last tile instead."""
+    n_k = (1 << 25) + 37
+    tail = 37
+    announce("key range past 32-bit byte offsets", n_k)
+    K = torch.zeros((1, 1, n_k, 64), dtype=torch.bfloat16, device=dev)
+    V = torch.zeros((1, 1, n_k, 64), dtype=torch.bfloat16, device=dev)
+    K[:, :, : n_k - tail, 0] = -64.0
+    g = torch.Generator("cpu")
+    g.manual_seed(25)
+    Kt = torch.randn((1, 1, tail, 64), generator=g).to(torch.bfloat16)
+    Kt[..., 0] = 0.0
+    Vt = torch.randn((1, 1, tail, 64), generator=g).to(torch.bfloat16)
+    K[:, :, n_k - tail:] = Kt.to(dev)
+    V[:, :, n_k - tail:] = Vt.to(dev)
+    for n_q in (1, 40, 64):  # the few-query kernel, then the streaming kernel
+        Q = torch.randn((1, 1, n_q, 64), generator=g).to(torch.bfloat16)
+        Q[..., 0] = 64.0
+        dO = torch.randn((1, 1, n_q, 64), generator=g).to(torch.bfloat16)
+        print(f"  n_q={n_q}", flush=True)
+        Qd = Q.to(dev)
+        O = hafa.sdpa_forward(Qd, K, V, 0.125, 0)
+        torch.cuda.synchronize()
+        args = [to_f64(t) for t in (Q, Kt, Vt)]
+        want = oracle.sdpa_ref(*args, 0.125, 0, None)
+        got = to_f64(O.cpu())
+        assert float(np.abs(got - want).max()) <= 2e-2, "forward"
+        if n_q != 64:
+            continue
+        O2, lse = hafa.sdpa_forward_lse(Qd, K, V, 0.125, 0)
+        dQ, dK, dV = hafa.sdpa_backward(Qd, K, V, O2, dO.to(dev), lse, 0.125, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(O2, O)
+        assert float(np.abs(to_f64(lse.cpu()) - oracle.row_logsumexp(args[0], args[1], 0.125, 0, None)).max()) <= U + 1e-6
+        assert int(torch.count_nonzero(dK[:, :, : n_k - tail])) == 0
+        assert int(torch.count_nonzero(dV[:, :, : n_k - tail])) == 0
+        wQ, wK, wV = oracle.sdpa_backward_ref(*args, to_f64(dO), 0.125, 0, None)
+        check_grad(dQ.cpu(), wQ, "dQ past 2^32 bytes")
+        check_grad(dK[:, :, n_k - tail:].cpu(), wK, "dK past 2^32 bytes")
+        check_grad(dV[:, :, n_k - tail:].cpu(), wV, "dV past 2^32 bytes")
+    del K, V
+    torch.cuda.empty_cache()
