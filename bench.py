@@ -133,23 +133,33 @@ def kernel_plan(w, n_launches=None):
         # one batched transpose: W^O, C, W^Q, W^K, W^V, X
         plan.append(dict(name="transposes", flops=0.0, bytes=float(2 * e * (4 * hd * dm + 2 * M * dm)),
                          peak_kind="hbm", has_attention=False))
-        gemm("do_gemm", M, dm, hd)
         def splits(Mo, No, Ko):  # the library's split-K factor for a weight gradient
             return 8
 
         def reduce(name, Mo, No):  # read the fp32 partials, write the bf16 result
             plan.append(dict(name=name, flops=0.0, bytes=float(4 * splits(Mo, No, M) * Mo * No + e * Mo * No),
                              peak_kind="hbm", has_attention=False))
-        gemm("dwo_gemm", hd, M, dm)   # split over K: fp32 partial sums
-        reduce("dwo_reduce", hd, dm)
+
+        def group(name, n):  # the last n entries run as one launch
+            parts = plan[-n:]
+            del plan[-n:]
+            plan.append(dict(name=name, flops=sum(q["flops"] for q in parts),
+                             bytes=sum(q["bytes"] for q in parts), peak_kind="mfma", has_attention=False))
+        # one launch: dC = dY W^O^T and the split-K partials of dW^O = C^T dY
+        gemm("do", M, dm, hd)
+        gemm("dwo", hd, M, dm)
+        group("do_dwo_gemm", 2)
         plan.append(dict(name="backward_dq", flops=6.0 * pairs * dk,
                          bytes=float(e * B * h * nq * dk * 4 + 8 * B * h * nq + e * B * h * nk * dk * 2),
                          peak_kind="mfma", has_attention=False))
         plan.append(dict(name="backward_dkdv", flops=8.0 * pairs * dk,
                          bytes=float(e * B * h * nk * dk * 4 + e * B * h * nq * dk * 2 + 8 * B * h * nq),
                          peak_kind="mfma", has_attention=False))
-        gemm("dx_gemm", M, 3 * hd, dm)
-        gemm("dw_gemm", dm, M, 3 * hd)  # split over K: fp32 partial sums
+        # one launch: dX, the split-K partials of dW^Q|dW^K|dW^V, the reduction of dW^O
+        gemm("dx", M, 3 * hd, dm)
+        gemm("dw", dm, M, 3 * hd)
+        reduce("dwo_reduce", hd, dm)
+        group("dx_dw_gemm", 3)
         reduce("dw_reduce", dm, 3 * hd)
         return plan, None
     if w.kind == "embed":
@@ -634,6 +644,7 @@ KERNEL_SOURCES = {
     "attn_bwd_dkdv_kernel": ("attn_bwd_bf16.hip", "wave_attention.h", "mha_api.hip"),
     "transpose_bf16_kernel": ("transpose_bf16.hip", "mha_api.hip"),
     "gemm_splitk_reduce_kernel": ("gemm_bf16.hip", "mha_api.hip"),
+    "gemm_group_kernel": ("gemm_bf16.hip", "mha_api.hip"),
 }
 
 

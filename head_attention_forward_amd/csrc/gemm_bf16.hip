@@ -82,8 +82,10 @@ __device__ __forceinline__ int seg_start(const GemmArgs& g, int s) {
   return s == 0 ? g.col_start[0] : (s == 1 ? g.col_start[1] : g.col_start[2]);
 }
 
+// One output tile (or one k range of one tile, split-K) of the GEMM g;
+// bid is the workgroup's index within the GEMM's own grid.
 template <int BM, int BN, int NS, int WM, int WN>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs g) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int bid_in) {
   static_assert(BM == 64 || BM == 128, "tile rows");
   static_assert(BN == 64 || BN == 128, "tile columns");
   static_assert(NS >= 2 && NS <= 4, "ring depth");
@@ -117,11 +119,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
   // operands for every tile, a slice its L2 holds.
   int tile, split = 0;
   if (g.splits > 1) {
-    tile = (int)blockIdx.x / g.splits;
-    split = (int)blockIdx.x - tile * g.splits;
+    tile = bid_in / g.splits;
+    split = bid_in - tile * g.splits;
   } else {
     const int T = MT * NT;
-    const int bid = blockIdx.x;
+    const int bid = bid_in;
     const int x = bid % kXcds;
     const int per = T / kXcds;
     const int rem = T - per * kXcds;
@@ -359,6 +361,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
   }
 }
 
+template <int BM, int BN, int NS, int WM, int WN>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs g) {
+  gemm_tile<BM, BN, NS, WM, WN>(g, (int)blockIdx.x);
+}
+
 template <int BM, int BN, int NS, int WM = 2, int WN = 2>
 hipError_t launch_tile(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
   const int N = g.col_start[g.nseg];
@@ -371,10 +378,10 @@ hipError_t launch_tile(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
 
 // Sum of the split-K partials, rounded once to bf16 and written to the
 // segments (plain row-major outputs).  One thread per 8 columns.
-__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const GemmArgs g) {
+__device__ __forceinline__ void splitk_reduce(const GemmArgs& g, const int bid) {
   const int N = g.col_start[g.nseg];
   const int chunks = N / 8;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t idx = (int64_t)bid * 256 + threadIdx.x;
   if (idx >= (int64_t)g.M * chunks) return;
   const int m = (int)(idx / chunks);
   const int n = (int)(idx - (int64_t)m * chunks) * 8;
@@ -394,6 +401,29 @@ __global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const GemmArgs 
   const int width = seg_field(g, sg, &GemmSeg::width);
   __bf16* dst = (__bf16*)seg_field(g, sg, &GemmSeg::dst) + (int64_t)m * width + (n - seg_start(g, sg));
   *(bf16x8*)dst = __builtin_convertvector(v, bf16x8);
+}
+
+__global__ __launch_bounds__(256) void gemm_splitk_reduce_kernel(const GemmArgs g) {
+  splitk_reduce(g, (int)blockIdx.x);
+}
+
+// Independent jobs of one launch (GemmGroup): job j owns workgroups
+// [start[j], start[j] + count[j]); starts are multiples of 8, so that the
+// XCD a workgroup lands on is the one the job's own tile order assumes.
+// Workgroups between jobs (padding) return at once.
+__global__ __launch_bounds__(256) void gemm_group_kernel(const GemmGroup gg) {
+  const int b = (int)blockIdx.x;
+  int j = -1;
+#pragma unroll
+  for (int i = 0; i < kMaxGroupJobs; ++i)
+    if (i < gg.n && b >= gg.start[i] && b < gg.start[i] + gg.count[i]) j = i;
+  j = __builtin_amdgcn_readfirstlane(j);
+  if (j < 0) return;
+  const GemmArgs& g = j == 0 ? gg.job[0] : (j == 1 ? gg.job[1] : gg.job[2]);
+  const int rb = b - (j == 0 ? gg.start[0] : (j == 1 ? gg.start[1] : gg.start[2]));
+  const int red = j == 0 ? gg.reduce[0] : (j == 1 ? gg.reduce[1] : gg.reduce[2]);
+  if (red) splitk_reduce(g, rb);
+  else gemm_tile<64, 64, 3, 2, 2>(g, rb);
 }
 
 // Every segment must start on a multiple of the tile width (a tile's columns
@@ -424,6 +454,36 @@ hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, Launc
     case 11: return launch_tile<64, 128, 2, 2, 4>(g, s, ev);
     default: return launch_tile<128, 64, 2, 4, 2>(g, s, ev);
   }
+}
+
+hipError_t launch_gemm_bf16_group(GemmGroup gg, hipStream_t s, LaunchEvents ev) {
+  if (gg.n < 1 || gg.n > kMaxGroupJobs) return hipErrorInvalidValue;
+  int next = 0;
+  for (int j = 0; j < gg.n; ++j) {
+    const GemmArgs& g = gg.job[j];
+    const int N = g.col_start[g.nseg];
+    int64_t cnt;
+    if (gg.reduce[j]) {
+      if (g.splits < 2 || g.partial == nullptr || N % 8 != 0) return hipErrorInvalidValue;
+      cnt = ((int64_t)g.M * (N / 8) + 255) / 256;
+    } else {
+      if (!tiles_fit(g, 64)) return hipErrorInvalidValue;
+      if (g.splits > 1) {
+        if (g.partial == nullptr || g.bias != nullptr || g.relu) return hipErrorInvalidValue;
+        for (int sg = 0; sg < g.nseg; ++sg)
+          if (g.seg[sg].heads != 1 || g.seg[sg].width % 8 != 0) return hipErrorInvalidValue;
+      }
+      cnt = (int64_t)((N + 63) / 64) * ((g.M + 63) / 64) * (g.splits > 1 ? g.splits : 1);
+    }
+    gg.start[j] = next;
+    gg.count[j] = (int)cnt;
+    const int64_t end = ((int64_t)next + cnt + kXcds - 1) / kXcds * kXcds;
+    if (end > (int64_t)1 << 30) return hipErrorInvalidValue;
+    next = (int)end;
+  }
+  void* args[] = {(void*)&gg};
+  return hipExtLaunchKernel((const void*)gemm_group_kernel, dim3(next), dim3(256), args, 0, s, ev.start,
+                            ev.stop, 0);
 }
 
 hipError_t launch_gemm_bf16_splitk(const GemmArgs& g, hipStream_t s, LaunchEvents ev_gemm,

@@ -152,6 +152,20 @@ hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev
 hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_gemm_bf16_splitk(const GemmArgs& g, hipStream_t s, LaunchEvents ev_gemm = {},
                                    LaunchEvents ev_reduce = {});
+// Up to three independent jobs in one launch, each a GEMM in 64 x 64 tiles
+// (plain, or split-K writing its fp32 partials) or, reduce[j] != 0, the
+// reduction of a split-K GEMM that an earlier launch finished.  The jobs
+// must not depend on each other (they run concurrently).  start and count
+// are filled in by the launcher.
+constexpr int kMaxGroupJobs = 3;
+struct GemmGroup {
+  GemmArgs job[kMaxGroupJobs];
+  int reduce[kMaxGroupJobs];
+  int start[kMaxGroupJobs];
+  int count[kMaxGroupJobs];
+  int n;
+};
+hipError_t launch_gemm_bf16_group(GemmGroup gg, hipStream_t s, LaunchEvents ev = {});
 // Backward: the dQ kernel (also writes Dw), then the dK/dV kernel (reads Dw).
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, hipStream_t s, LaunchEvents ev = {});
 hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, hipStream_t s, LaunchEvents ev = {});

@@ -341,7 +341,9 @@ struct BwdWs {
   void* WkvT;   // cross: [2hd][d_model]
   void* XqT;    // [d_model][M_q]
   void* XkvT;   // cross: [d_model][M_k]
-  float* partial;  // split-K partial sums of the weight-gradient GEMMs
+  float* partial;   // split-K partial sums of dW^O
+  float* partial1;  // ... of dW^Q (with dW^K, dW^V for self-attention)
+  float* partial2;  // cross-attention: ... of dW^K | dW^V
   size_t rows_each;
   size_t bytes;
 };
@@ -364,16 +366,14 @@ BwdWs carve_bwd(void* base, bool self_attn, int B, int n_q, int n_k, int d_model
   w.dO = take(2 * Mq * hd);
   w.OcT = take(2 * hd * Mq);
   w.rows_each = round_up((size_t)4 * B * h * n_q);
-  {
-    // the largest of the weight-gradient GEMMs' partial sums
-    size_t part = (size_t)wgrad_splits((int)hd, d_model, (int)Mq) * hd * dm;
-    if (self_attn) {
-      part = max(part, (size_t)wgrad_splits(d_model, 3 * (int)hd, (int)Mq) * dm * 3 * hd);
-    } else {
-      part = max(part, (size_t)wgrad_splits(d_model, (int)hd, (int)Mq) * dm * hd);
-      part = max(part, (size_t)wgrad_splits(d_model, 2 * (int)hd, (int)Mk) * dm * 2 * hd);
-    }
-    w.partial = (float*)take(4 * part);
+  // Partial sums of the weight-gradient GEMMs, one region each: a reduction
+  // runs in the same launch as a later split-K GEMM.
+  w.partial = (float*)take(4 * (size_t)wgrad_splits((int)hd, d_model, (int)Mq) * hd * dm);
+  if (self_attn) {
+    w.partial1 = (float*)take(4 * (size_t)wgrad_splits(d_model, 3 * (int)hd, (int)Mq) * dm * 3 * hd);
+  } else {
+    w.partial1 = (float*)take(4 * (size_t)wgrad_splits(d_model, (int)hd, (int)Mq) * dm * hd);
+    w.partial2 = (float*)take(4 * (size_t)wgrad_splits(d_model, 2 * (int)hd, (int)Mk) * dm * 2 * hd);
   }
   if (self_attn) {
     w.dQKV = take(2 * Mq * 3 * hd);
@@ -396,8 +396,8 @@ BwdWs carve_bwd(void* base, bool self_attn, int B, int n_q, int n_k, int d_model
 // C = A . [segments], A [M][K] row-major; each segment a row-major weight
 // (row stride ldw) written as a plain row-major [M][width] matrix.
 // partial != null: split-K (a weight gradient: small output, K = rows).
-int do_gemm_rm(const void* A, int M, int K, int nseg, const void* const* W, void* const* dst,
-               const int* width, int ldw, hipStream_t stream, Timer* tm, float* partial = nullptr) {
+GemmArgs rm_args(const void* A, int M, int K, int nseg, const void* const* W, void* const* dst,
+                 const int* width, int ldw, float* partial = nullptr) {
   GemmArgs g{};
   g.A = A;
   g.M = M;
@@ -413,6 +413,14 @@ int do_gemm_rm(const void* A, int M, int K, int nseg, const void* const* W, void
   if (partial != nullptr) {
     g.splits = wgrad_splits(M, c, K);
     g.partial = partial;
+  }
+  return g;
+}
+
+int do_gemm_rm(const void* A, int M, int K, int nseg, const void* const* W, void* const* dst,
+               const int* width, int ldw, hipStream_t stream, Timer* tm, float* partial = nullptr) {
+  const GemmArgs g = rm_args(A, M, K, nseg, W, dst, width, ldw, partial);
+  if (partial != nullptr) {
     const LaunchEvents e1 = next_events(tm);
     const LaunchEvents e2 = next_events(tm);
     return launch_status(launch_gemm_bf16_splitk(g, stream, e1, e2));
@@ -435,7 +443,25 @@ struct Transposes {
   }
 };
 
-int mha_bwd_launch_count(bool self_attn) { return self_attn ? 9 : 12; }
+// One grouped launch of independent GEMM / reduction jobs.
+struct Group {
+  GemmGroup gg{};
+  Group& gemm(const GemmArgs& g) {
+    gg.job[gg.n] = g;
+    gg.reduce[gg.n++] = 0;
+    return *this;
+  }
+  Group& reduce(const GemmArgs& g) {
+    gg.job[gg.n] = g;
+    gg.reduce[gg.n++] = 1;
+    return *this;
+  }
+  int launch(hipStream_t stream, Timer* tm) const {
+    return launch_status(launch_gemm_bf16_group(gg, stream, next_events(tm)));
+  }
+};
+
+int mha_bwd_launch_count(bool self_attn) { return self_attn ? 6 : 7; }
 
 }  // namespace
 }  // namespace mha
@@ -971,7 +997,9 @@ static int mha_bwd_impl(const void* X_q, const void* X_kv, const void* Wq, const
     st = tr.launch(stream, tm);
     if (st != MHA_OK) return st;
   }
-  // dC = dY W^O^T, scattered per head into dO [B][h][n_q][d]
+  // One launch: dC = dY W^O^T, scattered per head into dO [B][h][n_q][d],
+  // and the split-K partial sums of dW^O = C^T dY (reduced in a later launch).
+  GemmArgs g_dwo;
   {
     GemmArgs g{};
     g.A = dY;
@@ -981,15 +1009,11 @@ static int mha_bwd_impl(const void* X_q, const void* X_kv, const void* Wq, const
     g.seg[0] = GemmSeg{w.WoT, w.dO, hd, d_v, h, n_q, 0};
     g.col_start[0] = 0;
     g.col_start[1] = hd;
-    st = launch_status(launch_gemm_bf16(g, stream, next_events(tm)));
-    if (st != MHA_OK) return st;
-  }
-  // dW^O = C^T dY
-  {
     const void* W[1] = {dY};
     void* D[1] = {dWo};
     const int wd[1] = {dm};
-    st = do_gemm_rm(w.OcT, hd, (int)Mq, 1, W, D, wd, 0, stream, tm, w.partial);
+    g_dwo = rm_args(w.OcT, hd, (int)Mq, 1, W, D, wd, 0, w.partial);
+    st = Group().gemm(g).gemm(g_dwo).launch(stream, tm);
     if (st != MHA_OK) return st;
   }
   // attention gradients, written with the heads concatenated
@@ -1036,41 +1060,47 @@ static int mha_bwd_impl(const void* X_q, const void* X_kv, const void* Wq, const
     if (st != MHA_OK) return st;
   }
   if (self_attn) {
-    // dX = [dQ | dK | dV] [W^Q | W^K | W^V]^T
+    // One launch: dX = [dQ | dK | dV] [W^Q | W^K | W^V]^T, the partial sums
+    // of [dW^Q | dW^K | dW^V] = X^T [dQ | dK | dV], and the reduction of dW^O.
     const void* W[1] = {w.WT};
     void* D[1] = {dX_q};
     const int wd[1] = {dm};
-    st = do_gemm_rm(w.dQKV, (int)Mq, 3 * hd, 1, W, D, wd, 0, stream, tm);
-    if (st != MHA_OK) return st;
-    // [dW^Q | dW^K | dW^V] = X^T [dQ | dK | dV]
+    const GemmArgs g_dx = rm_args(w.dQKV, (int)Mq, 3 * hd, 1, W, D, wd, 0);
     const void* W3[3] = {w.dQKV, (__bf16*)w.dQKV + hd, (__bf16*)w.dQKV + 2 * hd};
     void* D3[3] = {dWq, dWk, dWv};
     const int wd3[3] = {hd, hd, hd};
-    return do_gemm_rm(w.XqT, dm, (int)Mq, 3, W3, D3, wd3, 3 * hd, stream, tm, w.partial);
+    const GemmArgs g_dw = rm_args(w.XqT, dm, (int)Mq, 3, W3, D3, wd3, 3 * hd, w.partial1);
+    st = Group().gemm(g_dx).gemm(g_dw).reduce(g_dwo).launch(stream, tm);
+    if (st != MHA_OK) return st;
+    return Group().reduce(g_dw).launch(stream, tm);
   }
-  // cross-attention: dX_q = dQ W^Q^T, dX_kv = [dK | dV] [W^K | W^V]^T
+  // cross-attention.  One launch: dX_q = dQ W^Q^T, dX_kv = [dK | dV]
+  // [W^K | W^V]^T and the reduction of dW^O; one launch: the partial sums of
+  // dW^Q = X_q^T dQ and [dW^K | dW^V] = X_kv^T [dK | dV]; one launch: their
+  // reductions.
   {
     const void* W[1] = {w.WT};
     void* D[1] = {dX_q};
     const int wd[1] = {dm};
-    st = do_gemm_rm(w.dQKV, (int)Mq, hd, 1, W, D, wd, 0, stream, tm);
-    if (st != MHA_OK) return st;
+    const GemmArgs g_dxq = rm_args(w.dQKV, (int)Mq, hd, 1, W, D, wd, 0);
     const void* W2[1] = {w.WkvT};
     void* D2[1] = {dX_kv};
-    st = do_gemm_rm(w.dKV, (int)Mk, 2 * hd, 1, W2, D2, wd, 0, stream, tm);
+    const GemmArgs g_dxkv = rm_args(w.dKV, (int)Mk, 2 * hd, 1, W2, D2, wd, 0);
+    st = Group().gemm(g_dxq).gemm(g_dxkv).reduce(g_dwo).launch(stream, tm);
     if (st != MHA_OK) return st;
   }
-  // dW^Q = X_q^T dQ, [dW^K | dW^V] = X_kv^T [dK | dV]
   {
     const void* W[1] = {w.dQKV};
     void* D[1] = {dWq};
     const int wd[1] = {hd};
-    st = do_gemm_rm(w.XqT, dm, (int)Mq, 1, W, D, wd, 0, stream, tm, w.partial);
-    if (st != MHA_OK) return st;
+    const GemmArgs g_dwq = rm_args(w.XqT, dm, (int)Mq, 1, W, D, wd, 0, w.partial1);
     const void* W2[2] = {w.dKV, (__bf16*)w.dKV + hd};
     void* D2[2] = {dWk, dWv};
     const int wd2[2] = {hd, hd};
-    return do_gemm_rm(w.XkvT, dm, (int)Mk, 2, W2, D2, wd2, 2 * hd, stream, tm, w.partial);
+    const GemmArgs g_dwkv = rm_args(w.XkvT, dm, (int)Mk, 2, W2, D2, wd2, 2 * hd, w.partial2);
+    st = Group().gemm(g_dwq).gemm(g_dwkv).launch(stream, tm);
+    if (st != MHA_OK) return st;
+    return Group().reduce(g_dwq).reduce(g_dwkv).launch(stream, tm);
   }
 }
 

@@ -350,10 +350,11 @@ size_t mha_backward_workspace_bytes(int B, int n_q, int n_k, int d_model, int h,
  * Launches (mha_backward_launches): one batched transpose of W^O, C, the
  * input weights (stacked for self-attention) and the inputs (bandwidth-bound
  * copies that let the projection GEMM take every product as A . B with
- * row-major operands), the GEMMs for dC and dX, the weight-gradient GEMMs
- * split over K (fp32 partial sums in the workspace, then one kernel that
- * adds them and rounds once), and the two attention-backward kernels.
- * bf16 in and out, fp32 accumulation.
+ * row-major operands); the GEMMs for dC and dX and the weight-gradient GEMMs
+ * split over K (fp32 partial sums in the workspace, each added up and
+ * rounded once by a reduction), with independent GEMMs and reductions
+ * sharing a launch; and the two attention-backward kernels.  bf16 in and
+ * out, fp32 accumulation.
  */
 int mha_backward(const void* X_q, const void* X_kv,
                  const void* Wq, const void* Wk, const void* Wv, const void* Wo,
@@ -375,8 +376,8 @@ int mha_backward_timed(const void* X_q, const void* X_kv,
                        void* workspace, size_t workspace_bytes, hipStream_t stream,
                        hipEvent_t* events, int capacity, int* n_launches);
 
-/* mha_backward_launches -- kernels mha_backward launches: 9 for
- * self-attention, 12 for cross-attention.  Host-only. */
+/* mha_backward_launches -- kernels mha_backward launches: 6 for
+ * self-attention, 7 for cross-attention.  Host-only. */
 int mha_backward_launches(int self_attention);
 
 /*
