@@ -167,6 +167,8 @@ LAYER_CASES = [
     (dict(B=2, n_q=129, n_k=129), "n = 129 (unfused projection plan)"),
     (dict(B=2, n_q=50, n_k=50, d_model=72, h=1, d_ff=136), "d_model 72 (not a multiple of 64)"),
     (dict(B=2, n_q=64, n_k=64, mask=1), "causal self-attention"),
+    (dict(B=1, n_q=7, n_k=7, d_model=256, h=4, d_ff=128), "7 rows, d_model 256"),
+    (dict(B=2, n_q=40, n_k=40, d_model=1024, h=16, d_ff=256), "d_model 1024 (the big model's width)"),
 ]
 
 
@@ -181,10 +183,12 @@ def test_encoder_layer(dev, over, label):
     assert_close(Y, _layer_ref(x, w, x["key_lengths"]), label)
 
 
-def test_encoder_layer_equals_its_entry_points(dev):
+@pytest.mark.parametrize("B,n", [(4, 100), (3, 77)])
+def test_encoder_layer_equals_its_entry_points(dev, B, n):
     """The layer is mha_forward, add_layernorm_forward, ffn_forward,
-    add_layernorm_forward on one stream: bit-identical results."""
-    w = WORKLOADS["encoder_layer_base"].replace(B=4)
+    add_layernorm_forward on one stream: bit-identical results (also for a
+    row count, 231, that no tile size divides)."""
+    w = WORKLOADS["encoder_layer_base"].replace(B=B, n_q=n, n_k=n)
     x = generate(w, seed=4)
     d = {k: v.to(dev) for k, v in x.items() if v is not None}
     announce("encoder_layer vs entry points", w.B, w.n_q)
