@@ -446,16 +446,16 @@ struct Transposes {
 // One grouped launch of independent GEMM / reduction jobs.
 struct Group {
   GemmGroup gg{};
-  Group& gemm(const GemmArgs& g) {
-    gg.job[gg.n] = g;
-    gg.reduce[gg.n++] = 0;
+  Group& add(const GemmArgs& g, int red) {
+    if (gg.n < kMaxGroupJobs) {
+      gg.job[gg.n] = g;
+      gg.reduce[gg.n] = red;
+    }
+    ++gg.n;  // past kMaxGroupJobs jobs the launcher rejects the group
     return *this;
   }
-  Group& reduce(const GemmArgs& g) {
-    gg.job[gg.n] = g;
-    gg.reduce[gg.n++] = 1;
-    return *this;
-  }
+  Group& gemm(const GemmArgs& g) { return add(g, 0); }
+  Group& reduce(const GemmArgs& g) { return add(g, 1); }
   int launch(hipStream_t stream, Timer* tm) const {
     return launch_status(launch_gemm_bf16_group(gg, stream, next_events(tm)));
   }
