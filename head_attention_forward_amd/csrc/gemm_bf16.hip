@@ -49,7 +49,7 @@ __device__ __forceinline__ int a_pos(int m, int chunk) { return chunk ^ ((m >> 1
 // BN = 64 -> 128-byte rows, chunk c of row k at c ^ (((k >> 1) & 1) << 2).
 template <int BN>
 __device__ __forceinline__ int b_pos(int k, int chunk) {
-  if constexpr (BN == 128) return chunk ^ ((k & 3) << 2);
+  if constexpr (BN >= 128) return chunk ^ ((k & 3) << 2);
   else return chunk ^ (((k >> 1) & 1) << 2);
 }
 
@@ -86,8 +86,8 @@ __device__ __forceinline__ int seg_start(const GemmArgs& g, int s) {
 // bid is the workgroup's index within the GEMM's own grid.
 template <int BM, int BN, int NS, int WM, int WN>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int bid_in) {
-  static_assert(BM == 64 || BM == 128, "tile rows");
-  static_assert(BN == 64 || BN == 128, "tile columns");
+  static_assert(BM == 64 || BM == 128 || BM == 256, "tile rows");
+  static_assert(BN == 64 || BN == 128 || BN == 256, "tile columns");
   static_assert(NS >= 2 && NS <= 4, "ring depth");
   constexpr int NWAVE = WM * WN;
   constexpr int MB = BM / WM / 32;     // 32-row MFMA tiles per wave
@@ -437,8 +437,8 @@ bool tiles_fit(const GemmArgs& g, int bn) {
 }  // namespace
 
 hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, LaunchEvents ev) {
-  static const int kBN[] = {128, 128, 128, 128, 128, 64, 64, 64, 64, 128, 128, 128, 64};
-  if (cfg < 0 || cfg > 12 || !tiles_fit(g, kBN[cfg])) return hipErrorInvalidValue;
+  static const int kBN[] = {128, 128, 128, 128, 128, 64, 64, 64, 64, 128, 128, 128, 64, 256};
+  if (cfg < 0 || cfg > 13 || !tiles_fit(g, kBN[cfg])) return hipErrorInvalidValue;
   switch (cfg) {
     case 0: return launch_tile<128, 128, 2>(g, s, ev);
     case 1: return launch_tile<128, 128, 3>(g, s, ev);
@@ -452,6 +452,7 @@ hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, Launc
     case 9: return launch_tile<128, 128, 2, 2, 4>(g, s, ev);
     case 10: return launch_tile<128, 128, 3, 2, 4>(g, s, ev);
     case 11: return launch_tile<64, 128, 2, 2, 4>(g, s, ev);
+    case 13: return launch_tile<256, 256, 2, 4, 4>(g, s, ev);
     default: return launch_tile<128, 64, 2, 4, 2>(g, s, ev);
   }
 }
@@ -510,6 +511,15 @@ hipError_t launch_gemm_bf16(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
   // tiles with 4 waves for parallelism.  Larger tiles (256 x 128) were
   // slower on every shape measured.
   const int N = g.col_start[g.nseg];
+  // 256 x 256 tiles with 16 waves (64 x 64 per wave: half the bytes brought
+  // into LDS per flop of 128 x 128, and 1 KB of LDS reads per MFMA) when they fill the compute
+  // units: their last round occupies at least three quarters of the 256
+  // (decoder QKV projection, 8192 x 1536, K = 512: 26.3 vs 30.3 us; with
+  // half the units idle, 128 tiles, they are 1.3x slower).
+  if (tiles_fit(g, 256)) {
+    const long t256 = (long)((N + 255) / 256) * ((g.M + 255) / 256);
+    if (t256 % 256 == 0 || t256 % 256 >= 192) return launch_gemm_bf16_cfg(g, 13, s, ev);
+  }
   if (!tiles_fit(g, 128)) return launch_gemm_bf16_cfg(g, 6, s, ev);
   const long t128 = (long)((N + 127) / 128) * ((g.M + 127) / 128);
   if (t128 >= 400) return launch_gemm_bf16_cfg(g, 9, s, ev);

@@ -105,6 +105,14 @@ def test_mha_workloads(dev, name):
     _mha_case(dev, WORKLOADS[name])
 
 
+def test_mha_ragged_rows_on_256_row_projection_tiles(dev):
+    """B = 5, n = 1631: 8155 rows x 1536 columns of the stacked projection
+    take 256 x 256 tiles (192 of them), the last row tile 219 rows deep."""
+    w = WORKLOADS["decoder_causal_base"].replace(name="ragged256", B=5, n_q=1631, n_k=1631,
+                                                 description="B=5 n=1631 causal, 256-row tiles")
+    _mha_case(dev, w, seed=5)
+
+
 def test_mha_stages_equal_forward_and_intermediates(dev):
     """The three stage calls reproduce mha_forward bit for bit, and the
     workspace intermediates match the oracle's projections and concat."""
