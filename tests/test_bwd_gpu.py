@@ -167,6 +167,7 @@ BLOCK_CASES = [
     (2, 256, 256, 512, 8, True, 1, None, "causal self-attention"),
     (4, 96, 128, 256, 4, False, 2, [128, 64, 100, 1], "cross-attention, key padding"),
     (8, 7, 9, 128, 2, False, 0, None, "tiny ragged cross-attention (B n multiples of 8)"),
+    (4, 30, 30, 72, 1, True, 1, None, "d_model 72: grouped GEMM jobs with 72 columns"),
 ]
 
 
