@@ -266,6 +266,8 @@ def test_mha_max_padded_batch_and_fused_boundary(dev):
 @pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", [
     (2, 3, 1, 129, 0, None), (3, 2, 1, 300, 2, [300, 1, 191]), (2, 2, 5, 1000, 2, [1000, 650]),
     (1, 4, 32, 777, 0, None), (4, 2, 1, 4096, 2, [4096, 2049, 1, 3000]), (1, 2, 17, 8193, 0, None),
+    # more (batch, head) pairs than compute units (a second wave of workgroups)
+    (9, 32, 3, 513, 0, None), (65, 4, 1, 1000, 2, [1 + (i * 397) % 1000 for i in range(65)]),
 ])
 def test_sdpa_decode_shapes(dev, B, h, n_q, n_k, mask, kl):
     """Few queries over long key ranges (one new query per sequence against
@@ -284,6 +286,20 @@ def test_sdpa_decode_shapes(dev, B, h, n_q, n_k, mask, kl):
         O2 = run_sdpa(dev, Q, K2, V2, 0.125, mask, kl)
         torch.cuda.synchronize()
         assert torch.equal(O2.cpu(), O.cpu())
+
+
+def test_decode_step_full_size(dev):
+    """The decode workload at its full size (B=32, h=16: 512 heads of one
+    query against cache lengths drawn from [1024, 4096]), every output
+    against the oracle."""
+    w = WORKLOADS["decode_step_sdpa"]
+    g = torch.Generator().manual_seed(9)
+    kl = torch.randint(w.key_len_range[0], w.key_len_range[1] + 1, (w.B,), generator=g).tolist()
+    Q, K, V = sdpa_inputs(w.B, w.h, w.n_q, w.n_k, torch.bfloat16, seed=43)
+    announce("sdpa decode full size", w.B, w.h, w.n_q, w.n_k, kl)
+    O = run_sdpa(dev, Q, K, V, 0.125, w.mask, kl)
+    torch.cuda.synchronize()
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, w.mask, kl), "decode_step_sdpa")
 
 
 def test_saturated_and_uniform(dev):
