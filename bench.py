@@ -616,11 +616,16 @@ def cpu_baseline(w, x, target_s):
     run(1)
     t1 = max(time.perf_counter() - t0, 1e-6)
     units = int(max(1, min(n_units, target_s / t1)))
-    reps = 1 if units < n_units else int(max(1, min(1000, target_s / (t1 * n_units))))
+    # whole passes until target_s has elapsed (a batched pass runs faster
+    # per unit than the single unit timed above)
+    reps = 0
     t0 = time.perf_counter()
-    for _ in range(reps):
+    while True:
         run(units)
-    t = time.perf_counter() - t0
+        reps += 1
+        t = time.perf_counter() - t0
+        if units < n_units or t >= target_s or reps >= 1000:
+            break
     flops = unit_flops * units * reps
     sample = f"{units} of {n_units} {what}" + (f", {reps} passes" if reps > 1 else "")
     return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
