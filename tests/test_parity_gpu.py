@@ -219,7 +219,8 @@ def test_sdpa_bf16_large_ragged_sampled(dev, B, h, n_q, n_k, mask, kl):
 
 @pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", [(1, 1, 1, 1, 0, None), (2, 2, 100, 100, 1, None),
                                                  (2, 1, 70, 129, 2, [5, 129]),
-                                                 (1, 2, 200, 200, 3, [150])])
+                                                 (1, 2, 200, 200, 3, [150]),
+                                                 (3, 2, 33, 1000, 2, [1, 999, 1000])])
 def test_sdpa_f32_edges(dev, B, h, n_q, n_k, mask, kl):
     Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.float32, seed=7 + n_q)
     announce("sdpa_forward f32 edge", dict(B=B, h=h, n_q=n_q, n_k=n_k, mask=mask, kl=kl))
