@@ -26,6 +26,28 @@ constexpr int NT = QB * SPLIT;      // threads per workgroup
 constexpr int KT = 64;              // keys per tile
 constexpr int RS = D + 4;           // padded LDS row stride (floats)
 
+// Sum and maximum over the 8 lanes of a group (lanes 8g .. 8g + 7) with DPP
+// moves instead of LDS permutes: exchange with lane ^ 1, then lane ^ 2 (quad
+// permutes), then the mirrored lane of the 8 (lane 7 - i, which after the
+// first two steps holds the same value as lane i ^ 4).  The same additions
+// in the same order as a butterfly over lane ^ 1, ^ 2, ^ 4.
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kXor1 = 0xB1;        // quad_perm [1, 0, 3, 2]
+constexpr int kXor2 = 0x4E;        // quad_perm [2, 3, 0, 1]
+constexpr int kHalfMirror = 0x141; // row_half_mirror
+__device__ __forceinline__ float group8_sum(float v) {
+  v += dpp<kXor1>(v);
+  v += dpp<kXor2>(v);
+  return v + dpp<kHalfMirror>(v);
+}
+__device__ __forceinline__ float group8_max(float v) {
+  v = fmaxf(v, dpp<kXor1>(v));
+  v = fmaxf(v, dpp<kXor2>(v));
+  return fmaxf(v, dpp<kHalfMirror>(v));
+}
 __global__ __launch_bounds__(NT) void attn_fwd_f32_d64_kernel(const AttnArgs a) {
   __shared__ __attribute__((aligned(16))) float Ks[KT * RS];
   __shared__ __attribute__((aligned(16))) float Vs[KT * RS];
@@ -127,20 +149,12 @@ __global__ __launch_bounds__(NT) void attn_fwd_f32_d64_kernel(const AttnArgs a) 
 
   // Merge the eight partial softmaxes of the row (lanes of a group are
   // adjacent).  Lane 0 of every group sees key 0, so the merged m is finite.
-  float mg = m;
-#pragma unroll
-  for (int o = 1; o < SPLIT; o <<= 1) mg = fmaxf(mg, __shfl_xor(mg, o, SPLIT));
+  static_assert(SPLIT == 8, "the group reductions span 8 lanes");
+  const float mg = group8_max(m);
   const float w = (m == -INFINITY) ? 0.f : expf(m - mg);
-  float lg = l * w;
+  const float lg = group8_sum(l * w);
 #pragma unroll
-  for (int o = 1; o < SPLIT; o <<= 1) lg += __shfl_xor(lg, o, SPLIT);
-#pragma unroll
-  for (int d = 0; d < D; ++d) {
-    float v = acc[d] * w;
-#pragma unroll
-    for (int o = 1; o < SPLIT; o <<= 1) v += __shfl_xor(v, o, SPLIT);
-    acc[d] = v;
-  }
+  for (int d = 0; d < D; ++d) acc[d] = group8_sum(acc[d] * w);
 
   if (my_q < a.n_q && r == 0) {
     float* orow = Op + (int64_t)my_q * a.o_sr;
