@@ -30,6 +30,14 @@ import os
 import sys
 import time
 
+# The CPU oracle runs on the host cores this process may use.  Its BLAS
+# thread pools read these variables when numpy first loads (torch loads it
+# too), so they are set here, before either import; a value the environment
+# already holds is kept.
+HOST_CORES = len(os.sched_getaffinity(0))
+for _var in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+    os.environ.setdefault(_var, str(HOST_CORES))
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
@@ -39,7 +47,10 @@ PEAK_BF16_TFLOPS = 2516.6      # 256 CU x 2.4 GHz x 4096 flop/clk (dense bf16 MF
 PEAK_FP32_TFLOPS = 157.3       # fp32 vector
 PEAK_HBM_GBS = 8000.0          # HBM3E
 MALL_BYTES = 256 << 20
-DEFAULT_WORKLOAD = "encoder_self_base"
+# The headline configuration: the long causal attention (B=4, h=16,
+# n=4096, d=64, bf16), the largest of the workloads and the one whose
+# attention kernel is bound by the matrix units.
+DEFAULT_WORKLOAD = "long_causal_sdpa"
 
 
 def parse_args():
@@ -82,6 +93,8 @@ def layer_launches(w):
 def step_launches(w):
     if w.kind in ("sdpa", "embed"):
         return 1
+    if w.kind == "floor":
+        return 2
     if w.kind == "bwd":
         return 2
     if w.kind == "mha_bwd":
@@ -109,6 +122,13 @@ def kernel_plan(w, n_launches=None):
         plan.append(dict(name=name, flops=0.0, bytes=float(e * (3 * M * d + 2 * d)),
                          peak_kind="hbm", has_attention=False))
 
+    if w.kind == "floor":
+        # an empty kernel, then one that reads Q, K, V and writes an O-sized output
+        plan.append(dict(name="empty_kernel", flops=0.0, bytes=0.0, peak_kind="hbm", has_attention=False))
+        plan.append(dict(name="xor3_copy", flops=0.0,
+                         bytes=float(e * B * h * (nq * dk + nk * (dk + dv) + nq * dv)),
+                         peak_kind="hbm", has_attention=False))
+        return plan, None
     if w.kind == "sdpa":
         plan.append(dict(name="attention", flops=0.0, bytes=0.0,
                          peak_kind="mfma" if w.dtype == "bf16" else "fp32", has_attention=True))
@@ -241,6 +261,13 @@ def attention_accounting(w, key_lengths):
     return flops, float(bytes_)
 
 
+def peak_percent(flops, us, peak_tflops=None):
+    """flops done in us microseconds, as a percent of a peak in TFLOP/s
+    (the bf16 dense MFMA peak by default)."""
+    peak = PEAK_BF16_TFLOPS if peak_tflops is None else peak_tflops
+    return 100.0 * flops / (us * 1e-6) / 1e12 / peak
+
+
 # ----------------------------------------------------------------------------- steps
 
 class Step:
@@ -261,7 +288,13 @@ class Step:
             self.kl = None
         P = ctypes.c_void_p
         for _ in range(sets):
-            if w.kind == "sdpa":
+            if w.kind == "floor":
+                Q, K, V = (x[k].to(dev) for k in ("Q", "K", "V"))
+                O = torch.empty_like(Q)
+                self.keep.append((Q, K, V, O))
+                self.sets.append((P(Q.data_ptr()), P(K.data_ptr()), P(V.data_ptr()), P(O.data_ptr()),
+                                  Q.numel() * Q.element_size(), floor_grid(w)))
+            elif w.kind == "sdpa":
                 Q, K, V = (x[k].to(dev) for k in ("Q", "K", "V"))
                 O = torch.empty((w.B, w.h, w.n_q, w.d_v), dtype=Q.dtype, device=dev)
                 self.keep.append((Q, K, V, O))
@@ -345,7 +378,8 @@ class Step:
                                   w.B, w.n_q, w.n_k, w.d_model, w.h, w.d_k, w.d_v, w.mask, self.kl,
                                   bnd.DTYPE_BF16, P(ws.data_ptr()), ws.numel()))
         self.n_launches = step_launches(w)
-        names = {"sdpa": "sdpa_forward", "mha": "mha_forward", "layer": "encoder_layer_forward",
+        names = {"floor": "mha_floor_probe",
+                 "sdpa": "sdpa_forward", "mha": "mha_forward", "layer": "encoder_layer_forward",
                  "embed": "embed_positional_forward", "bwd": "sdpa_backward",
                  "mha_bwd": "mha_backward"}
         self.entry = names[w.kind]
@@ -361,16 +395,39 @@ class Step:
         return self.keep[i][3]
 
     def run(self, i, stream):
+        if self.w.kind == "floor":  # the empty kernel, then the byte mover
+            q, k, v, o, nbytes, grid = self.sets[i]
+            for kind in (0, 1):
+                st = self.lib.mha_floor_probe(kind, q, k, v, o, nbytes, grid, stream)
+                if st != 0:
+                    raise RuntimeError(f"launch failed with status {st}")
+            return
         st = getattr(self.lib, self.entry)(*self.sets[i], stream)
         if st != 0:
             raise RuntimeError(f"launch failed with status {st}")
 
     def run_timed(self, i, stream, events_ptr, cap):
+        if self.w.kind == "floor":
+            q, k, v, o, nbytes, grid = self.sets[i]
+            n = ctypes.c_int()
+            for kind in (0, 1):
+                ev = ctypes.c_void_p(events_ptr.value + kind * 2 * ctypes.sizeof(ctypes.c_void_p))
+                st = self.lib.mha_floor_probe_timed(kind, q, k, v, o, nbytes, grid, stream, ev, 2,
+                                                    ctypes.byref(n))
+                if st != 0 or n.value != 1:
+                    raise RuntimeError(f"timed launch failed with status {st}")
+            return
         f = getattr(self.lib, self.entry + "_timed")
         n = ctypes.c_int()
         st = f(*self.sets[i], stream, events_ptr, cap, ctypes.byref(n))
         if st != 0 or n.value != self.n_launches:
             raise RuntimeError(f"timed launch failed with status {st} ({n.value} launches)")
+
+
+def floor_grid(w):
+    """Workgroups of the attention launch at w's shape: one per (batch, head)
+    and block of 128 queries."""
+    return w.B * w.h * ((w.n_q + 127) // 128)
 
 
 def set_bytes(w):
@@ -383,7 +440,7 @@ def set_bytes(w):
         return e * w.B * w.h * (w.n_q * 64 * 4 + w.n_k * 64 * 4) + 8 * w.B * w.h * w.n_q
     if w.kind == "embed":
         return e * (w.vocab * w.d_model + w.B * w.n_q * w.d_model) + 4 * w.B * w.n_q
-    if w.kind == "sdpa":
+    if w.kind in ("sdpa", "floor"):
         return e * w.B * w.h * (w.n_q * (w.d_k + w.d_v) + w.n_k * (w.d_k + w.d_v))
     xs = w.B * w.n_q * w.d_model * (1 if w.self_attn else 1) + (0 if w.self_attn else w.B * w.n_k * w.d_model)
     ws = w.B * w.h * (w.n_q * w.d_k + w.n_k * (w.d_k + w.d_v) + w.n_q * w.d_v)
@@ -413,6 +470,12 @@ def parity_check(w, x, out):
     from head_attention_forward_amd.workloads import to_f64
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
     rows = "all"
+    if w.kind == "floor":  # the byte mover's output, bit for bit (no attention arithmetic)
+        import torch
+        want = x["Q"].view(torch.int16) ^ x["K"].view(torch.int16) ^ x["V"].view(torch.int16)
+        ok = bool(torch.equal(out.cpu().view(torch.int16), want))
+        return dict(max_abs=0.0 if ok else None, rel_l2=0.0 if ok else None, ok=ok,
+                    rows="all (xor of Q, K, V, bit for bit)")
     if w.kind == "mha_bwd":
         # whole gradients; bar of the block-gradient tests: rel-L2 <= 4u and
         # every element within 8u max|want|, u = 2^-8
@@ -498,6 +561,15 @@ def parity_check(w, x, out):
 
 # ----------------------------------------------------------------------------- cpu baseline
 
+def blas_threads():
+    """Threads of numpy's BLAS pool as it actually runs (threadpoolctl)."""
+    try:
+        from threadpoolctl import threadpool_info
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
+    except Exception:  # pragma: no cover
+        return 1
+
+
 def cpu_baseline(w, x, target_s):
     """The oracle, as it is, on a bounded sample of the workload, sized to
     roughly target_s seconds: whole multi-head blocks (the first b
@@ -506,11 +578,7 @@ def cpu_baseline(w, x, target_s):
     import numpy as np
     import oracle
     from head_attention_forward_amd.workloads import to_f64
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = blas_threads()
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
 
     if w.kind == "mha_bwd":
@@ -530,7 +598,7 @@ def cpu_baseline(w, x, target_s):
         run(n)
         t = time.perf_counter() - t0
         flops = block_bwd_flops(w) / w.B * n
-        return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+        return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=int(threads), host_cores=HOST_CORES, kind="oracle",
                     sample=f"{n} of {w.B} sequences, block backward; {t:.2f} s, numpy float64"
                            " (algorithmic flops of the block's backward)", seconds=round(t, 3))
     if w.kind == "bwd":
@@ -554,7 +622,7 @@ def cpu_baseline(w, x, target_s):
         run_pairs(n)
         t = time.perf_counter() - t0
         flops = 10.0 * bwd_pairs(w) / (w.B * w.h) * w.d_k * n
-        return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+        return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=int(threads), host_cores=HOST_CORES, kind="oracle",
                     sample=f"{n} of {w.B * w.h} (batch, head) pairs, backward; {t:.2f} s, numpy float64"
                            " (algorithmic backward flops: 5 products per visible pair)",
                     seconds=round(t, 3))
@@ -575,7 +643,7 @@ def cpu_baseline(w, x, target_s):
             run(w.B)
         t = time.perf_counter() - t0
         byts = float(2 * e * w.B * w.n_q * w.d_model + 4 * w.B * w.n_q) * reps
-        return dict(value=byts / t / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+        return dict(value=byts / t / 1e9, unit="GB/s", cores=int(threads), host_cores=HOST_CORES, kind="oracle",
                     sample=f"{w.B} of {w.B} sequences, {reps} passes; {t:.2f} s, numpy float64",
                     seconds=round(t, 3))
     if w.kind == "layer":
@@ -628,7 +696,7 @@ def cpu_baseline(w, x, target_s):
             break
     flops = unit_flops * units * reps
     sample = f"{units} of {n_units} {what}" + (f", {reps} passes" if reps > 1 else "")
-    return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+    return dict(value=flops / t / 1e12, unit="TFLOP/s", cores=int(threads), host_cores=HOST_CORES, kind="oracle",
                 sample=sample + f"; {t:.2f} s, numpy float64", seconds=round(t, 3))
 
 
@@ -650,6 +718,8 @@ KERNEL_SOURCES = {
     "transpose_bf16_kernel": ("transpose_bf16.hip", "mha_api.hip"),
     "gemm_splitk_reduce_kernel": ("gemm_bf16.hip", "mha_api.hip"),
     "gemm_group_kernel": ("gemm_bf16.hip", "mha_api.hip"),
+    "floor_empty_kernel": ("floor_probe.hip",),
+    "floor_xor3_kernel": ("floor_probe.hip",),
 }
 
 
@@ -824,9 +894,11 @@ def main():
     nominal = w.nominal_attention_flops()
     att = next((k for k in kernels if k["has_attention"]), None)
     value = nominal / (ms_step * 1e-3) / 1e12 if att is not None else None
+    pct_alg = (peak_percent(att["flops"], att["avg_us"])
+               if att is not None and w.dtype == "bf16" else None)
 
     cpu = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and w.kind != "floor":  # the floor probe runs no oracle arithmetic
         log("timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(w, x, args.cpu_seconds)
         log(f"cpu baseline: {cpu}")
@@ -840,7 +912,8 @@ def main():
         torch.cuda.synchronize()
         log(f"copy calibration: {n} bytes read, {n} bytes written")
 
-    kinds = {"mha": "multi-head block (projections + attention + output projection)",
+    kinds = {"floor": "launch floor: an empty kernel and a kernel moving the attention's bytes",
+             "mha": "multi-head block (projections + attention + output projection)",
              "sdpa": "bare attention",
              "embed": "token embedding x sqrt(d_model) + sinusoidal positional encoding",
              "bwd": "attention backward (dQ, dK, dV from dO, O and the row log-sum-exp)",
@@ -862,7 +935,16 @@ def main():
         "metric": METRIC,
         "value": None if value is None else round(value, 3),
         "unit": "TFLOP/s",
-        "pct_of_bf16_mfma_peak": None if value is None else round(100 * value / PEAK_BF16_TFLOPS, 3),
+        # The peak fraction counts the work the method does: the attention
+        # kernel's algorithmic flops (visible (query, key) pairs x 2(d_k + d_v),
+        # plus the fused projections when the kernel also projects) over that
+        # kernel's own average launch time.  The nominal dense count of the
+        # metric's formula doubles a causal attention's work, so its step-level
+        # fraction is given separately and labelled.
+        "pct_of_bf16_mfma_peak": None if pct_alg is None else round(pct_alg, 3),
+        "pct_of_bf16_mfma_peak_basis": None if pct_alg is None else
+            "algorithmic flops of the attention kernel over its average launch time",
+        "nominal_pct_of_bf16_mfma_peak_step": None if value is None else round(100 * value / PEAK_BF16_TFLOPS, 3),
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -879,11 +961,13 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/d_model) weights)",
         "config": cfg,
         # the kernel that runs the attention (fused with the input
-        # projections for short sequences); kernel_tflops counts all its flops
+        # projections for short sequences); algorithmic_flops counts all its flops
         "attention_kernel": None if att is None else dict(
             kernel=att["name"], avg_us=att["avg_us"],
+            algorithmic_flops=att["flops"],
+            algorithmic_tflops=att["tflops"],
             nominal_attention_tflops=round(nominal / (att["avg_us"] * 1e-6) / 1e12, 2),
-            kernel_tflops=att["tflops"], gbs=att["gbs"]),
+            gbs=att["gbs"]),
         "kernels": [{k: v for k, v in kk.items() if k not in ("peak_kind", "has_attention")} for kk in kernels],
         "roofline": roof,
         "cpu_baseline": cpu,

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(HERE, "libmha.so")
 
 DTYPE_BF16 = 0
 DTYPE_F32 = 1
-MAX_PADDED_BATCH = 256
+MAX_PADDED_BATCH = 1024
 
 STATUS = {
     0: "MHA_OK", -1: "MHA_ERR_NULL", -2: "MHA_ERR_DIM", -3: "MHA_ERR_MASK", -4: "MHA_ERR_KEYLEN",
@@ -27,7 +27,7 @@ STATUS = {
     -9: "MHA_ERR_EVENTS",
 }
 
-# Every symbol include/mha.h declares, with its ctypes signature.
+# Every symbol include/*.h declares, with its ctypes signature.
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _SIG = {
@@ -70,6 +70,9 @@ _SIG = {
     "mha_backward_timed": (_I, [_P] * 13 + [_I] * 8 + [_P, _I, _P, ctypes.c_size_t, _P,
                                                        ctypes.c_size_t, _P, _P, _I, _P]),
     "mha_backward_launches": (_I, [_I]),
+    # include/mha_probe.h (measurement aids)
+    "mha_floor_probe": (_I, [_I, _P, _P, _P, _P, ctypes.c_size_t, _I, _P]),
+    "mha_floor_probe_timed": (_I, [_I, _P, _P, _P, _P, ctypes.c_size_t, _I, _P, _P, _I, _P]),
 }
 
 _lib = None

@@ -10,6 +10,11 @@
 
 namespace mha {
 
+// Per-batch key lengths travel inside the kernel arguments, which hold at
+// most this many; the C-ABI layer splits a padded call over more batches
+// into launches of at most kLaunchBatch batches each.
+constexpr int kLaunchBatch = 256;
+
 // Strides are in elements; the innermost (feature) dimension is contiguous.
 struct AttnArgs {
   const void* Q;
@@ -27,11 +32,11 @@ struct AttnArgs {
   // Optional (bf16 kernels): row log-sum-exp, lse[(b*h + head)*n_q + i] =
   // ln(sum over visible keys j of exp(scale * q_i . k_j)); null: not written.
   float* lse;
-  int32_t key_len[MHA_MAX_PADDED_BATCH];
+  int32_t key_len[kLaunchBatch];
   // Batches by decreasing key length (padded only; the few-query kernel
   // takes the longest sequences first, so the last workgroups to start are
   // short ones).
-  uint8_t order[MHA_MAX_PADDED_BATCH];
+  uint8_t order[kLaunchBatch];
 };
 
 // Attention backward: dQ, dK, dV of O = softmax(Q K^T * scale + M) V from
@@ -60,7 +65,7 @@ struct BwdArgs {
   float scale;
   int causal;
   int padded;
-  int32_t key_len[MHA_MAX_PADDED_BATCH];
+  int32_t key_len[kLaunchBatch];
 };
 
 // One column segment of a projection GEMM: columns [0, width) of weight W
@@ -131,7 +136,7 @@ struct ProjAttnArgs {
   float scale;
   int causal;
   int padded;
-  int32_t key_len[MHA_MAX_PADDED_BATCH];
+  int32_t key_len[kLaunchBatch];
 };
 
 // Launch-time events: when `start`/`stop` are non-null they are recorded at

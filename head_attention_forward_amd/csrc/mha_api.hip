@@ -45,26 +45,11 @@ int check_attn_dims(int B, int h, int n_q, int n_k, int d_k, int d_v) {
   return MHA_OK;
 }
 
-void fill_mask(AttnArgs& a, int mask_kind, const int32_t* key_lengths) {
+void fill_mask(AttnArgs& a, int mask_kind) {
   a.causal = (mask_kind & MHA_MASK_CAUSAL) ? 1 : 0;
   a.padded = (mask_kind & MHA_MASK_KEY_PADDING) ? 1 : 0;
-  if (a.padded) {
-    for (int b = 0; b < a.B; ++b) {
-      a.key_len[b] = key_lengths[b];
-      a.order[b] = (uint8_t)b;
-    }
-    // stable insertion sort by decreasing length (B <= 256)
-    for (int i = 1; i < a.B; ++i) {
-      const uint8_t v = a.order[i];
-      int j = i;
-      while (j > 0 && key_lengths[a.order[j - 1]] < key_lengths[v]) {
-        a.order[j] = a.order[j - 1];
-        --j;
-      }
-      a.order[j] = v;
-    }
-  }
 }
+
 
 struct Workspace {
   void* Q;
@@ -127,6 +112,103 @@ struct Timer {
 };
 
 LaunchEvents next_events(Timer* t) { return t ? t->next() : LaunchEvents{}; }
+
+// The key lengths of batches [b0, b0 + a.B) into a launch's arguments
+// (a.B <= kLaunchBatch), with the batches ordered by decreasing length.
+void fill_lengths(AttnArgs& a, const int32_t* key_lengths, int b0) {
+  const int32_t* kl = key_lengths + b0;
+  for (int b = 0; b < a.B; ++b) {
+    a.key_len[b] = kl[b];
+    a.order[b] = (uint8_t)b;
+  }
+  // stable insertion sort by decreasing length
+  for (int i = 1; i < a.B; ++i) {
+    const uint8_t v = a.order[i];
+    int j = i;
+    while (j > 0 && kl[a.order[j - 1]] < kl[v]) {
+      a.order[j] = a.order[j - 1];
+      --j;
+    }
+    a.order[j] = v;
+  }
+}
+
+template <typename T>
+T* advance(T* p, int64_t elems, size_t elt) {
+  return p == nullptr ? p : (T*)((char*)p + elems * (int64_t)elt);
+}
+
+// Batches per launch: all of them, unless the key lengths ride along.
+int launch_batch(int B, int padded) { return padded ? kLaunchBatch : B; }
+
+// One attention launch per chunk of at most kLaunchBatch batches when the
+// key lengths ride along (a padded call), else one launch.  `a` describes
+// the whole call; each chunk gets its own base pointers and lengths.
+hipError_t launch_attention(const AttnArgs& a, const int32_t* key_lengths, int f32, hipStream_t s,
+                            Timer* tm) {
+  const size_t e = f32 ? 4 : 2;
+  const int step = launch_batch(a.B, a.padded);
+  for (int b0 = 0; b0 < a.B; b0 += step) {
+    AttnArgs c = a;
+    c.B = a.B - b0 < step ? a.B - b0 : step;
+    c.Q = advance(a.Q, b0 * a.q_sb, e);
+    c.K = advance(a.K, b0 * a.k_sb, e);
+    c.V = advance(a.V, b0 * a.v_sb, e);
+    c.O = advance(a.O, b0 * a.o_sb, e);
+    c.lse = advance(a.lse, (int64_t)b0 * a.h * a.n_q, sizeof(float));
+    if (c.padded) fill_lengths(c, key_lengths, b0);
+    const LaunchEvents le = next_events(tm);
+    const hipError_t err = f32 ? launch_attn_f32_d64(c, s, le) : launch_attn_bf16_d64(c, s, le);
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+// The backward's two launches per chunk (the dQ kernel writes the chunk's
+// row terms, the dK/dV kernel of the same chunk reads them).
+hipError_t launch_backward(const BwdArgs& a, const int32_t* key_lengths, hipStream_t s, Timer* tm) {
+  const int step = launch_batch(a.B, a.padded);
+  for (int b0 = 0; b0 < a.B; b0 += step) {
+    BwdArgs c = a;
+    c.B = a.B - b0 < step ? a.B - b0 : step;
+    const int64_t q_rows = (int64_t)b0 * a.h * a.n_q, k_rows = (int64_t)b0 * a.h * a.n_k;
+    c.Q = advance(a.Q, q_rows * 64, 2);   // dense head-major, head size 64
+    c.dO = advance(a.dO, q_rows * 64, 2);
+    c.K = advance(a.K, k_rows * 64, 2);
+    c.V = advance(a.V, k_rows * 64, 2);
+    c.O = advance(a.O, b0 * a.o_sb, 2);
+    c.dQ = advance(a.dQ, b0 * a.dq_sb, 2);
+    c.dK = advance(a.dK, b0 * a.dk_sb, 2);
+    c.dV = advance(a.dV, b0 * a.dv_sb, 2);
+    c.lse = advance(a.lse, q_rows, sizeof(float));
+    c.Dw = advance(a.Dw, q_rows, sizeof(float));
+    c.Lw = advance(a.Lw, q_rows, sizeof(float));
+    if (c.padded)
+      for (int b = 0; b < c.B; ++b) c.key_len[b] = key_lengths[b0 + b];
+    hipError_t err = launch_attn_bwd_dq(c, s, next_events(tm));
+    if (err != hipSuccess) return err;
+    err = launch_attn_bwd_dkdv(c, s, next_events(tm));
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+// The fused projection + attention kernel, one launch per chunk likewise.
+hipError_t launch_fused(const ProjAttnArgs& a, const int32_t* key_lengths, hipStream_t s, Timer* tm) {
+  const int step = launch_batch(a.B, a.padded);
+  for (int b0 = 0; b0 < a.B; b0 += step) {
+    ProjAttnArgs c = a;
+    c.B = a.B - b0 < step ? a.B - b0 : step;
+    c.Xq = advance(a.Xq, (int64_t)b0 * a.n_q * a.d_model, 2);
+    c.Xkv = advance(a.Xkv, (int64_t)b0 * a.n_k * a.d_model, 2);
+    c.O = advance(a.O, (int64_t)b0 * a.n_q * a.h * 64, 2);
+    if (c.padded)
+      for (int b = 0; b < c.B; ++b) c.key_len[b] = key_lengths[b0 + b];
+    const hipError_t err = launch_proj_attn_bf16(c, s, next_events(tm));
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
 
 // Short sequences (both <= 128 rows) with d_model a multiple of 64 take the
 // fused projection + attention kernel, then the output projection.
@@ -214,8 +296,8 @@ int do_attend(int B, int n_q, int n_k, int h, int d_k, int d_v, int mask_kind,
   a.n_k = n_k;
   a.scale = 1.0f / sqrtf((float)d_k);
   a.lse = lse;
-  fill_mask(a, mask_kind, key_lengths);
-  return launch_status(launch_attn_bf16_d64(a, stream, next_events(tm)));
+  fill_mask(a, mask_kind);
+  return launch_status(launch_attention(a, key_lengths, 0, stream, tm));
 }
 
 int do_project_out(const void* Wo, void* Y, int B, int n_q, int d_model, int h, int d_v,
@@ -524,11 +606,8 @@ static int sdpa_impl(const void* Q, const void* K, const void* V, void* O, int B
   a.n_q = n_q;
   a.n_k = n_k;
   a.scale = scale;
-  fill_mask(a, mask_kind, key_lengths);
-  const LaunchEvents le = next_events(tm);
-  const hipError_t e = dtype == MHA_DTYPE_BF16 ? launch_attn_bf16_d64(a, stream, le)
-                                               : launch_attn_f32_d64(a, stream, le);
-  return launch_status(e);
+  fill_mask(a, mask_kind);
+  return launch_status(launch_attention(a, key_lengths, dtype == MHA_DTYPE_F32, stream, tm));
 }
 
 int sdpa_forward(const void* Q, const void* K, const void* V, void* O, int B, int h, int n_q,
@@ -617,9 +696,7 @@ static int mha_impl(const void* X_q, const void* X_kv, const void* Wq, const voi
     pa.scale = 1.0f / sqrtf((float)d_k);
     pa.causal = (mask_kind & MHA_MASK_CAUSAL) ? 1 : 0;
     pa.padded = (mask_kind & MHA_MASK_KEY_PADDING) ? 1 : 0;
-    if (pa.padded)
-      for (int b = 0; b < B; ++b) pa.key_len[b] = key_lengths[b];
-    st = launch_status(launch_proj_attn_bf16(pa, stream, next_events(tm)));
+    st = launch_status(launch_fused(pa, key_lengths, stream, tm));
   } else {
     st = do_project_in(X_q, X_kv, Wq, Wk, Wv, B, n_q, n_k, d_model, h, d_k, d_v, w, stream, tm);
     if (st != MHA_OK) return st;
@@ -825,8 +902,8 @@ int sdpa_forward_lse(const void* Q, const void* K, const void* V, void* O, float
   a.n_q = n_q;
   a.n_k = n_k;
   a.scale = scale;
-  fill_mask(a, mask_kind, key_lengths);
-  return launch_status(launch_attn_bf16_d64(a, stream, {}));
+  fill_mask(a, mask_kind);
+  return launch_status(launch_attention(a, key_lengths, 0, stream, nullptr));
 }
 
 size_t sdpa_backward_workspace_bytes(int B, int h, int n_q) {
@@ -878,11 +955,7 @@ static int bwd_impl(const void* Q, const void* K, const void* V, const void* O, 
   a.scale = scale;
   a.causal = (mask_kind & MHA_MASK_CAUSAL) ? 1 : 0;
   a.padded = (mask_kind & MHA_MASK_KEY_PADDING) ? 1 : 0;
-  if (a.padded)
-    for (int b = 0; b < B; ++b) a.key_len[b] = key_lengths[b];
-  st = launch_status(launch_attn_bwd_dq(a, stream, next_events(tm)));
-  if (st != MHA_OK) return st;
-  return launch_status(launch_attn_bwd_dkdv(a, stream, next_events(tm)));
+  return launch_status(launch_backward(a, key_lengths, stream, tm));
 }
 
 int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -1052,11 +1125,7 @@ static int mha_bwd_impl(const void* X_q, const void* X_kv, const void* Wq, const
     a.scale = 1.0f / sqrtf((float)d_k);
     a.causal = (mask_kind & MHA_MASK_CAUSAL) ? 1 : 0;
     a.padded = (mask_kind & MHA_MASK_KEY_PADDING) ? 1 : 0;
-    if (a.padded)
-      for (int b = 0; b < B; ++b) a.key_len[b] = key_lengths[b];
-    st = launch_status(launch_attn_bwd_dq(a, stream, next_events(tm)));
-    if (st != MHA_OK) return st;
-    st = launch_status(launch_attn_bwd_dkdv(a, stream, next_events(tm)));
+    st = launch_status(launch_backward(a, key_lengths, stream, tm));
     if (st != MHA_OK) return st;
   }
   if (self_attn) {

@@ -108,6 +108,15 @@ WORKLOADS = {
         mask=MASK_NONE,
         description="bare attention at the encoder block's shape, bf16, B=32 h=8 n=100 d=64, "
                     "unmasked"),
+    # The fixed cost of a launch at that shape, measured the same way: a
+    # kernel that does nothing over the attention's grid (32 x 8 workgroups of
+    # 256 threads), and one that only reads Q, K, V (9.8 MB) and writes an
+    # output of O's size (3.3 MB) -- the floor under the short attention.
+    "launch_floor_encoder_sdpa": Workload(
+        "launch_floor_encoder_sdpa", "floor", "bf16", B=32, n_q=100, n_k=100, h=8, d_k=64, d_v=64,
+        mask=MASK_NONE,
+        description="launch floor at the encoder attention's shape: an empty kernel and a "
+                    "kernel moving the same 13.1 MB, 256 workgroups of 256 threads"),
     "long_causal_sdpa": Workload(
         "long_causal_sdpa", "sdpa", "bf16", B=4, n_q=4096, n_k=4096, h=16, d_k=64, d_v=64,
         mask=MASK_CAUSAL,
@@ -168,6 +177,7 @@ def generate(w: Workload, seed: int = 0):
 
     sdpa: Q [B][h][n_q][d_k], K [B][h][n_k][d_k], V [B][h][n_k][d_v], scale,
           key_lengths (int32 [B] or None).
+    floor: the same draws as sdpa (the bytes a launch of that shape moves).
     bwd:  as sdpa, then the upstream gradient dO [B][h][n_q][d_v].
     mha_bwd: as mha, then the upstream gradient dY [B][n_q][d_model].
     mha:  X_q [B][n_q][d_model], X_kv (the same tensor object for
@@ -182,7 +192,7 @@ def generate(w: Workload, seed: int = 0):
     g.manual_seed(seed)
     dt = w.torch_dtype
     out = {}
-    if w.kind in ("sdpa", "bwd"):
+    if w.kind in ("sdpa", "bwd", "floor"):
         out["Q"] = _normal(g, (w.B, w.h, w.n_q, w.d_k), 1.0, dt)
         out["K"] = _normal(g, (w.B, w.h, w.n_k, w.d_k), 1.0, dt)
         out["V"] = _normal(g, (w.B, w.h, w.n_k, w.d_v), 1.0, dt)

@@ -77,9 +77,11 @@ extern "C" {
 #define MHA_DTYPE_BF16  0
 #define MHA_DTYPE_F32   1
 
-/* Largest batch accepted together with key padding (lengths travel as kernel
- * arguments). */
-#define MHA_MAX_PADDED_BATCH 256
+/* Largest batch accepted together with key padding.  The lengths travel to
+ * the kernels inside their argument blocks, 256 batches per launch: a padded
+ * call over more batches is split on the host into launches of at most 256
+ * batches each (a *_timed call then records one event pair per launch). */
+#define MHA_MAX_PADDED_BATCH 1024
 
 /*
  * sdpa_forward -- bare scaled dot-product attention for every (batch, head).

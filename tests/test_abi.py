@@ -94,8 +94,14 @@ def test_sdpa_rejections(L):
     assert sdpa(L, mask=2, kl=p) == KEYLEN             # length 0
     p, keep = keylens(9, 3)
     assert sdpa(L, mask=2, kl=p) == KEYLEN             # length > n_k
-    p, keep = keylens(*([4] * 300))
-    assert sdpa(L, mask=2, kl=p, B=300, h=1) == UNSUP  # batch above the padded limit
+    p, keep = keylens(*([4] * 1025))
+    assert sdpa(L, mask=2, kl=p, B=1025, h=1) == UNSUP  # batch above the padded limit
+    # 1024 padded batches pass the batch limit: the check reaches the last
+    # length (0 here, so the call stops at KEYLEN before any launch)
+    p, keep = keylens(*([4] * 1023 + [0]))
+    assert sdpa(L, mask=2, kl=p, B=1024, h=1) == KEYLEN
+    assert mha(L, mask=2, kl=p, B=1024) == KEYLEN
+    assert mha(L, mask=2, kl=p, B=1025) == UNSUP
     assert sdpa(L, dtype=5) == UNSUP
     assert sdpa(L, Q=MISALIGNED) == UNSUP
 
@@ -346,3 +352,18 @@ def test_mha_backward_rejections(L):
     assert bwd(dtype=F32) == UNSUP
     assert L.mha_forward_train(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, B, n, n, dm, h, 64, 64, 0,
                                None, BF16, FAKE, tws - 256, None) == WS
+
+
+def test_floor_probe_rejections(L):
+    P = ctypes.c_void_p
+    # unknown kind, bad grid, null buffers, ragged or empty byte counts, misalignment
+    assert L.mha_floor_probe(7, FAKE, FAKE, FAKE, FAKE2, 4096, 16, None) == UNSUP
+    assert L.mha_floor_probe(0, None, None, None, None, 0, 0, None) == DIM
+    assert L.mha_floor_probe(0, None, None, None, None, 0, (1 << 20) + 1, None) == DIM
+    assert L.mha_floor_probe(1, None, FAKE, FAKE, FAKE2, 4096, 16, None) == NULL
+    assert L.mha_floor_probe(1, FAKE, FAKE, FAKE, FAKE2, 4100, 16, None) == DIM
+    assert L.mha_floor_probe(1, FAKE, FAKE, FAKE, FAKE2, 0, 16, None) == DIM
+    assert L.mha_floor_probe(1, MISALIGNED, FAKE, FAKE, FAKE2, 4096, 16, None) == UNSUP
+    n = ctypes.c_int(-1)
+    assert L.mha_floor_probe_timed(1, FAKE, FAKE, FAKE, FAKE2, 4096, 16, None, None, 2,
+                                   ctypes.byref(n)) == -9

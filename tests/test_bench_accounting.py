@@ -81,3 +81,28 @@ def test_gpus_above_one_is_refused(monkeypatch, capsys):
         bench.main()
     assert e.value.code == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_peak_fraction_uses_algorithmic_causal_flops():
+    """The long causal attention does (n + 1) / (2n) of the nominal dense
+    work; its peak fraction must count only that.  At 110 us, 137.5 GFLOP
+    is 49.7% of 2516.6 TFLOP/s, while the nominal count would claim 99%."""
+    w = WORKLOADS["long_causal_sdpa"]
+    f, _ = bench.attention_accounting(w, None)
+    pct = bench.peak_percent(f, 110.0)
+    assert abs(pct - 100 * f / 110e-6 / 1e12 / 2516.6) < 1e-9
+    assert 49.5 < pct < 50.0
+    nominal = bench.peak_percent(w.nominal_attention_flops(), 110.0)
+    assert abs(nominal / pct - 2 * 4096 / 4097) < 1e-9
+
+
+def test_headline_workload_is_long_causal():
+    assert bench.DEFAULT_WORKLOAD == "long_causal_sdpa"
+    w = WORKLOADS[bench.DEFAULT_WORKLOAD]
+    assert (w.B, w.h, w.n_q, w.n_k, w.d_k, w.mask) == (4, 16, 4096, 4096, 64, 1)
+
+
+def test_oracle_threads_follow_host_cores():
+    import os
+    assert bench.HOST_CORES == len(os.sched_getaffinity(0))
+    assert int(os.environ["OMP_NUM_THREADS"]) >= 1

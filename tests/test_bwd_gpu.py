@@ -71,6 +71,8 @@ CASES = [
     (1, 1, 1, 1, 0, None, "one query, one key"),
     (1, 2, 1, 300, 0, None, "one query over 300 keys"),
     (4, 8, 100, 100, 0, None, "the encoder block's heads"),
+    # more padded batches than one launch carries lengths for (two launches per kernel)
+    (300, 1, 20, 20, 3, [1 + (i * 7) % 20 for i in range(300)], "300 padded batches"),
 ]
 
 

@@ -151,6 +151,13 @@ def test_sdpa_long_causal_sampled(dev):
                                 w.mask, None, idx)
     got = O[idx[:, 0], idx[:, 1], idx[:, 2]]
     assert_bf16_close(got, want, w.name + " sampled rows")
+    # Two whole heads, every query tile: every row of the first and of the
+    # last (batch, head) against the oracle, element by element.
+    Q64, K64, V64 = to_f64(x["Q"]), to_f64(x["K"]), to_f64(x["V"])
+    for b, hh in ((0, 0), (w.B - 1, w.h - 1)):
+        sl = lambda t: t[b:b + 1, hh:hh + 1]  # noqa: E731
+        want_h = oracle.sdpa_ref(sl(Q64), sl(K64), sl(V64), x["scale"], w.mask, None)
+        assert_bf16_close(O[b:b + 1, hh:hh + 1], want_h, f"{w.name} whole head ({b}, {hh})")
     # Causal row 0 sees only key 0: exactly value row 0.
     assert torch.equal(O[:, :, 0].cpu(), x["V"][:, :, 0])
     # Every output row is a convex combination of V rows: coordinates within the
@@ -229,20 +236,35 @@ def test_sdpa_f32_edges(dev, B, h, n_q, n_k, mask, kl):
     assert_f32_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"f32 edge {n_q}x{n_k} m{mask}")
 
 
-@pytest.mark.parametrize("mask", [2, 3])
-def test_sdpa_bf16_max_padded_batch(dev, mask):
-    """The largest batch that takes per-batch key lengths (256, passed in the
-    kernel arguments): every batch's lengths are honoured."""
-    B, h, n = 256, 1, 24
+@pytest.mark.parametrize("B,mask", [(256, 2), (256, 3), (257, 3), (1024, 2), (1024, 3)])
+def test_sdpa_bf16_max_padded_batch(dev, B, mask):
+    """Per-batch key lengths up to the largest padded batch (1024; they
+    travel in the kernel arguments, 256 batches per launch, so 257 and 1024
+    take two and four launches): every batch's lengths are honoured."""
+    h, n = 1, 24
     Q, K, V = sdpa_inputs(B, h, n, n, torch.bfloat16, seed=31)
     g = torch.Generator("cpu")
     g.manual_seed(32)
     kl = torch.randint(1, n + 1, (B,), generator=g).tolist()
     kl[0], kl[-1] = 1, n
-    announce("sdpa max padded batch", mask)
+    announce("sdpa max padded batch", B, mask)
     O = run_sdpa(dev, Q, K, V, 0.125, mask, kl)
     torch.cuda.synchronize()
-    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"B=256 mask {mask}")
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"B={B} mask {mask}")
+
+
+def test_sdpa_decode_padded_batch_1024(dev):
+    """One query per sequence over a 300-key cache for 1024 sequences with
+    their own cache lengths (the few-query kernel, four launches of 256)."""
+    B, h, n_k = 1024, 2, 300
+    Q, K, V = sdpa_inputs(B, h, 1, n_k, torch.bfloat16, seed=47)
+    g = torch.Generator("cpu").manual_seed(48)
+    kl = torch.randint(1, n_k + 1, (B,), generator=g).tolist()
+    kl[0], kl[255], kl[256], kl[-1] = 1, n_k, 2, n_k
+    announce("sdpa decode padded B=1024")
+    O = run_sdpa(dev, Q, K, V, 0.125, 2, kl)
+    torch.cuda.synchronize()
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, 2, kl), "decode B=1024")
 
 
 def test_mha_max_padded_batch_and_fused_boundary(dev):
@@ -250,6 +272,8 @@ def test_mha_max_padded_batch_and_fused_boundary(dev):
     the fused kernel's 128-row limit (n = 129: the staged path)."""
     cases = [
         dict(B=256, n_q=16, n_k=16, d_model=64, h=1, mask=3, self_attn=True, key_len_range=(1, 16)),
+        dict(B=1024, n_q=16, n_k=24, d_model=64, h=1, mask=2, self_attn=False, key_len_range=(1, 24)),
+        dict(B=300, n_q=136, n_k=136, d_model=64, h=1, mask=3, self_attn=True, key_len_range=(1, 136)),
         dict(B=2, n_q=129, n_k=129, d_model=128, h=2, mask=1, self_attn=True),
         dict(B=2, n_q=128, n_k=129, d_model=128, h=2, mask=2, self_attn=False, key_len_range=(1, 129)),
     ]
