@@ -60,6 +60,7 @@ _SIG = {
                               _P]),
     "sdpa_backward_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
     "sdpa_backward": (_I, [_P] * 9 + [_I] * 6 + [ctypes.c_float, _I, _P, _I, _P, ctypes.c_size_t, _P]),
+    "sdpa_backward_noalloc": (_I, [_P] * 9 + [_I] * 6 + [ctypes.c_float, _I, _P, _I, _P]),
     "sdpa_backward_timed": (_I, [_P] * 9 + [_I] * 6 + [ctypes.c_float, _I, _P, _I, _P,
                                                       ctypes.c_size_t, _P, _P, _I, _P]),
     "mha_train_workspace_bytes": (ctypes.c_size_t, [_I] * 7),

@@ -190,6 +190,11 @@ hipError_t launch_transpose_bf16(const TransposeBatch& tb, hipStream_t s, Launch
 hipError_t launch_embed_positional(const EmbedArgs& a, int f32, hipStream_t s, LaunchEvents ev = {});
 bool proj_attn_supported(int n_q, int n_k, int d_model);
 hipError_t launch_proj_attn_bf16(const ProjAttnArgs& a, hipStream_t s, LaunchEvents ev = {});
+// The argument checks of sdpa_backward (everything but the workspace), host only.
+int check_backward_args(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                        const float* lse, const void* dQ, const void* dK, const void* dV, int B,
+                        int h, int n_q, int n_k, int d_k, int d_v, float scale, int mask_kind,
+                        const int32_t* key_lengths, int dtype);
 // One fixed tile configuration (index into the instantiated set); for sweeps.
 hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, LaunchEvents ev = {});
 

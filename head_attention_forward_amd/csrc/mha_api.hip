@@ -550,6 +550,26 @@ int mha_bwd_launch_count(bool self_attn) { return self_attn ? 6 : 7; }
 
 using namespace mha;
 
+namespace mha {
+int check_backward_args(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                        const float* lse, const void* dQ, const void* dK, const void* dV, int B,
+                        int h, int n_q, int n_k, int d_k, int d_v, float scale, int mask_kind,
+                        const int32_t* key_lengths, int dtype) {
+  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV) return MHA_ERR_NULL;
+  int st = check_attn_dims(B, h, n_q, n_k, d_k, d_v);
+  if (st != MHA_OK) return st;
+  if (!(isfinite(scale) && scale > 0.f)) return MHA_ERR_SCALE;
+  st = check_mask(mask_kind, B, n_q, n_k, key_lengths);
+  if (st != MHA_OK) return st;
+  if (dtype != MHA_DTYPE_BF16) return MHA_ERR_UNSUPPORTED;
+  const void* p16[] = {Q, K, V, O, dO, dQ, dK, dV};
+  for (const void* p : p16)
+    if (!aligned16(p)) return MHA_ERR_UNSUPPORTED;
+  if ((uintptr_t)lse & 3u) return MHA_ERR_UNSUPPORTED;
+  return MHA_OK;
+}
+}  // namespace mha
+
 extern "C" {
 
 const char* mha_status_str(int status) {
@@ -911,22 +931,15 @@ size_t sdpa_backward_workspace_bytes(int B, int h, int n_q) {
   return 2 * round_up((size_t)4 * B * h * n_q);
 }
 
+
 static int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                     const float* lse, void* dQ, void* dK, void* dV, int B, int h, int n_q, int n_k,
                     int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lengths,
                     int dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
                     Timer* tm) {
-  if (!Q || !K || !V || !O || !dO || !lse || !dQ || !dK || !dV) return MHA_ERR_NULL;
-  int st = check_attn_dims(B, h, n_q, n_k, d_k, d_v);
+  const int st = check_backward_args(Q, K, V, O, dO, lse, dQ, dK, dV, B, h, n_q, n_k, d_k, d_v, scale,
+                                     mask_kind, key_lengths, dtype);
   if (st != MHA_OK) return st;
-  if (!(isfinite(scale) && scale > 0.f)) return MHA_ERR_SCALE;
-  st = check_mask(mask_kind, B, n_q, n_k, key_lengths);
-  if (st != MHA_OK) return st;
-  if (dtype != MHA_DTYPE_BF16) return MHA_ERR_UNSUPPORTED;
-  const void* p16[] = {Q, K, V, O, dO, dQ, dK, dV};
-  for (const void* p : p16)
-    if (!aligned16(p)) return MHA_ERR_UNSUPPORTED;
-  if ((uintptr_t)lse & 3u) return MHA_ERR_UNSUPPORTED;
   const size_t row_terms = round_up((size_t)4 * B * h * n_q);
   if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0 ||
       workspace_bytes < 2 * row_terms)

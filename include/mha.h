@@ -286,6 +286,24 @@ int sdpa_backward(const void* Q, const void* K, const void* V, const void* O, co
                   float scale, int mask_kind, const int32_t* key_lengths, int dtype,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * sdpa_backward_noalloc -- sdpa_backward for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving or training
+ * loops, harnesses that forbid hipMalloc.  Same arguments, checks and
+ * kernels as sdpa_backward, without the workspace: the row terms live in an
+ * 8 MiB device array of the library (one per GPU, held until the process
+ * ends), so B * h * n_q may be at most 2^20 (else MHA_ERR_WORKSPACE, before
+ * any HIP call).  The array's device address is looked up on the first call
+ * on each device; MHA_ERR_HIP if that lookup fails.  Calls on one GPU share
+ * the array: calls that overlap in time on one GPU (different streams) race
+ * and must be ordered by the caller.  Allocates nothing.
+ */
+int sdpa_backward_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                          const void* dO, const float* lse, void* dQ, void* dK, void* dV,
+                          int B, int h, int n_q, int n_k, int d_k, int d_v,
+                          float scale, int mask_kind, const int32_t* key_lengths, int dtype,
+                          hipStream_t stream);
+
 /* sdpa_backward with launch events (2 launches), as the other _timed variants. */
 int sdpa_backward_timed(const void* Q, const void* K, const void* V, const void* O,
                         const void* dO, const float* lse, void* dQ, void* dK, void* dV,

@@ -367,3 +367,20 @@ def test_floor_probe_rejections(L):
     n = ctypes.c_int(-1)
     assert L.mha_floor_probe_timed(1, FAKE, FAKE, FAKE, FAKE2, 4096, 16, None, None, 2,
                                    ctypes.byref(n)) == -9
+
+
+def test_backward_noalloc_rejections(L):
+    """The allocation-free backward keeps its row terms in an 8 MiB device
+    array: at most 2^20 query rows; every check is made before any HIP call
+    (the device-address lookup comes after them)."""
+    def call(B=2, h=2, n_q=8, n_k=8, Q=FAKE, d_k=64, scale=0.125, mask=0, kl=None, dtype=BF16):
+        return L.sdpa_backward_noalloc(Q, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE2, FAKE2, FAKE2, B, h,
+                                       n_q, n_k, d_k, 64, scale, mask, kl, dtype, None)
+    assert call(Q=None) == NULL
+    assert call(B=0) == DIM
+    assert call(d_k=32) == UNSUP
+    assert call(scale=0.0) == SCALE
+    assert call(mask=2) == KEYLEN
+    assert call(dtype=F32) == UNSUP
+    assert call(B=1, h=16, n_q=(1 << 16) + 1, n_k=8) == WS     # 2^20 + 16 query rows
+    assert call(B=4, h=16, n_q=1 << 15, n_k=8) == WS           # 2^21 query rows
