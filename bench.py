@@ -95,6 +95,9 @@ def step_launches(w):
         return 1
     if w.kind == "floor":
         return 2
+    if w.kind == "decode":
+        from head_attention_forward_amd import _binding as bnd
+        return int(bnd.lib().sdpa_decode_launches(w.B, w.h, w.n_q, w.n_k, w.mask))
     if w.kind == "bwd":
         return 2
     if w.kind == "mha_bwd":
@@ -128,6 +131,16 @@ def kernel_plan(w, n_launches=None):
         plan.append(dict(name="xor3_copy", flops=0.0,
                          bytes=float(e * B * h * (nq * dk + nk * (dk + dv) + nq * dv)),
                          peak_kind="hbm", has_attention=False))
+        return plan, None
+    if w.kind == "decode":
+        plan.append(dict(name="attention", flops=0.0, bytes=0.0, peak_kind="mfma", has_attention=True))
+        if (n_launches or step_launches(w)) == 2:
+            # the partial states (m, l and 32 accumulators per lane, 64 lanes per
+            # workgroup) of every split, read once; O written
+            from head_attention_forward_amd import _binding as bnd
+            nb = int(bnd.lib().sdpa_decode_workspace_bytes(B, h, nq, nk))
+            plan.append(dict(name="decode_merge", flops=0.0, bytes=float(nb + e * B * h * nq * dv),
+                             peak_kind="hbm", has_attention=False))
         return plan, None
     if w.kind == "sdpa":
         plan.append(dict(name="attention", flops=0.0, bytes=0.0,
@@ -294,6 +307,15 @@ class Step:
                 self.keep.append((Q, K, V, O))
                 self.sets.append((P(Q.data_ptr()), P(K.data_ptr()), P(V.data_ptr()), P(O.data_ptr()),
                                   Q.numel() * Q.element_size(), floor_grid(w)))
+            elif w.kind == "decode":
+                Q, K, V = (x[k].to(dev) for k in ("Q", "K", "V"))
+                O = torch.empty((w.B, w.h, w.n_q, w.d_v), dtype=Q.dtype, device=dev)
+                nbytes = int(self.lib.sdpa_decode_workspace_bytes(w.B, w.h, w.n_q, w.n_k))
+                ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+                self.keep.append((Q, K, V, O, ws))
+                self.sets.append((P(Q.data_ptr()), P(K.data_ptr()), P(V.data_ptr()), P(O.data_ptr()),
+                                  w.B, w.h, w.n_q, w.n_k, w.d_k, w.d_v, float(x["scale"]), w.mask,
+                                  self.kl, bnd.DTYPE_BF16, P(ws.data_ptr()), nbytes))
             elif w.kind == "sdpa":
                 Q, K, V = (x[k].to(dev) for k in ("Q", "K", "V"))
                 O = torch.empty((w.B, w.h, w.n_q, w.d_v), dtype=Q.dtype, device=dev)
@@ -378,7 +400,7 @@ class Step:
                                   w.B, w.n_q, w.n_k, w.d_model, w.h, w.d_k, w.d_v, w.mask, self.kl,
                                   bnd.DTYPE_BF16, P(ws.data_ptr()), ws.numel()))
         self.n_launches = step_launches(w)
-        names = {"floor": "mha_floor_probe",
+        names = {"floor": "mha_floor_probe", "decode": "sdpa_decode",
                  "sdpa": "sdpa_forward", "mha": "mha_forward", "layer": "encoder_layer_forward",
                  "embed": "embed_positional_forward", "bwd": "sdpa_backward",
                  "mha_bwd": "mha_backward"}
@@ -440,7 +462,7 @@ def set_bytes(w):
         return e * w.B * w.h * (w.n_q * 64 * 4 + w.n_k * 64 * 4) + 8 * w.B * w.h * w.n_q
     if w.kind == "embed":
         return e * (w.vocab * w.d_model + w.B * w.n_q * w.d_model) + 4 * w.B * w.n_q
-    if w.kind in ("sdpa", "floor"):
+    if w.kind in ("sdpa", "decode", "floor"):
         return e * w.B * w.h * (w.n_q * (w.d_k + w.d_v) + w.n_k * (w.d_k + w.d_v))
     xs = w.B * w.n_q * w.d_model * (1 if w.self_attn else 1) + (0 if w.self_attn else w.B * w.n_k * w.d_model)
     ws = w.B * w.h * (w.n_q * w.d_k + w.n_k * (w.d_k + w.d_v) + w.n_q * w.d_v)
@@ -707,7 +729,10 @@ def cpu_baseline(w, x, target_s):
 _COMMON_SOURCES = ("device.h", "kernels.h")
 KERNEL_SOURCES = {
     "attn_fwd_bf16_d64_kernel": ("attn_bf16.hip", "attn_decode_bf16.hip", "wave_attention.h"),
-    "attn_decode_bf16_d64_kernel": ("attn_decode_bf16.hip", "attn_bf16.hip", "wave_attention.h"),
+    "attn_decode_bf16_d64_kernel": ("attn_decode_bf16.hip", "attn_bf16.hip", "wave_attention.h",
+                                    "mha_api.hip", "device_info.hip"),
+    "attn_decode_merge_kernel": ("attn_decode_bf16.hip", "wave_attention.h", "mha_api.hip",
+                                 "device_info.hip"),
     "attn_fwd_f32_d64_kernel": ("attn_f32.hip",),
     "proj_attn_bf16_kernel": ("proj_attn_bf16.hip", "wave_attention.h", "mha_api.hip"),
     "gemm_bf16_kernel": ("gemm_bf16.hip", "mha_api.hip"),
@@ -915,6 +940,7 @@ def main():
     kinds = {"floor": "launch floor: an empty kernel and a kernel moving the attention's bytes",
              "mha": "multi-head block (projections + attention + output projection)",
              "sdpa": "bare attention",
+             "decode": "bare attention, few queries over long caches (sdpa_decode)",
              "embed": "token embedding x sqrt(d_model) + sinusoidal positional encoding",
              "bwd": "attention backward (dQ, dK, dV from dO, O and the row log-sum-exp)",
              "mha_bwd": "multi-head block backward (dX, dW^Q, dW^K, dW^V, dW^O)",

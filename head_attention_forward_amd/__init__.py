@@ -22,6 +22,7 @@ from ._binding import (  # noqa: F401
     mha_project_in,
     mha_project_out,
     sdpa_backward,
+    sdpa_decode,
     sdpa_forward,
     sdpa_forward_lse,
     workspace_bytes,

@@ -33,6 +33,12 @@ _I = ctypes.c_int
 _SIG = {
     "sdpa_forward": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _I, _P]),
     "mha_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I, _I]),
+    "sdpa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _I, _P,
+                         ctypes.c_size_t, _P]),
+    "sdpa_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I]),
+    "sdpa_decode_launches": (_I, [_I, _I, _I, _I, _I]),
+    "sdpa_decode_timed": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, ctypes.c_float, _I, _P, _I, _P,
+                               ctypes.c_size_t, _P, _P, _I, _P]),
     "mha_forward": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P, _I, _P,
                          ctypes.c_size_t, _P]),
     "mha_project_in": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _P,
@@ -167,6 +173,36 @@ def sdpa_forward(Q, K, V, scale=None, mask_kind=0, key_lengths=None, out=None, s
                             B, h, n_q, n_k, d_k, d_v, float(scale), int(mask_kind), kl,
                             _dtype_code(Q), _stream(stream))
     _check("sdpa_forward", st)
+    return out
+
+
+def sdpa_decode(Q, K, V, scale=None, mask_kind=0, key_lengths=None, out=None, workspace=None,
+                stream=None):
+    """sdpa_forward for few queries over long cached key ranges, with a
+    workspace so that the keys of each (batch, head) can be split over
+    several workgroups when B * h is small.  Arguments and result as
+    sdpa_forward; `workspace` (uint8 GPU tensor) is allocated if omitted."""
+    B, h, n_q, d_k = Q.shape
+    n_k, d_v = K.shape[2], V.shape[3]
+    if K.shape != (B, h, n_k, d_k) or V.shape != (B, h, n_k, d_v):
+        raise ValueError("Q, K, V shapes disagree")
+    if not (Q.dtype == K.dtype == V.dtype):
+        raise TypeError("Q, K, V must share a dtype")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_k)
+    if out is None:
+        out = torch.empty((B, h, n_q, d_v), dtype=Q.dtype, device=Q.device)
+    elif out.shape != (B, h, n_q, d_v) or out.dtype != Q.dtype:
+        raise ValueError("out has the wrong shape or dtype")
+    nbytes = int(lib().sdpa_decode_workspace_bytes(B, h, n_q, n_k))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=Q.device)
+    arr, kl = _key_lengths(mask_kind, key_lengths, B)
+    st = lib().sdpa_decode(_dev(Q, "Q"), _dev(K, "K"), _dev(V, "V"), _dev(out, "out"),
+                           B, h, n_q, n_k, d_k, d_v, float(scale), int(mask_kind), kl,
+                           _dtype_code(Q), _dev(workspace, "workspace"), workspace.numel(),
+                           _stream(stream))
+    _check("sdpa_decode", st)
     return out
 
 

@@ -45,9 +45,14 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_bf16_d64_kernel(const Att
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31;
 
-  // Workgroups in dispatch order take the longest sequences first.
-  const int slot = __builtin_amdgcn_readfirstlane((int)blockIdx.x / a.h);
-  const int hh = (int)blockIdx.x - slot * a.h;
+  // Workgroups in dispatch order take the longest sequences first.  With
+  // splits > 1, the `splits` consecutive workgroups of a (batch, head) share
+  // its key tiles: workgroup sp, wave w takes tiles sp * NW + w + k * NW * splits.
+  const int S = a.splits > 1 ? a.splits : 1;
+  const int grp = __builtin_amdgcn_readfirstlane((int)blockIdx.x / S);
+  const int sp = (int)blockIdx.x - grp * S;
+  const int slot = __builtin_amdgcn_readfirstlane(grp / a.h);
+  const int hh = grp - slot * a.h;
   const int b = __builtin_amdgcn_readfirstlane(a.padded ? (int)a.order[slot] : slot);
   const __bf16* Qp = wave_uniform((const __bf16*)a.Q + b * a.q_sb + hh * a.q_sh);
   const char* Kp = wave_uniform((const char*)((const __bf16*)a.K + b * a.k_sb + hh * a.k_sh));
@@ -100,8 +105,9 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_bf16_d64_kernel(const Att
   WaveAttention wa;
   wa.init(lane, a.scale);
   wa.load_q(Qp + (int64_t)min(my_q, a.n_q - 1) * a.q_sr);
-  if (wave < ntiles) issue(wave);
-  for (int t = wave; t < ntiles; t += NW) {
+  const int first = sp * NW + wave, stride = NW * S;
+  if (first < ntiles) issue(first);
+  for (int t = first; t < ntiles; t += stride) {
     wait_vmcnt<0>();
     const __bf16* ks = &ring[wave][0];
     // The tile moves into registers; once those reads have returned, the
@@ -110,7 +116,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_bf16_d64_kernel(const Att
     WaveAttention::TileRegs r;
     wa.read_tile(ks, ks + KT * D, r);
     wait_lgkmcnt0();
-    if (t + NW < ntiles) issue(t + NW);
+    if (t + stride < ntiles) issue(t + stride);
     wa.tile_regs(r, t * KT, L, L);
   }
   wait_vmcnt<0>();
@@ -148,10 +154,59 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_bf16_d64_kernel(const Att
       wa.o1[i] = wa.o1[i] * a0 + p[128 + 64 * (16 + i) + lane] * a1;
     }
   }
+  if (S > 1) {  // this workgroup's state, for the merge launch
+    float* st = a.part + ((int64_t)(b * a.h + hh) * S + sp) * kDecodeStateFloats;
+    st[lane] = wa.m;
+    st[64 + lane] = wa.l;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      st[128 + 64 * i + lane] = wa.o0[i];
+      st[128 + 64 * (16 + i) + lane] = wa.o1[i];
+    }
+    return;
+  }
   const float inv = wa.inv_sum();
   if (my_q < a.n_q) wa.store(Op + (int64_t)my_q * a.o_sr, inv);
   if (a.lse != nullptr && my_q < a.n_q && wa.g == 0)
     a.lse[(int64_t)(b * a.h + hh) * a.n_q + my_q] = wa.row_lse(inv);
+}
+
+// One wave per (batch, head): folds the `splits` partial states in the same
+// way the workgroup folded its waves' states, then normalises and stores.
+__global__ __launch_bounds__(64) void attn_decode_merge_kernel(const AttnArgs a) {
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const int b = bh / a.h;
+  const int hh = bh - b * a.h;
+  const float* st = a.part + (int64_t)bh * a.splits * kDecodeStateFloats;
+  WaveAttention wa;
+  wa.init(lane, a.scale);
+  wa.m = st[lane];
+  wa.l = st[64 + lane];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    wa.o0[i] = st[128 + 64 * i + lane];
+    wa.o1[i] = st[128 + 64 * (16 + i) + lane];
+  }
+  for (int s = 1; s < a.splits; ++s) {
+    const float* p = st + (int64_t)s * kDecodeStateFloats;
+    const float m1 = p[lane], l1 = p[64 + lane];
+    const float mm = fmaxf(wa.m, m1);
+    const float a0 = fast_exp2((wa.m - mm) * wa.c2), a1 = fast_exp2((m1 - mm) * wa.c2);
+    wa.m = mm;
+    wa.l = wa.l * a0 + l1 * a1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      wa.o0[i] = wa.o0[i] * a0 + p[128 + 64 * i + lane] * a1;
+      wa.o1[i] = wa.o1[i] * a0 + p[128 + 64 * (16 + i) + lane] * a1;
+    }
+  }
+  const int my_q = lane & 31;
+  __bf16* Op = (__bf16*)a.O + b * a.o_sb + hh * a.o_sh;
+  const float inv = wa.inv_sum();
+  if (my_q < a.n_q) wa.store(Op + (int64_t)my_q * a.o_sr, inv);
+  if (a.lse != nullptr && my_q < a.n_q && wa.g == 0)
+    a.lse[(int64_t)bh * a.n_q + my_q] = wa.row_lse(inv);
 }
 
 }  // namespace
@@ -163,10 +218,21 @@ bool attn_decode_applies(const AttnArgs& a) {
 }
 
 hipError_t launch_attn_decode_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev) {
-  if (!attn_decode_applies(a)) return hipErrorInvalidValue;
+  if (!attn_decode_applies(a) || a.splits > 1) return hipErrorInvalidValue;
   void* args[] = {(void*)&a};
   return hipExtLaunchKernel((const void*)attn_decode_bf16_d64_kernel, dim3(a.B * a.h), dim3(NW * 64),
                             args, 0, s, ev.start, ev.stop, 0);
+}
+
+hipError_t launch_attn_decode_split_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev_part,
+                                             LaunchEvents ev_merge) {
+  if (!attn_decode_applies(a) || a.splits < 2 || a.part == nullptr) return hipErrorInvalidValue;
+  void* args[] = {(void*)&a};
+  hipError_t e = hipExtLaunchKernel((const void*)attn_decode_bf16_d64_kernel, dim3(a.B * a.h * a.splits),
+                                    dim3(NW * 64), args, 0, s, ev_part.start, ev_part.stop, 0);
+  if (e != hipSuccess) return e;
+  return hipExtLaunchKernel((const void*)attn_decode_merge_kernel, dim3(a.B * a.h), dim3(64), args, 0, s,
+                            ev_merge.start, ev_merge.stop, 0);
 }
 
 }  // namespace mha

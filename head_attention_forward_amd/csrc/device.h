@@ -45,9 +45,10 @@ __device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsign
   const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
   const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)p);
   const unsigned long long sp = ((unsigned long long)hi << 32) | (unsigned long long)lo;
+  const unsigned ls = (unsigned)__builtin_amdgcn_readfirstlane(lds);  // wave-uniform: pin to an SGPR
   asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(lds), "v"(voff), "s"((const void*)(size_t)sp)
+               : "s"(ls), "v"(voff), "s"((const void*)(size_t)sp)
                : "memory", "m0");
 }
 

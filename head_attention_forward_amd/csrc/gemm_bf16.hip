@@ -28,7 +28,8 @@
 // is the MFMA's first operand.  A lane then holds, for one output row, four
 // runs of 4 consecutive columns, which it stores as 8-byte vectors.
 //
-// Tile order: workgroups are dealt to the 8 XCDs round-robin; the linear
+// Tile order: workgroups are dealt to the XCDs round-robin (8 on MI355X; the
+// launchers read the count from the device); the linear
 // workgroup id is remapped so that each XCD owns a contiguous band of the
 // row-major tile order (whole rows of tiles), i.e. each XCD's L2 streams its
 // own band of activation rows and the (small) weight matrix, instead of
@@ -41,7 +42,6 @@ namespace {
 using namespace dev;
 
 constexpr int BK = 64;
-constexpr int kXcds = 8;
 
 // A tile [BM][64]: 128-byte rows; chunk c of row m sits at chunk c ^ ((m >> 1) & 7).
 __device__ __forceinline__ int a_pos(int m, int chunk) { return chunk ^ ((m >> 1) & 7); }
@@ -124,10 +124,11 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& g, const int bid_in) {
   } else {
     const int T = MT * NT;
     const int bid = bid_in;
-    const int x = bid % kXcds;
-    const int per = T / kXcds;
-    const int rem = T - per * kXcds;
-    tile = x * per + min(x, rem) + bid / kXcds;
+    const int X = g.xcds > 0 ? g.xcds : 1;
+    const int x = bid % X;
+    const int per = T / X;
+    const int rem = T - per * X;
+    tile = x * per + min(x, rem) + bid / X;
   }
   const int m0 = (tile / NT) * BM;
   const int n0 = (tile % NT) * BN;
@@ -367,7 +368,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_bf16_kernel(const GemmArgs 
 }
 
 template <int BM, int BN, int NS, int WM = 2, int WN = 2>
-hipError_t launch_tile(const GemmArgs& g, hipStream_t s, LaunchEvents ev) {
+hipError_t launch_tile(const GemmArgs& g0, hipStream_t s, LaunchEvents ev) {
+  GemmArgs g = g0;
+  g.xcds = device_xcds();
   const int N = g.col_start[g.nseg];
   const int tiles = ((N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
   void* args[] = {(void*)&g};
@@ -460,6 +463,7 @@ hipError_t launch_gemm_bf16_cfg(const GemmArgs& g, int cfg, hipStream_t s, Launc
 
 hipError_t launch_gemm_bf16_group(GemmGroup gg, hipStream_t s, LaunchEvents ev) {
   if (gg.n < 1 || gg.n > kMaxGroupJobs) return hipErrorInvalidValue;
+  const int X = device_xcds();  // each job starts on a multiple of it: its own XCD-aware order
   int next = 0;
   for (int j = 0; j < gg.n; ++j) {
     const GemmArgs& g = gg.job[j];
@@ -479,7 +483,8 @@ hipError_t launch_gemm_bf16_group(GemmGroup gg, hipStream_t s, LaunchEvents ev) 
     }
     gg.start[j] = next;
     gg.count[j] = (int)cnt;
-    const int64_t end = ((int64_t)next + cnt + kXcds - 1) / kXcds * kXcds;
+    gg.job[j].xcds = X;
+    const int64_t end = ((int64_t)next + cnt + X - 1) / X * X;
     if (end > (int64_t)1 << 30) return hipErrorInvalidValue;
     next = (int)end;
   }

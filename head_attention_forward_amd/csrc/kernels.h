@@ -32,6 +32,11 @@ struct AttnArgs {
   // Optional (bf16 kernels): row log-sum-exp, lse[(b*h + head)*n_q + i] =
   // ln(sum over visible keys j of exp(scale * q_i . k_j)); null: not written.
   float* lse;
+  // Few-query kernel only: the key tiles of each (batch, head) are dealt to
+  // `splits` workgroups, each writing its partial softmax state to `part`
+  // (splits > 1; a second launch merges them).
+  int splits;
+  float* part;
   int32_t key_len[kLaunchBatch];
   // Batches by decreasing key length (padded only; the few-query kernel
   // takes the longest sequences first, so the last workgroups to start are
@@ -98,6 +103,9 @@ struct GemmArgs {
   // partial[z][M][N]; a second kernel adds them and rounds once.
   int splits;
   float* partial;
+  // XCDs of the device (set by the launchers): the tile order gives each
+  // XCD's workgroups a contiguous band of tile rows.
+  int xcds;
 };
 
 // Residual + LayerNorm over rows of d features (bf16):
@@ -150,6 +158,17 @@ struct LaunchEvents {
 // of each (batch, head) are split over the workgroup's waves.
 bool attn_decode_applies(const AttnArgs& a);
 hipError_t launch_attn_decode_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev);
+// Split form (a.splits > 1, a.part holding decode_part_floats(a) floats):
+// the partial launch, then the merge launch.
+constexpr int kDecodeStateFloats = 34 * 64;  // one workgroup's state: m, l, 32 accumulators per lane
+inline int64_t decode_part_floats(const AttnArgs& a) {
+  return (int64_t)a.B * a.h * a.splits * kDecodeStateFloats;
+}
+hipError_t launch_attn_decode_split_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev_part,
+                                             LaunchEvents ev_merge);
+// Compute units and XCDs of the current device (read once per device).
+int device_compute_units();
+int device_xcds();
 hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev = {});
 // One fixed attention configuration (index into the instantiated set); for sweeps.
 hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, LaunchEvents ev = {});

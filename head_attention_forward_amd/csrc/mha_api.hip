@@ -193,6 +193,25 @@ hipError_t launch_backward(const BwdArgs& a, const int32_t* key_lengths, hipStre
   return hipSuccess;
 }
 
+// Few-query attention: workgroups per (batch, head) so that B * h of them
+// fill the compute units (key tiles dealt out by eights per workgroup; at
+// most kMaxDecodeSplits).  1 when the plain few-query launch already fills
+// the chip, when the split does not apply, or for padded calls of more than
+// one launch's batches.
+constexpr int kMaxDecodeSplits = 8;
+int decode_splits(int B, int h, int n_q, int n_k, int mask_kind) {
+  if (n_q > 32 || (mask_kind & MHA_MASK_CAUSAL) || n_k <= 128 || B > kLaunchBatch) return 1;
+  const int64_t bh = (int64_t)B * h;
+  const int cus = device_compute_units();
+  if (bh >= cus) return 1;
+  int s = (int)((cus + bh - 1) / bh);
+  const int tiles = (n_k + 63) / 64;
+  const int by_tiles = (tiles + 7) / 8;  // each workgroup's eight waves want at least a tile each
+  if (s > by_tiles) s = by_tiles;
+  if (s > kMaxDecodeSplits) s = kMaxDecodeSplits;
+  return s < 1 ? 1 : s;
+}
+
 // The fused projection + attention kernel, one launch per chunk likewise.
 hipError_t launch_fused(const ProjAttnArgs& a, const int32_t* key_lengths, hipStream_t s, Timer* tm) {
   const int step = launch_batch(a.B, a.padded);
@@ -890,6 +909,86 @@ int embed_positional_forward_timed(const int32_t* tokens, const void* E, void* o
     return MHA_ERR_EVENTS;
   Timer tm{events, capacity, 0};
   const int st = embed_impl(tokens, E, out, B, n, vocab, d_model, pos0, dtype, stream, &tm);
+  if (n_launches) *n_launches = tm.used;
+  return st;
+}
+
+size_t sdpa_decode_workspace_bytes(int B, int h, int n_q, int n_k) {
+  if (B <= 0 || h <= 0 || n_q <= 0 || n_k <= 0) return 0;
+  const int S = decode_splits(B, h, n_q, n_k, 0);
+  const int64_t floats = S > 1 ? (int64_t)B * h * S * kDecodeStateFloats : 0;
+  return round_up((size_t)(floats * 4 > 0 ? floats * 4 : 1));
+}
+
+int sdpa_decode_launches(int B, int h, int n_q, int n_k, int mask_kind) {
+  if (B <= 0 || h <= 0 || n_q <= 0 || n_k <= 0) return MHA_ERR_DIM;
+  const int step = (mask_kind & MHA_MASK_KEY_PADDING) ? kLaunchBatch : B;
+  return decode_splits(B, h, n_q, n_k, mask_kind) > 1 ? 2 : (B + step - 1) / step;
+}
+
+static int decode_impl(const void* Q, const void* K, const void* V, void* O, int B, int h, int n_q,
+                       int n_k, int d_k, int d_v, float scale, int mask_kind,
+                       const int32_t* key_lengths, int dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream, Timer* tm) {
+  // The checks of sdpa_forward first (no HIP call before them) ...
+  if (!Q || !K || !V || !O) return MHA_ERR_NULL;
+  int st = check_attn_dims(B, h, n_q, n_k, d_k, d_v);
+  if (st != MHA_OK) return st;
+  if (!(isfinite(scale) && scale > 0.f)) return MHA_ERR_SCALE;
+  st = check_mask(mask_kind, B, n_q, n_k, key_lengths);
+  if (st != MHA_OK) return st;
+  if (dtype != MHA_DTYPE_BF16 && dtype != MHA_DTYPE_F32) return MHA_ERR_UNSUPPORTED;
+  if (!aligned16(Q) || !aligned16(K) || !aligned16(V) || !aligned16(O)) return MHA_ERR_UNSUPPORTED;
+  // ... then the split, which reads the device's compute-unit count.
+  const int S = dtype == MHA_DTYPE_BF16 ? decode_splits(B, h, n_q, n_k, mask_kind) : 1;
+  if (S == 1)  // the plain launch fills the chip (or the split does not apply)
+    return sdpa_impl(Q, K, V, O, B, h, n_q, n_k, d_k, d_v, scale, mask_kind, key_lengths, dtype,
+                     stream, tm);
+  const size_t need = (size_t)B * h * S * kDecodeStateFloats * 4;
+  if (workspace == nullptr || ((uintptr_t)workspace & (kAlign - 1)) != 0 || workspace_bytes < need)
+    return MHA_ERR_WORKSPACE;
+  AttnArgs a;
+  memset(&a, 0, sizeof(a));
+  a.Q = Q;
+  a.K = K;
+  a.V = V;
+  a.O = O;
+  set_head_major(a.q_sb, a.q_sh, a.q_sr, h, n_q, d_k);
+  set_head_major(a.k_sb, a.k_sh, a.k_sr, h, n_k, d_k);
+  set_head_major(a.v_sb, a.v_sh, a.v_sr, h, n_k, d_v);
+  set_head_major(a.o_sb, a.o_sh, a.o_sr, h, n_q, d_v);
+  a.B = B;
+  a.h = h;
+  a.n_q = n_q;
+  a.n_k = n_k;
+  a.scale = scale;
+  a.splits = S;
+  a.part = (float*)workspace;
+  fill_mask(a, mask_kind);
+  if (a.padded) fill_lengths(a, key_lengths, 0);  // B <= kLaunchBatch here
+  const LaunchEvents e_part = next_events(tm);
+  const LaunchEvents e_merge = next_events(tm);
+  return launch_status(launch_attn_decode_split_bf16_d64(a, stream, e_part, e_merge));
+}
+
+int sdpa_decode(const void* Q, const void* K, const void* V, void* O, int B, int h, int n_q, int n_k,
+                int d_k, int d_v, float scale, int mask_kind, const int32_t* key_lengths, int dtype,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(Q, K, V, O, B, h, n_q, n_k, d_k, d_v, scale, mask_kind, key_lengths, dtype,
+                     workspace, workspace_bytes, stream, nullptr);
+}
+
+int sdpa_decode_timed(const void* Q, const void* K, const void* V, void* O, int B, int h, int n_q,
+                      int n_k, int d_k, int d_v, float scale, int mask_kind,
+                      const int32_t* key_lengths, int dtype, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, hipEvent_t* events, int capacity,
+                      int* n_launches) {
+  if (events == nullptr || capacity < 2) return MHA_ERR_EVENTS;
+  for (int i = 0; i < 2; ++i)
+    if (events[i] == nullptr) return MHA_ERR_EVENTS;
+  Timer tm{events, capacity, 0};
+  const int st = decode_impl(Q, K, V, O, B, h, n_q, n_k, d_k, d_v, scale, mask_kind, key_lengths,
+                             dtype, workspace, workspace_bytes, stream, &tm);
   if (n_launches) *n_launches = tm.used;
   return st;
 }

@@ -34,7 +34,6 @@ namespace {
 using namespace dev;
 
 constexpr int ROWS = 128;  // rows of the projection tile (>= n_q, n_k)
-constexpr int kComputeUnits = 256;  // MI355X
 constexpr int BKP = 64;    // k per stage
 
 // Activation tile [128][64]: 128-byte rows; chunk c of row m at c ^ ((m >> 1) & 7).
@@ -281,7 +280,7 @@ hipError_t launch_proj_attn_bf16(const ProjAttnArgs& a, hipStream_t s, LaunchEve
   // one workgroup per unit with a deep ring: four 40 KB stages (all 160 KB
   // of LDS) for self-attention, measured 3% faster than three; two 56 KB
   // stages for cross-attention.
-  if ((int64_t)a.B * a.h > kComputeUnits) return self ? launch<false, 1>(a, s, ev) : launch<true, 1>(a, s, ev);
+  if ((int64_t)a.B * a.h > device_compute_units()) return self ? launch<false, 1>(a, s, ev) : launch<true, 1>(a, s, ev);
   return self ? launch<false, 4>(a, s, ev) : launch<true, 2>(a, s, ev);
 }
 

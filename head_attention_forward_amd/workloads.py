@@ -143,6 +143,15 @@ WORKLOADS = {
         mask=MASK_KEY_PADDING, key_len_range=(1024, 4096),
         description="bare attention, one query per sequence over a 4096-key cache, bf16, "
                     "B=32 h=16 d=64, cache lengths in [1024,4096]"),
+    # The same decoding step at a small batch: 8 sequences x 16 heads = 128
+    # (batch, head) pairs, fewer than the compute units, each over a full
+    # 4096-key cache (sdpa_decode, which splits each pair's keys over several
+    # workgroups).
+    "decode_small_batch_sdpa": Workload(
+        "decode_small_batch_sdpa", "decode", "bf16", B=8, n_q=1, n_k=4096, h=16, d_k=64, d_v=64,
+        mask=MASK_NONE,
+        description="bare attention, one query per sequence over a full 4096-key cache, bf16, "
+                    "B=8 h=16 d=64 (sdpa_decode)"),
     # One Post-LN encoder layer of the base model (multi-head self-attention,
     # residual + LayerNorm, FFN 512 -> 2048 -> 512, residual + LayerNorm) on
     # the encoder block's batch.
@@ -177,7 +186,7 @@ def generate(w: Workload, seed: int = 0):
 
     sdpa: Q [B][h][n_q][d_k], K [B][h][n_k][d_k], V [B][h][n_k][d_v], scale,
           key_lengths (int32 [B] or None).
-    floor: the same draws as sdpa (the bytes a launch of that shape moves).
+    decode, floor: the same draws as sdpa.
     bwd:  as sdpa, then the upstream gradient dO [B][h][n_q][d_v].
     mha_bwd: as mha, then the upstream gradient dY [B][n_q][d_model].
     mha:  X_q [B][n_q][d_model], X_kv (the same tensor object for
@@ -192,7 +201,7 @@ def generate(w: Workload, seed: int = 0):
     g.manual_seed(seed)
     dt = w.torch_dtype
     out = {}
-    if w.kind in ("sdpa", "bwd", "floor"):
+    if w.kind in ("sdpa", "decode", "bwd", "floor"):
         out["Q"] = _normal(g, (w.B, w.h, w.n_q, w.d_k), 1.0, dt)
         out["K"] = _normal(g, (w.B, w.h, w.n_k, w.d_k), 1.0, dt)
         out["V"] = _normal(g, (w.B, w.h, w.n_k, w.d_v), 1.0, dt)

@@ -116,6 +116,43 @@ int sdpa_forward(const void* Q, const void* K, const void* V, void* O,
                  int dtype, hipStream_t stream);
 
 /*
+ * sdpa_decode -- sdpa_forward for the incremental-decoding shape (few new
+ * queries per sequence against long cached key ranges; hex4c59.cc
+ * "读懂 Attention Is All You Need", section "训练能并行，不意味着一次生成整句话":
+ * generation produces one position per step).  Same arguments, result and
+ * checks as sdpa_forward, plus a workspace.  When n_q <= 32, no causal bit,
+ * n_k > 128, B <= 256 and B * h is below the device's compute-unit count,
+ * the key tiles of each (batch, head) are dealt to several workgroups, each
+ * leaving its partial softmax state (reference m, sum l, accumulator) in the
+ * workspace, and a second launch merges them (the same softmax: the split
+ * only reorders the sum over keys).  Otherwise it is sdpa_forward and the
+ * workspace is not touched.
+ *   workspace  >= sdpa_decode_workspace_bytes(B, h, n_q, n_k), 256-byte
+ *              aligned, caller-owned device memory (contents need no init).
+ * Errors as sdpa_forward; MHA_ERR_WORKSPACE if a split call's workspace is
+ * missing, misaligned or too small.
+ */
+int sdpa_decode(const void* Q, const void* K, const void* V, void* O,
+                int B, int h, int n_q, int n_k, int d_k, int d_v,
+                float scale, int mask_kind, const int32_t* key_lengths, int dtype,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes of sdpa_decode (at least 256; the split count depends on
+ * the current device's compute units); 0 for non-positive sizes. */
+size_t sdpa_decode_workspace_bytes(int B, int h, int n_q, int n_k);
+
+/* Launches an sdpa_decode call makes on the current device (2 when it
+ * splits); a negative status for invalid sizes. */
+int sdpa_decode_launches(int B, int h, int n_q, int n_k, int mask_kind);
+
+/* sdpa_decode with launch events, as the other _timed variants. */
+int sdpa_decode_timed(const void* Q, const void* K, const void* V, void* O,
+                      int B, int h, int n_q, int n_k, int d_k, int d_v,
+                      float scale, int mask_kind, const int32_t* key_lengths, int dtype,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream,
+                      hipEvent_t* events, int capacity, int* n_launches);
+
+/*
  * mha_workspace_bytes -- device scratch that mha_forward and the stage calls
  * need for the projected heads and the concatenated attention output:
  *   Q [B][h][n_q][d_k], K [B][h][n_k][d_k], V [B][h][n_k][d_v],

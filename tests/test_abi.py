@@ -384,3 +384,21 @@ def test_backward_noalloc_rejections(L):
     assert call(dtype=F32) == UNSUP
     assert call(B=1, h=16, n_q=(1 << 16) + 1, n_k=8) == WS     # 2^20 + 16 query rows
     assert call(B=4, h=16, n_q=1 << 15, n_k=8) == WS           # 2^21 query rows
+
+
+def test_decode_rejections(L):
+    """sdpa_decode's argument checks run before any HIP call (the split
+    count, which reads the device's compute units, comes after them)."""
+    def dec(Q=FAKE, B=2, h=2, n_q=1, n_k=1000, d_k=64, scale=0.125, mask=0, kl=None, dtype=BF16):
+        return L.sdpa_decode(Q, FAKE, FAKE, FAKE2, B, h, n_q, n_k, d_k, 64, scale, mask, kl, dtype,
+                             FAKE, 1 << 20, None)
+    assert dec(Q=None) == NULL
+    assert dec(B=0) == DIM
+    assert dec(d_k=32) == UNSUP
+    assert dec(scale=-1.0) == SCALE
+    assert dec(mask=2) == KEYLEN
+    assert dec(mask=5) == MASK
+    assert dec(dtype=7) == UNSUP
+    assert dec(Q=MISALIGNED) == UNSUP
+    assert L.sdpa_decode_workspace_bytes(0, 1, 1, 1) == 0
+    assert L.sdpa_decode_launches(1, 0, 1, 1, 0) == DIM

@@ -506,3 +506,35 @@ def test_fused_plan_equals_staged(dev, case):
     hafa.mha_project_out(Ws[3], Y2, w.B, w.n_q, w.n_k, w.h, w.d_k, w.d_v, ws)
     torch.cuda.synchronize()
     assert torch.equal(Y, Y2)
+
+
+@pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", [
+    (8, 16, 1, 4096, 0, None),                 # 128 (batch, head) pairs: two workgroups each
+    (1, 2, 3, 1000, 2, [777]),                 # few pairs, short range: split bounded by the tiles
+    (2, 4, 32, 8193, 0, None),                 # eight splits, ragged last tile
+    (3, 1, 5, 2000, 2, [2000, 1, 1100]),       # a sequence with one visible key: empty splits
+    (4, 2, 1, 300, 2, [1, 300, 64, 129]),      # too few tiles to split: the plain path
+    (2, 2, 64, 640, 0, None),                  # more than 32 queries: the plain path
+    (1, 2, 200, 200, 1, None),                 # causal: the plain path
+])
+def test_sdpa_decode_split(dev, B, h, n_q, n_k, mask, kl):
+    """sdpa_decode: with few (batch, head) pairs the key tiles of each pair
+    are dealt to several workgroups and their partial softmax states merged
+    by a second launch.  Every output against the oracle; keys past a
+    sequence's length have exactly zero weight."""
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.bfloat16, seed=61 + n_k)
+    L = hafa.lib()
+    announce("sdpa_decode", B, h, n_q, n_k, mask, kl,
+             "launches", L.sdpa_decode_launches(B, h, n_q, n_k, mask))
+    Qd, Kd, Vd = Q.to(dev), K.to(dev), V.to(dev)
+    O = hafa.sdpa_decode(Qd, Kd, Vd, 0.125, mask, kl)
+    torch.cuda.synchronize()
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"decode split {B}x{h} {n_q}x{n_k}")
+    if kl is not None:
+        K2, V2 = Kd.clone(), Vd.clone()
+        for b, Lb in enumerate(kl):
+            K2[b, :, Lb:] = 40.0
+            V2[b, :, Lb:] = -9.0
+        O2 = hafa.sdpa_decode(Qd, K2, V2, 0.125, mask, kl)
+        torch.cuda.synchronize()
+        assert torch.equal(O2, O)
