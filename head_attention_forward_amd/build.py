@@ -1,10 +1,13 @@
 """Build libmha.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m head_attention_forward_amd.build
+    python -m head_attention_forward_amd.build [--asan]
 
 Compiles every ``csrc/*.hip`` with hipcc (one process per file, in
 parallel) into ``_build/`` and links ``libmha.so`` next to this file.  Always
-rebuilds.
+rebuilds.  ``--asan`` (or build(asan=True)) builds ``libmha_asan.so`` instead:
+the host code instrumented with AddressSanitizer (device code unchanged), for
+the CPU check of the C ABI's host paths; it needs the sanitizer runtime
+preloaded into the process that loads it.
 """
 
 import concurrent.futures
@@ -18,6 +21,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libmha.so")
+ASAN_BUILD_DIR = os.path.join(HERE, "_build_asan")
+ASAN_LIB_PATH = os.path.join(HERE, "libmha_asan.so")
+# Host-side AddressSanitizer only (each option applies to the host pass).
+ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are switched off for all device code.
@@ -48,15 +55,29 @@ def _run(cmd):
     return p.returncode, out
 
 
-def build(verbose=False):
+def asan_runtime():
+    """Path of the AddressSanitizer runtime matching hipcc's clang, or None."""
+    try:
+        out = subprocess.run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"],
+                             stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True).stdout.strip()
+    except Exception:
+        return None
+    return out if out and os.path.isabs(out) and os.path.exists(out) else None
+
+
+def build(verbose=False, asan=False):
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    build_dir = ASAN_BUILD_DIR if asan else BUILD_DIR
+    lib_path = ASAN_LIB_PATH if asan else LIB_PATH
+    extra_all = ASAN_FLAGS if asan else []
+    os.makedirs(build_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in sources]
+    objs = [os.path.join(build_dir, os.path.basename(s)[:-4] + ".o") for s in sources]
 
     def compile_one(src_obj):
         src, obj = src_obj
-        cmd = [hipcc] + COMMON + EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
+        cmd = ([hipcc] + COMMON + extra_all + EXTRA.get(os.path.basename(src), []) +
+               ["-c", src, "-o", obj])
         rc, out = _run(cmd)
         return src, rc, out, cmd
 
@@ -71,14 +92,15 @@ def build(verbose=False):
             failed = True
     if failed:
         raise RuntimeError("libmha: compilation failed")
-    tmp = LIB_PATH + ".tmp"
+    tmp = lib_path + ".tmp"
+    # (the sanitizer runtime is not linked in: the loading process preloads it)
     rc, out = _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
     if rc:
         sys.stderr.write(out + "\n")
         raise RuntimeError("libmha: link failed")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, lib_path)
+    return lib_path
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, asan="--asan" in sys.argv))

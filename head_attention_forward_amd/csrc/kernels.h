@@ -144,6 +144,7 @@ struct ProjAttnArgs {
   float scale;
   int causal;
   int padded;
+  int xcds;           // XCDs of the device (set by the launcher)
   int32_t key_len[kLaunchBatch];
 };
 

@@ -75,7 +75,7 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
   const int col = lane & 31;
   const int grp = lane >> 5;
 
-  // XCD-aware order: workgroups are dealt to the 8 XCDs round-robin; unit
+  // XCD-aware order: workgroups are dealt to the XCDs round-robin; unit
   // (b, head) = b*h + head is remapped so that each XCD owns a contiguous
   // run of units, i.e. whole batches: an activation row block is then read
   // into one XCD's L2 only.  When the run is made of whole batches, the
@@ -88,12 +88,13 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
   {
     const int T = a.B * a.h;
     const int bid = blockIdx.x;
-    const int x = bid % 8;
-    const int per = T / 8;
-    const int rem = T - per * 8;
+    const int X = a.xcds > 0 ? a.xcds : 1;
+    const int x = bid % X;
+    const int per = T / X;
+    const int rem = T - per * X;
     const int start = x * per + min(x, rem);
     const int len = per + (x < rem ? 1 : 0);
-    const int j = bid / 8;
+    const int j = bid / X;
     int u = start + j;
     if (len % a.h == 0 && start % a.h == 0) {
       const int nb = len / a.h;  // whole batches in this XCD's run
@@ -259,7 +260,9 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
 }
 
 template <bool CROSS, int NS>
-hipError_t launch(const ProjAttnArgs& a, hipStream_t s, LaunchEvents ev) {
+hipError_t launch(const ProjAttnArgs& a0, hipStream_t s, LaunchEvents ev) {
+  ProjAttnArgs a = a0;
+  a.xcds = device_xcds();
   void* args[] = {(void*)&a};
   return hipExtLaunchKernel((const void*)proj_attn_bf16_kernel<CROSS, NS>, dim3(a.B * a.h), dim3(512),
                             args, 0, s, ev.start, ev.stop, 0);
