@@ -1,13 +1,15 @@
 """Build libmha.so (the HIP kernels and the C ABI) in-tree for gfx950.
 
-    python -m head_attention_forward_amd.build [--asan]
+    python -m head_attention_forward_amd.build [--asan | --fault]
 
 Compiles every ``csrc/*.hip`` with hipcc (one process per file, in
 parallel) into ``_build/`` and links ``libmha.so`` next to this file.  Always
 rebuilds.  ``--asan`` (or build(asan=True)) builds ``libmha_asan.so`` instead:
 the host code instrumented with AddressSanitizer (device code unchanged), for
 the CPU check of the C ABI's host paths; it needs the sanitizer runtime
-preloaded into the process that loads it.
+preloaded into the process that loads it.  ``--fault`` builds
+``libmha_fault.so``, whose launches can be made to fail on demand
+(mha_fault_inject), for tests of the error path.
 """
 
 import concurrent.futures
@@ -25,6 +27,10 @@ ASAN_BUILD_DIR = os.path.join(HERE, "_build_asan")
 ASAN_LIB_PATH = os.path.join(HERE, "libmha_asan.so")
 # Host-side AddressSanitizer only (each option applies to the host pass).
 ASAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+# The fault-injection test build (launch failures on demand, mha_fault_inject).
+FAULT_BUILD_DIR = os.path.join(HERE, "_build_fault")
+FAULT_LIB_PATH = os.path.join(HERE, "libmha_fault.so")
+FAULT_FLAGS = ["-DMHA_FAULT_INJECTION"]
 
 ARCH = "gfx950"
 # Packed fp32 VALU instructions are switched off for all device code.
@@ -65,11 +71,11 @@ def asan_runtime():
     return out if out and os.path.isabs(out) and os.path.exists(out) else None
 
 
-def build(verbose=False, asan=False):
+def build(verbose=False, asan=False, fault=False):
     hipcc = _hipcc()
-    build_dir = ASAN_BUILD_DIR if asan else BUILD_DIR
-    lib_path = ASAN_LIB_PATH if asan else LIB_PATH
-    extra_all = ASAN_FLAGS if asan else []
+    build_dir = ASAN_BUILD_DIR if asan else (FAULT_BUILD_DIR if fault else BUILD_DIR)
+    lib_path = ASAN_LIB_PATH if asan else (FAULT_LIB_PATH if fault else LIB_PATH)
+    extra_all = (ASAN_FLAGS if asan else []) + (FAULT_FLAGS if fault else [])
     os.makedirs(build_dir, exist_ok=True)
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     objs = [os.path.join(build_dir, os.path.basename(s)[:-4] + ".o") for s in sources]
@@ -103,4 +109,4 @@ def build(verbose=False, asan=False):
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv, asan="--asan" in sys.argv))
+    print(build(verbose="-v" in sys.argv, asan="--asan" in sys.argv, fault="--fault" in sys.argv))

@@ -98,7 +98,7 @@ template <int CH>
 hipError_t launch_ch(const LnArgs& a, hipStream_t s, LaunchEvents ev) {
   void* args[] = {(void*)&a};
   const int blocks = (a.M + kRowsPerBlock - 1) / kRowsPerBlock;
-  return hipExtLaunchKernel((const void*)add_layernorm_bf16_kernel<CH>, dim3(blocks),
+  return launch_kernel((const void*)add_layernorm_bf16_kernel<CH>, dim3(blocks),
                             dim3(64 * kRowsPerBlock), args, 0, s, ev.start, ev.stop, 0);
 }
 

@@ -146,7 +146,7 @@ hipError_t launch_cfg(const AttnArgs& a, hipStream_t s, LaunchEvents ev) {
   constexpr int QT = NW * 32;
   dim3 grid(a.B * a.h, (a.n_q + QT - 1) / QT);
   void* args[] = {(void*)&a};
-  return hipExtLaunchKernel((const void*)attn_fwd_bf16_d64_kernel<NW, NS, WPE>, grid, dim3(NW * 64),
+  return launch_kernel((const void*)attn_fwd_bf16_d64_kernel<NW, NS, WPE>, grid, dim3(NW * 64),
                             args, 0, s, ev.start, ev.stop, 0);
 }
 

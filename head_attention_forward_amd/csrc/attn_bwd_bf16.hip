@@ -404,14 +404,14 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
 hipError_t launch_attn_bwd_dq(const BwdArgs& a, hipStream_t s, LaunchEvents ev) {
   void* args[] = {(void*)&a};
   dim3 grid(a.B * a.h, (a.n_q + NW * 32 - 1) / (NW * 32));
-  return hipExtLaunchKernel((const void*)attn_bwd_dq_kernel, grid, dim3(NW * 64), args, 0, s,
+  return launch_kernel((const void*)attn_bwd_dq_kernel, grid, dim3(NW * 64), args, 0, s,
                             ev.start, ev.stop, 0);
 }
 
 hipError_t launch_attn_bwd_dkdv(const BwdArgs& a, hipStream_t s, LaunchEvents ev) {
   void* args[] = {(void*)&a};
   dim3 grid(a.B * a.h, (a.n_k + NW * 32 - 1) / (NW * 32));
-  return hipExtLaunchKernel((const void*)attn_bwd_dkdv_kernel, grid, dim3(NW * 64), args, 0, s,
+  return launch_kernel((const void*)attn_bwd_dkdv_kernel, grid, dim3(NW * 64), args, 0, s,
                             ev.start, ev.stop, 0);
 }
 

@@ -220,7 +220,7 @@ bool attn_decode_applies(const AttnArgs& a) {
 hipError_t launch_attn_decode_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev) {
   if (!attn_decode_applies(a) || a.splits > 1) return hipErrorInvalidValue;
   void* args[] = {(void*)&a};
-  return hipExtLaunchKernel((const void*)attn_decode_bf16_d64_kernel, dim3(a.B * a.h), dim3(NW * 64),
+  return launch_kernel((const void*)attn_decode_bf16_d64_kernel, dim3(a.B * a.h), dim3(NW * 64),
                             args, 0, s, ev.start, ev.stop, 0);
 }
 
@@ -228,10 +228,10 @@ hipError_t launch_attn_decode_split_bf16_d64(const AttnArgs& a, hipStream_t s, L
                                              LaunchEvents ev_merge) {
   if (!attn_decode_applies(a) || a.splits < 2 || a.part == nullptr) return hipErrorInvalidValue;
   void* args[] = {(void*)&a};
-  hipError_t e = hipExtLaunchKernel((const void*)attn_decode_bf16_d64_kernel, dim3(a.B * a.h * a.splits),
+  hipError_t e = launch_kernel((const void*)attn_decode_bf16_d64_kernel, dim3(a.B * a.h * a.splits),
                                     dim3(NW * 64), args, 0, s, ev_part.start, ev_part.stop, 0);
   if (e != hipSuccess) return e;
-  return hipExtLaunchKernel((const void*)attn_decode_merge_kernel, dim3(a.B * a.h), dim3(64), args, 0, s,
+  return launch_kernel((const void*)attn_decode_merge_kernel, dim3(a.B * a.h), dim3(64), args, 0, s,
                             ev_merge.start, ev_merge.stop, 0);
 }
 

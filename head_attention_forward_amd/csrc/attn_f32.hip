@@ -173,7 +173,7 @@ hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev
   const int nqt = (a.n_q + QB - 1) / QB;
   dim3 grid(a.B * a.h, nqt);
   void* args[] = {(void*)&a};
-  return hipExtLaunchKernel((const void*)attn_fwd_f32_d64_kernel, grid, dim3(NT), args, 0, s, ev.start,
+  return launch_kernel((const void*)attn_fwd_f32_d64_kernel, grid, dim3(NT), args, 0, s, ev.start,
                             ev.stop, 0);
 }
 

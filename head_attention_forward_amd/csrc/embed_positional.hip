@@ -114,7 +114,7 @@ hipError_t launch_t(const EmbedArgs& a, hipStream_t s, LaunchEvents ev) {
   const int threads = min(256, (chunks + 63) / 64 * 64);
   dim3 grid(a.n, (a.B + kRowsPerGroup - 1) / kRowsPerGroup);
   void* args[] = {(void*)&a};
-  return hipExtLaunchKernel((const void*)embed_positional_kernel<T>, grid, dim3(threads), args, 0,
+  return launch_kernel((const void*)embed_positional_kernel<T>, grid, dim3(threads), args, 0,
                             s, ev.start, ev.stop, 0);
 }
 

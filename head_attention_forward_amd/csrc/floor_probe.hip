@@ -29,7 +29,7 @@ int probe_impl(int kind, const void* a, const void* b, const void* c, void* dst,
   if (grid < 1 || grid > (1 << 20)) return MHA_ERR_DIM;
   hipError_t e;
   if (kind == MHA_PROBE_EMPTY) {
-    e = hipExtLaunchKernel((const void*)floor_empty_kernel, dim3(grid), dim3(256), nullptr, 0, stream,
+    e = launch_kernel((const void*)floor_empty_kernel, dim3(grid), dim3(256), nullptr, 0, stream,
                            ev.start, ev.stop, 0);
   } else if (kind == MHA_PROBE_XOR3) {
     if (!a || !b || !c || !dst) return MHA_ERR_NULL;
@@ -37,7 +37,7 @@ int probe_impl(int kind, const void* a, const void* b, const void* c, void* dst,
     if ((((uintptr_t)a | (uintptr_t)b | (uintptr_t)c | (uintptr_t)dst) & 15u) != 0) return MHA_ERR_UNSUPPORTED;
     int64_t n = (int64_t)(bytes / 16);
     void* args[] = {(void*)&a, (void*)&b, (void*)&c, (void*)&dst, (void*)&n};
-    e = hipExtLaunchKernel((const void*)floor_xor3_kernel, dim3(grid), dim3(256), args, 0, stream,
+    e = launch_kernel((const void*)floor_xor3_kernel, dim3(grid), dim3(256), args, 0, stream,
                            ev.start, ev.stop, 0);
   } else {
     return MHA_ERR_UNSUPPORTED;

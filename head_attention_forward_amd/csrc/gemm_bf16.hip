@@ -374,7 +374,7 @@ hipError_t launch_tile(const GemmArgs& g0, hipStream_t s, LaunchEvents ev) {
   const int N = g.col_start[g.nseg];
   const int tiles = ((N + BN - 1) / BN) * ((g.M + BM - 1) / BM);
   void* args[] = {(void*)&g};
-  return hipExtLaunchKernel((const void*)gemm_bf16_kernel<BM, BN, NS, WM, WN>,
+  return launch_kernel((const void*)gemm_bf16_kernel<BM, BN, NS, WM, WN>,
                             dim3(tiles * (g.splits > 1 ? g.splits : 1)), dim3(64 * WM * WN), args, 0, s,
                             ev.start, ev.stop, 0);
 }
@@ -489,7 +489,7 @@ hipError_t launch_gemm_bf16_group(GemmGroup gg, hipStream_t s, LaunchEvents ev) 
     next = (int)end;
   }
   void* args[] = {(void*)&gg};
-  return hipExtLaunchKernel((const void*)gemm_group_kernel, dim3(next), dim3(256), args, 0, s, ev.start,
+  return launch_kernel((const void*)gemm_group_kernel, dim3(next), dim3(256), args, 0, s, ev.start,
                             ev.stop, 0);
 }
 
@@ -505,7 +505,7 @@ hipError_t launch_gemm_bf16_splitk(const GemmArgs& g, hipStream_t s, LaunchEvent
   const int N = g.col_start[g.nseg];
   const int64_t threads = (int64_t)g.M * (N / 8);
   void* args[] = {(void*)&g};
-  return hipExtLaunchKernel((const void*)gemm_splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)),
+  return launch_kernel((const void*)gemm_splitk_reduce_kernel, dim3((unsigned)((threads + 255) / 256)),
                             dim3(256), args, 0, s, ev_reduce.start, ev_reduce.stop, 0);
 }
 

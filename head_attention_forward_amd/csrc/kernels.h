@@ -155,6 +155,23 @@ struct LaunchEvents {
   hipEvent_t stop = nullptr;
 };
 
+#ifdef MHA_FAULT_INJECTION
+// Test builds only (fault_injection.hip): true while armed launches remain.
+bool fault_injection_fires();
+#endif
+
+// Every kernel launch of the library goes through here (same arguments as
+// hipExtLaunchKernel).  A build with MHA_FAULT_INJECTION defined can make
+// launches fail here, without reaching the runtime, to test how a launch
+// error travels back to the caller; the normal build has no such path.
+inline hipError_t launch_kernel(const void* f, dim3 grid, dim3 block, void** args, size_t shared,
+                                hipStream_t stream, hipEvent_t start, hipEvent_t stop, int flags) {
+#ifdef MHA_FAULT_INJECTION
+  if (fault_injection_fires()) return hipErrorLaunchFailure;
+#endif
+  return hipExtLaunchKernel(f, grid, block, args, shared, stream, start, stop, flags);
+}
+
 // Few queries (n_q <= 32, no causal mask) over more than 128 keys: the keys
 // of each (batch, head) are split over the workgroup's waves.
 bool attn_decode_applies(const AttnArgs& a);

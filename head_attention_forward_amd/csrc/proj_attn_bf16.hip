@@ -264,7 +264,7 @@ hipError_t launch(const ProjAttnArgs& a0, hipStream_t s, LaunchEvents ev) {
   ProjAttnArgs a = a0;
   a.xcds = device_xcds();
   void* args[] = {(void*)&a};
-  return hipExtLaunchKernel((const void*)proj_attn_bf16_kernel<CROSS, NS>, dim3(a.B * a.h), dim3(512),
+  return launch_kernel((const void*)proj_attn_bf16_kernel<CROSS, NS>, dim3(a.B * a.h), dim3(512),
                             args, 0, s, ev.start, ev.stop, 0);
 }
 

@@ -78,7 +78,7 @@ hipError_t launch_transpose_bf16(const TransposeBatch& tb, hipStream_t s, Launch
   dim3 grid((maxC + TB - 1) / TB, (maxR + TB - 1) / TB, tb.n);
   if (grid.y > 65535) return hipErrorInvalidValue;
   void* args[] = {(void*)&tb};
-  return hipExtLaunchKernel((const void*)transpose_bf16_kernel, grid, dim3(256), args, 0, s, ev.start,
+  return launch_kernel((const void*)transpose_bf16_kernel, grid, dim3(256), args, 0, s, ev.start,
                             ev.stop, 0);
 }
 
