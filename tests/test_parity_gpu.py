@@ -516,6 +516,7 @@ def test_fused_plan_equals_staged(dev, case):
     (4, 2, 1, 300, 2, [1, 300, 64, 129]),      # too few tiles to split: the plain path
     (2, 2, 64, 640, 0, None),                  # more than 32 queries: the plain path
     (1, 2, 200, 200, 1, None),                 # causal: the plain path
+    (300, 1, 1, 600, 2, [1 + (i * 37) % 600 for i in range(300)]),  # padded beyond one launch: plain, chunked
 ])
 def test_sdpa_decode_split(dev, B, h, n_q, n_k, mask, kl):
     """sdpa_decode: with few (batch, head) pairs the key tiles of each pair

@@ -56,6 +56,9 @@ def test_noalloc_backward_equals_workspace_backward(dev):
         # larger first, then smaller: the second call reuses the same device array
         (3, 4, 640, 640, 3, [640, 333, 1], 11),
         (1, 2, 100, 77, 0, None, 12),
+        # padded beyond one launch's 256 batches: two launches per kernel, each
+        # with its own rows of the array
+        (300, 1, 24, 24, 3, [1 + (i * 5) % 24 for i in range(300)], 13),
     ]
     for B, h, n_q, n_k, mask, kl, seed in cases:
         print("[gpu case] sdpa_backward_noalloc", B, h, n_q, n_k, mask, kl, flush=True)
