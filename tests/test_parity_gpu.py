@@ -480,9 +480,17 @@ def test_mha_small_shapes(dev):
 @pytest.mark.parametrize("case", [
     dict(B=3, n_q=100, n_k=100, d_model=512, h=8, mask=0, self_attn=True),
     dict(B=2, n_q=96, n_k=128, d_model=1024, h=16, mask=2, self_attn=False, key_len_range=(1, 128)),
-    # more (batch, head) workgroups than compute units: the one-stage ring
+    # more (batch, head) units than compute units: two heads per workgroup
     dict(B=40, n_q=100, n_k=100, d_model=512, h=8, mask=1, self_attn=True),
     dict(B=20, n_q=96, n_k=128, d_model=1024, h=16, mask=2, self_attn=False, key_len_range=(1, 128)),
+    # ... query rows ending inside an 8-row copy block, units not a multiple of the XCDs
+    dict(B=33, n_q=100, n_k=77, d_model=512, h=8, mask=2, self_attn=False, key_len_range=(1, 77)),
+    # ... one 32-row query block (the other Q row blocks skipped)
+    dict(B=130, n_q=20, n_k=128, d_model=128, h=2, mask=0, self_attn=False),
+    # ... a single k stage, all 128 rows
+    dict(B=130, n_q=128, n_k=128, d_model=64, h=2, mask=0, self_attn=True),
+    # ... an odd head count: one head per workgroup, the one-stage ring
+    dict(B=100, n_q=50, n_k=50, d_model=192, h=3, mask=0, self_attn=True),
     dict(B=2, n_q=128, n_k=128, d_model=128, h=2, mask=1, self_attn=True),
     dict(B=4, n_q=1, n_k=77, d_model=64, h=1, mask=0, self_attn=False),
     dict(B=2, n_q=65, n_k=65, d_model=192, h=3, mask=3, self_attn=True, key_len_range=(1, 65)),
