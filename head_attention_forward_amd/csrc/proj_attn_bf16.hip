@@ -41,6 +41,40 @@ __device__ __forceinline__ int x_pos(int m, int chunk) { return chunk ^ ((m >> 1
 // Weight tile [64][64]: 128-byte rows; chunk c of row k at c ^ (((k >> 1) & 1) << 2).
 __device__ __forceinline__ int w_pos(int k, int chunk) { return chunk ^ (((k >> 1) & 1) << 2); }
 
+// One 32 x 32 projection tile (MFMA accumulators: lane (col, grp) holds row
+// `row` and columns 8 q + 4 grp .. +3 of the block, q = 0..3) rounded to bf16
+// and stored as 32 rows of a Q, K (k_off) or V (v_off) tile, columns
+// 32 half .. +31.  Lanes l and l + 32 hold the two halves of each 16-byte
+// chunk; one permlane32 swap per register gives each lane a whole chunk
+// (lane l chunk q = 2p, lane l + 32 chunk q = 2p + 1), so the tile goes
+// out in 16-byte LDS writes (LDS writes cost the same per instruction at
+// 8 and 16 bytes).  Call with all lanes active.
+__device__ __forceinline__ void store_tile_bf16(__bf16* dst, bool v_layout, int row, int half, int grp,
+                                                const f32x16& acc) {
+  u32x2 pk[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    f32x4 v;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) v[r] = acc[4 * q + r];
+    pk[q] = __builtin_bit_cast(u32x2, __builtin_convertvector(v, bf16x4));
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    // Lanes 0-31 keep columns 16 p .. +3 and receive 16 p + 4 .. +7 from
+    // lane + 32; lanes 32-63 receive 16 p + 8 .. +11 and keep 16 p + 12 .. +15.
+    u32x4 out;
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      const auto r = __builtin_amdgcn_permlane32_swap(pk[2 * p][w], pk[2 * p + 1][w], false, false);
+      out[w] = r[0];
+      out[2 + w] = r[1];
+    }
+    const int chunk = 4 * half + 2 * p + grp;
+    *(u32x4*)&dst[v_layout ? v_off(row, chunk) : k_off(row, chunk)] = out;
+  }
+}
+
 // Waits until at most `later` stages issued after the current one are still
 // in flight (LPS loads per stage and wave), i.e. the current stage landed.
 template <int NS, int LPS>
@@ -224,16 +258,7 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
   for (int c = 0; c < 3; ++c) {
     const int cb = cb0 + c;
     const int mat = cb >> 1;
-    __bf16* dst = mat == 0 ? Qs : (mat == 1 ? Ks : Vs);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = 32 * (cb & 1) + 8 * q + 4 * grp;  // 4 consecutive columns
-      const int off = (mat == 2 ? v_off(xrow, n >> 3) : k_off(xrow, n >> 3)) + (n & 7);
-      f32x4 v;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) v[r] = acc[c][4 * q + r];
-      *(bf16x4*)&dst[off] = __builtin_convertvector(v, bf16x4);
-    }
+    store_tile_bf16(mat == 0 ? Qs : (mat == 1 ? Ks : Vs), mat == 2, xrow, cb & 1, grp, acc[c]);
   }
   __syncthreads();
 
@@ -448,20 +473,9 @@ void proj_attn2_bf16_kernel(const ProjAttnArgs a) {
   for (int c = 0; c < 3; ++c) {
     const int cb = 3 * cg + c;
     const int mat = (cb % 6) >> 1;
-    __bf16* dst = &ring[(cb >> 1) * ROWS * D];
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int xrow = 64 * rh + 32 * rr + col;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = 32 * (cb & 1) + 8 * q + 4 * grp;  // 4 consecutive columns
-        const int off = (mat == 2 ? v_off(xrow, n >> 3) : k_off(xrow, n >> 3)) + (n & 7);
-        f32x4 v;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = acc[rr][c][4 * q + r];
-        *(bf16x4*)&dst[off] = __builtin_convertvector(v, bf16x4);
-      }
-    }
+    for (int rr = 0; rr < 2; ++rr)
+      store_tile_bf16(&ring[(cb >> 1) * ROWS * D], mat == 2, 64 * rh + 32 * rr + col, cb & 1, grp, acc[rr][c]);
   }
   __syncthreads();
 
