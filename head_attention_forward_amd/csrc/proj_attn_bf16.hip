@@ -33,6 +33,8 @@ namespace {
 
 using namespace dev;
 
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+
 constexpr int ROWS = 128;  // rows of the projection tile (>= n_q, n_k)
 constexpr int BKP = 64;    // k per stage
 
