@@ -136,7 +136,7 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
   wait_vmcnt<0>();  // no load may still target LDS when the workgroup ends
 
   const float inv = wa.inv_sum();
-  if (my_q < a.n_q) wa.store(Op + (int64_t)my_q * a.o_sr, inv);
+  wa.store(Op + (int64_t)min(my_q, a.n_q - 1) * a.o_sr, inv, my_q < a.n_q);
   if (a.lse != nullptr && my_q < a.n_q && wa.g == 0)
     a.lse[(int64_t)(b * a.h + hh) * a.n_q + my_q] = wa.row_lse(inv);
 }

@@ -166,7 +166,7 @@ __global__ __launch_bounds__(NW * 64) void attn_decode_bf16_d64_kernel(const Att
     return;
   }
   const float inv = wa.inv_sum();
-  if (my_q < a.n_q) wa.store(Op + (int64_t)my_q * a.o_sr, inv);
+  wa.store(Op + (int64_t)min(my_q, a.n_q - 1) * a.o_sr, inv, my_q < a.n_q);
   if (a.lse != nullptr && my_q < a.n_q && wa.g == 0)
     a.lse[(int64_t)(b * a.h + hh) * a.n_q + my_q] = wa.row_lse(inv);
 }
@@ -204,7 +204,7 @@ __global__ __launch_bounds__(64) void attn_decode_merge_kernel(const AttnArgs a)
   const int my_q = lane & 31;
   __bf16* Op = (__bf16*)a.O + b * a.o_sb + hh * a.o_sh;
   const float inv = wa.inv_sum();
-  if (my_q < a.n_q) wa.store(Op + (int64_t)my_q * a.o_sr, inv);
+  wa.store(Op + (int64_t)min(my_q, a.n_q - 1) * a.o_sr, inv, my_q < a.n_q);
   if (a.lse != nullptr && my_q < a.n_q && wa.g == 0)
     a.lse[(int64_t)bh * a.n_q + my_q] = wa.row_lse(inv);
 }

@@ -33,8 +33,6 @@ namespace {
 
 using namespace dev;
 
-typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int ROWS = 128;  // rows of the projection tile (>= n_q, n_k)
 constexpr int BKP = 64;    // k per stage
 
@@ -281,8 +279,7 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
   for (int t = 0; t < ROWS / KT; ++t)
     if (t * KT < wv_keys) wa.tile(Ks + t * KT * D, Vs + t * KT * D, t * KT, lim, lim_min);
   const float inv = wa.inv_sum();
-  if (my_q < a.n_q)
-    wa.store((__bf16*)a.O + ((int64_t)b * a.n_q + my_q) * ldw + hh * D, inv);
+  wa.store((__bf16*)a.O + ((int64_t)b * a.n_q + min(my_q, a.n_q - 1)) * ldw + hh * D, inv, my_q < a.n_q);
 }
 
 // Two heads per workgroup, for launches with more (batch, head) units than
@@ -502,8 +499,8 @@ void proj_attn2_bf16_kernel(const ProjAttnArgs a) {
   for (int t = 0; t < ROWS / KT; ++t)
     if (t * KT < wv_keys) wa.tile(Ks + t * KT * D, Vs + t * KT * D, t * KT, lim, lim_min);
   const float inv = wa.inv_sum();
-  if (my_q < a.n_q)
-    wa.store((__bf16*)a.O + ((int64_t)b * a.n_q + my_q) * ldw + (2 * hp + head) * D, inv);
+  wa.store((__bf16*)a.O + ((int64_t)b * a.n_q + min(my_q, a.n_q - 1)) * ldw + (2 * hp + head) * D, inv,
+           my_q < a.n_q);
 }
 
 template <bool CROSS>

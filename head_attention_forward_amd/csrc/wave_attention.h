@@ -287,7 +287,13 @@ struct WaveAttention {
 
   // O row of this lane's query = acc * inv, rounded to bf16 (lane g writes d
   // 8i + 4g .. +3 of both 32-wide halves).
-  __device__ __forceinline__ void store(__bf16* orow, float inv) const {
+  // Output row = acc / l rounded to bf16.  Lanes l and l + 32 hold the two
+  // halves (4 columns each) of every 16-byte chunk of the row; one
+  // permlane32 swap per register gives each lane a whole chunk, so the row
+  // goes out in 16-byte stores.  Call with every lane active; `valid`
+  // predicates the stores (orow must be a readable row address either way).
+  __device__ __forceinline__ void store(__bf16* orow, float inv, bool valid) const {
+    u32x2 pk[8];
 #pragma unroll
     for (int i4 = 0; i4 < 4; ++i4) {
       f32x4 v0, v1;
@@ -296,9 +302,23 @@ struct WaveAttention {
         v0[r] = o0[4 * i4 + r] * inv;
         v1[r] = o1[4 * i4 + r] * inv;
       }
-      *(bf16x4*)(orow + 8 * i4 + 4 * g) = __builtin_convertvector(v0, bf16x4);
-      *(bf16x4*)(orow + 32 + 8 * i4 + 4 * g) = __builtin_convertvector(v1, bf16x4);
+      pk[i4] = __builtin_bit_cast(u32x2, __builtin_convertvector(v0, bf16x4));
+      pk[4 + i4] = __builtin_bit_cast(u32x2, __builtin_convertvector(v1, bf16x4));
     }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) {
+        u32x4 out;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(pk[4 * blk + 2 * p][w], pk[4 * blk + 2 * p + 1][w],
+                                                           false, false);
+          out[w] = sw[0];
+          out[2 + w] = sw[1];
+        }
+        if (valid) *(u32x4*)(orow + 32 * blk + 16 * p + 8 * g) = out;
+      }
   }
 };
 
