@@ -99,21 +99,6 @@ __device__ __forceinline__ f32x16 score32(const __bf16* t, const int rx[4], int 
   return s;
 }
 
-// Store a lane's 64-wide accumulator row (as WaveAttention::store) times c.
-__device__ __forceinline__ void store_row(__bf16* row, int g, const f32x16& a0, const f32x16& a1, float c) {
-#pragma unroll
-  for (int i4 = 0; i4 < 4; ++i4) {
-    f32x4 v0, v1;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      v0[r] = a0[4 * i4 + r] * c;
-      v1[r] = a1[4 * i4 + r] * c;
-    }
-    *(bf16x4*)(row + 8 * i4 + 4 * g) = __builtin_convertvector(v0, bf16x4);
-    *(bf16x4*)(row + 32 + 8 * i4 + 4 * g) = __builtin_convertvector(v1, bf16x4);
-  }
-}
-
 // Source column chunk that lands in stored chunk (q & 7) of row (q >> 3)
 // under the k_off (row reads) and v_off (transposing reads) swizzles.
 __device__ __forceinline__ void swz(int q, int& row, int& kc, int& vc) {
@@ -255,9 +240,9 @@ void attn_bwd_dq_kernel(const BwdArgs a) {
     }
   }
   wait_vmcnt<0>();
-  if (my_q < a.n_q)
-    store_row((__bf16*)a.dQ + b * a.dq_sb + (int64_t)(bh - b * a.h) * a.dq_sh + (int64_t)my_q * a.dq_sr, g,
-              dq0, dq1, a.scale);
+  store_row_bf16((__bf16*)a.dQ + b * a.dq_sb + (int64_t)(bh - b * a.h) * a.dq_sh +
+                     (int64_t)min(my_q, a.n_q - 1) * a.dq_sr,
+                 g, dq0, dq1, a.scale, my_q < a.n_q);
 }
 
 // ---------------------------------------------------------------- dK and dV
@@ -392,11 +377,10 @@ void attn_bwd_dkdv_kernel(const BwdArgs a) {
     }
   }
   wait_vmcnt<0>();
-  if (my_k < a.n_k) {
-    const int64_t hh = bh - b * a.h;
-    store_row((__bf16*)a.dK + b * a.dk_sb + hh * a.dk_sh + (int64_t)my_k * a.dk_sr, g, dk0, dk1, a.scale);
-    store_row((__bf16*)a.dV + b * a.dv_sb + hh * a.dv_sh + (int64_t)my_k * a.dv_sr, g, dv0, dv1, 1.0f);
-  }
+  const int64_t hh = bh - b * a.h;
+  const int64_t kr = min(my_k, a.n_k - 1);
+  store_row_bf16((__bf16*)a.dK + b * a.dk_sb + hh * a.dk_sh + kr * a.dk_sr, g, dk0, dk1, a.scale, my_k < a.n_k);
+  store_row_bf16((__bf16*)a.dV + b * a.dv_sb + hh * a.dv_sh + kr * a.dv_sr, g, dv0, dv1, 1.0f, my_k < a.n_k);
 }
 
 }  // namespace

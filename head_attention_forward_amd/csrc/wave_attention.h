@@ -65,6 +65,43 @@ __device__ __forceinline__ float sum_halves(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// A lane's 64-wide row of transposed-product accumulators (a0: columns
+// 8 i + 4 g + r at a0[4 i + r], i = 0..3; a1 the same 32 columns further),
+// times c, rounded to bf16 and stored at `row`.  Lanes l and l + 32 hold the
+// two halves of every 16-byte chunk of the row; one permlane32 swap per
+// register gives each lane a whole chunk, so the row goes out in 16-byte
+// stores.  Call with every lane active; `valid` predicates the stores (row
+// must be a valid row address either way).
+__device__ __forceinline__ void store_row_bf16(__bf16* row, int g, const f32x16& a0, const f32x16& a1,
+                                               float c, bool valid) {
+  u32x2 pk[8];
+#pragma unroll
+  for (int i4 = 0; i4 < 4; ++i4) {
+    f32x4 v0, v1;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      v0[r] = a0[4 * i4 + r] * c;
+      v1[r] = a1[4 * i4 + r] * c;
+    }
+    pk[i4] = __builtin_bit_cast(u32x2, __builtin_convertvector(v0, bf16x4));
+    pk[4 + i4] = __builtin_bit_cast(u32x2, __builtin_convertvector(v1, bf16x4));
+  }
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      u32x4 out;
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(pk[4 * blk + 2 * p][w], pk[4 * blk + 2 * p + 1][w],
+                                                         false, false);
+        out[w] = sw[0];
+        out[2 + w] = sw[1];
+      }
+      if (valid) *(u32x4*)(row + 32 * blk + 16 * p + 8 * g) = out;
+    }
+}
+
 // Streaming attention state of one wave: 32 queries of one (batch, head).
 // Key tiles come from LDS in the k_off (K) and v_off (V) layouts.
 struct WaveAttention {
@@ -287,38 +324,10 @@ struct WaveAttention {
 
   // O row of this lane's query = acc * inv, rounded to bf16 (lane g writes d
   // 8i + 4g .. +3 of both 32-wide halves).
-  // Output row = acc / l rounded to bf16.  Lanes l and l + 32 hold the two
-  // halves (4 columns each) of every 16-byte chunk of the row; one
-  // permlane32 swap per register gives each lane a whole chunk, so the row
-  // goes out in 16-byte stores.  Call with every lane active; `valid`
-  // predicates the stores (orow must be a readable row address either way).
+  // Output row = acc / l rounded to bf16 (store_row_bf16).  Call with
+  // every lane active; `valid` predicates the stores.
   __device__ __forceinline__ void store(__bf16* orow, float inv, bool valid) const {
-    u32x2 pk[8];
-#pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      f32x4 v0, v1;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        v0[r] = o0[4 * i4 + r] * inv;
-        v1[r] = o1[4 * i4 + r] * inv;
-      }
-      pk[i4] = __builtin_bit_cast(u32x2, __builtin_convertvector(v0, bf16x4));
-      pk[4 + i4] = __builtin_bit_cast(u32x2, __builtin_convertvector(v1, bf16x4));
-    }
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        u32x4 out;
-#pragma unroll
-        for (int w = 0; w < 2; ++w) {
-          const auto sw = __builtin_amdgcn_permlane32_swap(pk[4 * blk + 2 * p][w], pk[4 * blk + 2 * p + 1][w],
-                                                           false, false);
-          out[w] = sw[0];
-          out[2 + w] = sw[1];
-        }
-        if (valid) *(u32x4*)(orow + 32 * blk + 16 * p + 8 * g) = out;
-      }
+    store_row_bf16(orow, g, o0, o1, inv, valid);
   }
 };
 
