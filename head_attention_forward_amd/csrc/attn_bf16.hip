@@ -168,8 +168,18 @@ hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents e
   // A few queries over many keys: split the keys over waves instead
   // (attn_decode_bf16.hip).
   if (attn_decode_applies(a)) return launch_attn_decode_bf16_d64(a, s, ev);
-  // Measured on MI355X: 4-wave workgroups (128 queries) with a 2-tile ring
-  // and four waves per SIMD are fastest for short and long sequences alike.
+  // Unmasked attention with at least two 8-wave workgroups (256 queries)
+  // per compute unit: each K/V tile copied into LDS serves twice the
+  // queries.  Measured on MI355X, same box: 4 x 16 x 2048 78.2 -> 73.4 us,
+  // 4 x 16 x 4096 284 -> 278 us, 1 x 16 x 8192 284 -> 268 us; with fewer
+  // workgroups than that they lose up to 30% (1 x 8 x 4096, 2 x 16 x 1024),
+  // and on causal shapes the uneven work per query tile favours the
+  // smaller workgroups.
+  const int64_t wg8 = (int64_t)a.B * a.h * ((a.n_q + 255) / 256);
+  if (!a.causal && !a.padded && wg8 >= 2 * (int64_t)device_compute_units())
+    return launch_attn_bf16_d64_cfg(a, 3, s, ev);
+  // Otherwise 4-wave workgroups (128 queries) with a 2-tile ring and four
+  // waves per SIMD are fastest, for short and long sequences alike.
   return launch_attn_bf16_d64_cfg(a, 0, s, ev);
 }
 

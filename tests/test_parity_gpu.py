@@ -169,6 +169,38 @@ def test_sdpa_long_causal_sampled(dev):
     assert bool(((Of >= lo - 1e-2) & (Of <= hi + 1e-2)).all())
 
 
+def test_sdpa_unmasked_eight_wave_workgroups(dev):
+    """Unmasked attention large enough for 8-wave workgroups (B=4, h=16,
+    n=2048: 512 of them): sampled rows (every tile boundary included) and two
+    whole heads against the oracle; the forward with lse returns the same
+    output and, on those heads, the oracle's row log-sum-exp (to 2^-8, the
+    bound the backward tests use)."""
+    B, h, n = 4, 16, 2048
+    Q, K, V = sdpa_inputs(B, h, n, n, torch.bfloat16, seed=2048)
+    announce("sdpa_forward bf16 unmasked, 8-wave workgroups", dict(B=B, h=h, n=n))
+    Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
+    O = hafa.sdpa_forward(Qd, Kd, Vd, 0.125, 0)
+    O2, lse = hafa.sdpa_forward_lse(Qd, Kd, Vd, 0.125, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2)
+    rng = np.random.default_rng(1)
+    special = [0, 1, 127, 128, 255, 256, 1023, 1024, 2046, 2047]
+    idx = [(b, hh, q) for b in range(B) for hh in (0, h - 1) for q in special]
+    idx += [(int(rng.integers(B)), int(rng.integers(h)), int(rng.integers(n))) for _ in range(300)]
+    idx = np.array(idx)
+    Q64, K64, V64 = to_f64(Q), to_f64(K), to_f64(V)
+    want = oracle.sdpa_ref_rows(Q64, K64, V64, 0.125, 0, None, idx)
+    assert_bf16_close(O[idx[:, 0], idx[:, 1], idx[:, 2]], want, "unmasked 4x16x2048 sampled rows")
+    for b, hh in ((0, 0), (B - 1, h - 1)):
+        sl = lambda t: t[b:b + 1, hh:hh + 1]  # noqa: E731
+        want_h = oracle.sdpa_ref(sl(Q64), sl(K64), sl(V64), 0.125, 0, None)
+        assert_bf16_close(O[b:b + 1, hh:hh + 1], want_h, f"unmasked whole head ({b}, {hh})")
+        want_l = oracle.row_logsumexp(sl(Q64), sl(K64), 0.125, 0, None)
+        lerr = float(np.abs(to_f64(lse[b:b + 1, hh:hh + 1]) - want_l).max())
+        print(f"  lse ({b}, {hh}) max_abs={lerr:.2e}", flush=True)
+        assert lerr <= 2.0 ** -8 + 1e-6
+
+
 # ------------------------------------------------------------------ edge shapes
 
 EDGE = [
