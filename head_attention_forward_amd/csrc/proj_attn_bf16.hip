@@ -284,8 +284,8 @@ void proj_attn_bf16_kernel(const ProjAttnArgs a) {
 
 // Two heads per workgroup, for launches with more (batch, head) units than
 // compute units (a unit per workgroup would give two workgroups per unit
-// with one stage buffer each).  Workgroup (b, pair p) computes
-// X_q,b [W^Q_i | .] and X_kv,b [W^K_i | W^V_i | .] for heads i = 2p, 2p + 1:
+// with one stage buffer each).  Workgroup (b, pair p) computes Q_i = X_q,b
+// W^Q_i, K_i = X_kv,b W^K_i and V_i = X_kv,b W^V_i for heads i = 2p, 2p + 1:
 // the activation tiles of a k stage are copied into LDS once for both heads
 // (per unit 40 KB instead of 56 KB a stage in cross-attention), and each
 // wave computes a 64 x 96 block of the [128 x 384] result (two row blocks,
@@ -357,10 +357,9 @@ void proj_attn2_bf16_kernel(const ProjAttnArgs a) {
 
   // DMA sources.  Activation load r of this wave fills block XL wave + r of
   // a tile (rows 8 blk .. +7; in cross-attention X_q blocks at or past n_q
-  // are skipped);
-  // weight load r fills block WL wave + r of the 48 weight blocks (block j:
-  // tile j / 8 = (head, matrix) = ((j / 8) / 3, (j / 8) % 3), rows
-  // 8 (j % 8) .. +7).
+  // are skipped); weight load r fills block WL wave + r of the 48 weight
+  // blocks (block j: tile j / 8 = (head, matrix) = ((j / 8) / 3, (j / 8) % 3),
+  // rows 8 (j % 8) .. +7).
   unsigned xq_off[XL], xkv_off[XL], w_off[WL];
   const char* w_src[WL];
 #pragma unroll
@@ -400,8 +399,9 @@ void proj_attn2_bf16_kernel(const ProjAttnArgs a) {
   };
 
   // This wave's six 32 x 32 output tiles: row blocks 2 rh, 2 rh + 1 and
-  // column blocks 3 cg .. 3 cg + 2 of (Q0 Q1 K0 K1 V0 V1) of head 2p, then
-  // the same six of head 2p + 1.  Column block cb reads weight tile cb / 2.
+  // column blocks 3 cg .. 3 cg + 2 of the twelve (Q0 Q1 K0 K1 V0 V1 of head
+  // 2p, then the same six of head 2p + 1).  Column block cb reads weight
+  // tile cb / 2.
   // The first two column blocks of a wave are both Q blocks (cg even) or
   // both K/V blocks (cg odd); the third is always a K/V block.  So the
   // products take activation fragments fa (X_q or X_kv, a wave-uniform
