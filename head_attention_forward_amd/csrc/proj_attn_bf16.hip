@@ -530,12 +530,15 @@ bool proj_attn_supported(int n_q, int n_k, int d_model) {
 hipError_t launch_proj_attn_bf16(const ProjAttnArgs& a, hipStream_t s, LaunchEvents ev) {
   if (!proj_attn_supported(a.n_q, a.n_k, a.d_model)) return hipErrorInvalidValue;
   const bool self = a.Xq == a.Xkv && a.n_q == a.n_k;
-  // More (batch, head) workgroups than compute units: one stage buffer, so
-  // that two workgroups share a unit and one's copies overlap the other's
-  // products (cross-attention block, 512 workgroups: 49 -> 39 us).  Otherwise
-  // one workgroup per unit with a deep ring: four 40 KB stages (all 160 KB
-  // of LDS) for self-attention, measured 3% faster than three; two 56 KB
-  // stages for cross-attention.
+  // More (batch, head) units than compute units: with an even head count,
+  // two heads per workgroup (proj_attn2_bf16_kernel: the cross-attention
+  // block's fused kernel 38.4 -> 32.0 us); with an odd one, one head per
+  // workgroup and one stage buffer, so that two workgroups share a unit and
+  // one's copies overlap the other's products (that block, 512 workgroups:
+  // 49 -> 39 us against the deep ring).  Otherwise one workgroup per unit
+  // with a deep ring: four 40 KB stages (all 160 KB of LDS) for
+  // self-attention, measured 3% faster than three; two 56 KB stages for
+  // cross-attention.
   if ((int64_t)a.B * a.h > device_compute_units()) {
     if (a.h % 2 == 0) return self ? launch2<false>(a, s, ev) : launch2<true>(a, s, ev);
     return self ? launch<false, 1>(a, s, ev) : launch<true, 1>(a, s, ev);
