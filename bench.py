@@ -91,7 +91,7 @@ def layer_launches(w):
 
 
 def step_launches(w):
-    if w.kind in ("sdpa", "embed"):
+    if w.kind in ("sdpa", "embed", "mfma"):
         return 1
     if w.kind == "floor":
         return 2
@@ -125,6 +125,11 @@ def kernel_plan(w, n_launches=None):
         plan.append(dict(name=name, flops=0.0, bytes=float(e * (3 * M * d + 2 * d)),
                          peak_kind="hbm", has_attention=False))
 
+    if w.kind == "mfma":
+        # the matrix-core probe: products only (4 waves x 4 chains per workgroup)
+        plan.append(dict(name="mfma_probe", flops=float(B) * 16 * w.iters * 2 * 32 * 32 * 16, bytes=0.0,
+                         peak_kind="mfma", has_attention=False))
+        return plan, None
     if w.kind == "floor":
         # an empty kernel, then one that reads Q, K, V and writes an O-sized output
         plan.append(dict(name="empty_kernel", flops=0.0, bytes=0.0, peak_kind="hbm", has_attention=False))
@@ -301,6 +306,11 @@ class Step:
             self.kl = None
         P = ctypes.c_void_p
         for _ in range(sets):
+            if w.kind == "mfma":
+                sink = torch.empty((w.B, 256), dtype=torch.float32, device=dev)
+                self.keep.append((None, None, None, sink))
+                self.sets.append((1 if w.operands == "sparse" else 0, w.B, w.iters, P(sink.data_ptr())))
+                continue
             if w.kind == "floor":
                 Q, K, V = (x[k].to(dev) for k in ("Q", "K", "V"))
                 O = torch.empty_like(Q)
@@ -400,7 +410,7 @@ class Step:
                                   w.B, w.n_q, w.n_k, w.d_model, w.h, w.d_k, w.d_v, w.mask, self.kl,
                                   bnd.DTYPE_BF16, P(ws.data_ptr()), ws.numel()))
         self.n_launches = step_launches(w)
-        names = {"floor": "mha_floor_probe", "decode": "sdpa_decode",
+        names = {"floor": "mha_floor_probe", "mfma": "mha_mfma_probe", "decode": "sdpa_decode",
                  "sdpa": "sdpa_forward", "mha": "mha_forward", "layer": "encoder_layer_forward",
                  "embed": "embed_positional_forward", "bwd": "sdpa_backward",
                  "mha_bwd": "mha_backward"}
@@ -454,6 +464,8 @@ def floor_grid(w):
 
 def set_bytes(w):
     e = 2 if w.dtype == "bf16" else 4
+    if w.kind == "mfma":
+        return 4 * w.B * 256
     if w.kind == "mha_bwd":
         M, dm, hd = w.B * w.n_q, w.d_model, w.h * w.d_k
         return e * (3 * M * dm + 8 * dm * hd + 4 * M * hd + 2 * M * 3 * hd + 3 * M * hd + hd * M +
@@ -492,6 +504,12 @@ def parity_check(w, x, out):
     from head_attention_forward_amd.workloads import to_f64
     kl = None if x["key_lengths"] is None else x["key_lengths"].numpy()
     rows = "all"
+    if w.kind == "mfma":  # every workgroup of the probe writes the same 256 finite values
+        import torch
+        o = out.cpu()
+        ok = bool(torch.isfinite(o).all()) and bool((o == o[0:1]).all())
+        return dict(max_abs=0.0 if ok else None, rel_l2=0.0 if ok else None, ok=ok,
+                    rows="all (equal across workgroups, finite)")
     if w.kind == "floor":  # the byte mover's output, bit for bit (no attention arithmetic)
         import torch
         want = x["Q"].view(torch.int16) ^ x["K"].view(torch.int16) ^ x["V"].view(torch.int16)
@@ -746,6 +764,7 @@ KERNEL_SOURCES = {
     "gemm_group_kernel": ("gemm_bf16.hip", "mha_api.hip"),
     "floor_empty_kernel": ("floor_probe.hip",),
     "floor_xor3_kernel": ("floor_probe.hip",),
+    "probe_mfma_kernel": ("floor_probe.hip",),
 }
 
 
@@ -909,7 +928,7 @@ def main():
     dom = max(working, key=lambda k: k["avg_us"])
     peak_flops = PEAK_BF16_TFLOPS if dom["peak_kind"] == "mfma" else PEAK_FP32_TFLOPS
     ridge = peak_flops * 1e12 / (PEAK_HBM_GBS * 1e9)
-    ai = dom["flops"] / dom["bytes"] if dom["bytes"] > 0 else 0.0
+    ai = dom["flops"] / dom["bytes"] if dom["bytes"] > 0 else (math.inf if dom["flops"] > 0 else 0.0)
     traffic = recorded_traffic(w.name, dom["name"])
     if ai < ridge:
         roof = dict(bound="hbm", achieved=dom["gbs"], peak=PEAK_HBM_GBS, unit="GB/s",
@@ -927,7 +946,7 @@ def main():
                if att is not None and w.dtype == "bf16" else None)
 
     cpu = None
-    if not args.no_cpu_baseline and w.kind != "floor":  # the floor probe runs no oracle arithmetic
+    if not args.no_cpu_baseline and w.kind not in ("floor", "mfma"):  # the probes run no oracle arithmetic
         log("timing the CPU oracle on a bounded sample ...")
         cpu = cpu_baseline(w, x, args.cpu_seconds)
         log(f"cpu baseline: {cpu}")
@@ -942,6 +961,7 @@ def main():
         log(f"copy calibration: {n} bytes read, {n} bytes written")
 
     kinds = {"floor": "launch floor: an empty kernel and a kernel moving the attention's bytes",
+             "mfma": "matrix-core probe: dense bf16 products only, no memory traffic",
              "mha": "multi-head block (projections + attention + output projection)",
              "sdpa": "bare attention",
              "decode": "bare attention, few queries over long caches (sdpa_decode)",
@@ -958,6 +978,10 @@ def main():
         cfg.update(d_ff=w.d_ff, eps=w.eps)
     if w.kind == "embed":
         cfg = dict(workload=w.name, B=w.B, n=w.n_q, d_model=w.d_model, vocab=w.vocab, pos0=0,
+                   kind=kinds[w.kind], buffer_sets=sets)
+    if w.kind == "mfma":
+        cfg = dict(workload=w.name, workgroups=w.B, waves_per_workgroup=4, chains_per_wave=4,
+                   products_per_chain=w.iters, instruction="v_mfma_f32_32x32x16_bf16", operands=w.operands,
                    kind=kinds[w.kind], buffer_sets=sets)
     if x["key_lengths"] is not None:
         cfg["key_lengths_mean"] = float(x["key_lengths"].float().mean())

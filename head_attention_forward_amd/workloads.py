@@ -69,6 +69,8 @@ class Workload:
     d_ff: int = 0        # encoder layer: FFN hidden width
     eps: float = 1e-5    # encoder layer: LayerNorm epsilon
     vocab: int = 0       # input embedding: vocabulary size
+    iters: int = 0       # matrix-core probe: products per chain (B is its workgroup count)
+    operands: str = ""   # matrix-core probe: "dense" (random bits) or "sparse" (few set bits)
 
     @property
     def torch_dtype(self):
@@ -117,6 +119,22 @@ WORKLOADS = {
         mask=MASK_NONE,
         description="launch floor at the encoder attention's shape: an empty kernel and a "
                     "kernel moving the same 13.1 MB, 256 workgroups of 256 threads"),
+    # The dense bf16 throughput the matrix cores sustain on this device as it
+    # runs (shader clock under that load included): the practical ceiling the
+    # nominal 2516.6 TFLOP/s overstates.  1024 workgroups of four waves (four
+    # per compute unit), four independent chains of 16384 products per wave,
+    # with operands whose bits are as busy as those of normally distributed
+    # data; the sparse variant feeds operands with few set bits, which draw
+    # less power and let the clock stay higher.
+    "mfma_peak_probe": Workload(
+        "mfma_peak_probe", "mfma", "bf16", B=1024, n_q=1, n_k=1, h=1, d_k=64, d_v=64,
+        mask=MASK_NONE, iters=16384, operands="dense",
+        description="matrix-core probe: 1024 workgroups x 4 waves x 4 chains of 16384 "
+                    "v_mfma_f32_32x32x16_bf16 on random-bit operands, no memory traffic"),
+    "mfma_peak_probe_sparse": Workload(
+        "mfma_peak_probe_sparse", "mfma", "bf16", B=1024, n_q=1, n_k=1, h=1, d_k=64, d_v=64,
+        mask=MASK_NONE, iters=16384, operands="sparse",
+        description="matrix-core probe as mfma_peak_probe, operands small multiples of 1/1024"),
     "long_causal_sdpa": Workload(
         "long_causal_sdpa", "sdpa", "bf16", B=4, n_q=4096, n_k=4096, h=16, d_k=64, d_v=64,
         mask=MASK_CAUSAL,
@@ -201,6 +219,9 @@ def generate(w: Workload, seed: int = 0):
     g.manual_seed(seed)
     dt = w.torch_dtype
     out = {}
+    if w.kind == "mfma":  # the probe reads no inputs
+        out["key_lengths"] = None
+        return out
     if w.kind in ("sdpa", "decode", "bwd", "floor"):
         out["Q"] = _normal(g, (w.B, w.h, w.n_q, w.d_k), 1.0, dt)
         out["K"] = _normal(g, (w.B, w.h, w.n_k, w.d_k), 1.0, dt)

@@ -369,6 +369,21 @@ def test_floor_probe_rejections(L):
                                    ctypes.byref(n)) == -9
 
 
+def test_mfma_probe_rejections(L):
+    # unknown operand mode, bad grid or product count, null or misaligned sink, missing events
+    assert L.mha_mfma_probe(2, 8, 16, FAKE, None) == UNSUP
+    assert L.mha_mfma_probe(-1, 8, 16, FAKE, None) == UNSUP
+    for mode in (0, 1):
+        assert L.mha_mfma_probe(mode, 0, 16, FAKE, None) == DIM
+        assert L.mha_mfma_probe(mode, (1 << 20) + 1, 16, FAKE, None) == DIM
+        assert L.mha_mfma_probe(mode, 8, 0, FAKE, None) == DIM
+        assert L.mha_mfma_probe(mode, 8, (1 << 24) + 1, FAKE, None) == DIM
+        assert L.mha_mfma_probe(mode, 8, 16, None, None) == NULL
+        assert L.mha_mfma_probe(mode, 8, 16, ctypes.c_void_p(0x10002), None) == UNSUP
+    n = ctypes.c_int(-1)
+    assert L.mha_mfma_probe_timed(0, 8, 16, FAKE, None, None, 2, ctypes.byref(n)) == -9
+
+
 def test_backward_noalloc_rejections(L):
     """The allocation-free backward keeps its row terms in an 8 MiB device
     array: at most 2^20 query rows; every check is made before any HIP call
