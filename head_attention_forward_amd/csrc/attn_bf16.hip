@@ -14,6 +14,15 @@
 //   buffers, NS-1 tiles ahead of the one being computed; 16-byte chunks are
 //   XOR-swizzled so that both LDS read patterns are conflict-free.  A wave
 //   skips the tiles none of its queries can see (causal).
+//   Key split (KS = 2, for launches too small to give every SIMD several
+//   waves): the workgroup holds two groups of NW waves over the same
+//   queries; group 0 takes the first half of the query tile's key tiles,
+//   group 1 the second half, each through its own ring slot of every stage.
+//   At the end group 1 hands its softmax state (reference value, sum,
+//   accumulators) to group 0 through LDS, which merges the two (the
+//   streaming softmax's own rescaling rule) and writes the output.  The
+//   longest chain of dependent tiles a wave walks is halved and twice as
+//   many waves share each SIMD.
 #include "wave_attention.h"
 
 namespace mha {
@@ -22,21 +31,27 @@ namespace {
 using namespace dev;
 
 // WPE waves per SIMD (4: <= 128 VGPRs, 3: <= 168); LDS allows four for NW * NS <= 16.
-template <int NW, int NS, int WPE>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
+// KS key groups of NW waves each (1 or 2).
+template <int NW, int NS, int WPE, int KS>
+__global__ __launch_bounds__(NW * KS * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
   static_assert(NS == 2 || NS == 3, "ring depth");
+  static_assert(KS == 1 || (KS == 2 && NS == 2), "key split: two groups, two-slot ring");
   constexpr int BLK = KT * D * 2 / 1024;  // 1 KB blocks per tile and matrix
   constexpr int CHW = BLK / NW;           // load instructions per wave, tile and matrix
   constexpr int QT = NW * 32;
   static_assert(CHW * NW == BLK, "waves must split the tile evenly");
+  static_assert(KS == 1 || NW * 32 * 64 * 4 <= NS * KS * KT * D * 2, "merge buffer fits the K ring");
 
-  __shared__ __attribute__((aligned(1024))) __bf16 Ks[NS][KT * D];
-  __shared__ __attribute__((aligned(1024))) __bf16 Vs[NS][KT * D];
+  // Ring slot s of group j: Ks[s][j], Vs[s][j].
+  __shared__ __attribute__((aligned(1024))) __bf16 Ks[NS][KS][KT * D];
+  __shared__ __attribute__((aligned(1024))) __bf16 Vs[NS][KS][KT * D];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kg = KS == 1 ? 0 : wave_all / NW;  // key group
+  const int wave = wave_all - kg * NW;         // query block of the tile
   const int col = lane & 31;
 
   const int bh = blockIdx.x;
@@ -62,11 +77,17 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
   const int wv_keys =
       __builtin_amdgcn_readfirstlane(wv_last < qw0 ? 0 : (a.causal ? min(L, wv_last + 1) : L));
   const int ntiles = __builtin_amdgcn_readfirstlane((wg_keys + KT - 1) / KT);
+  // Group kg walks tiles first_tile .. first_tile + my_tiles - 1; both groups
+  // step through n_steps iterations (one barrier each).
+  const int n_steps = (ntiles + KS - 1) / KS;
+  const int first_tile = kg * n_steps;
+  const int my_tiles = __builtin_amdgcn_readfirstlane(max(0, min(n_steps, ntiles - first_tile)));
 
   // Direct loads: instruction r of this wave fills LDS block (wave*CHW + r)
-  // (8 rows); lane l writes 16-byte chunk l of it, i.e. row q >> 3, stored
-  // chunk q & 7 with q = block*64 + l, which holds the source chunk that
-  // the swizzle maps there.  Byte offsets from the tile's first row.
+  // (8 rows) of its group's tile; lane l writes 16-byte chunk l of it, i.e.
+  // row q >> 3, stored chunk q & 7 with q = block*64 + l, which holds the
+  // source chunk that the swizzle maps there.  Byte offsets from the tile's
+  // first row.
   auto chunk_of = [&](int r, int& row, int& kc, int& vc) {
     const int q = (wave * CHW + r) * 64 + lane;
     row = q >> 3;
@@ -81,17 +102,17 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
     koff[r] = (unsigned)(row * a.k_sr + kc) * 2u;
     voff[r] = (unsigned)(row * a.v_sr + vc) * 2u;
   }
-  const unsigned ks_lds = lds_addr(&Ks[0][0]);
-  const unsigned vs_lds = lds_addr(&Vs[0][0]);
-  // Tiles are issued in order; kb/vb point at the next one (wave-uniform,
-  // advanced with scalar adds).
+  const unsigned ks_lds = lds_addr(&Ks[0][kg][0]);
+  const unsigned vs_lds = lds_addr(&Vs[0][kg][0]);
+  // Tiles are issued in order; kb/vb point at the group's next one
+  // (wave-uniform, advanced with scalar adds).
   const int64_t kstep = (int64_t)KT * a.k_sr * 2, vstep = (int64_t)KT * a.v_sr * 2;
-  const char* kb = Kp;
-  const char* vb = Vp;
-  auto issue = [&](int tile, int buf) {
-    const unsigned kd = ks_lds + (unsigned)(buf * KT * D + wave * CHW * 512) * 2u;
-    const unsigned vd = vs_lds + (unsigned)(buf * KT * D + wave * CHW * 512) * 2u;
-    const int k0 = tile * KT;
+  const char* kb = Kp + first_tile * kstep;
+  const char* vb = Vp + first_tile * vstep;
+  auto issue = [&](int step, int buf) {
+    const unsigned kd = ks_lds + (unsigned)(buf * KS * KT * D + wave * CHW * 512) * 2u;
+    const unsigned vd = vs_lds + (unsigned)(buf * KS * KT * D + wave * CHW * 512) * 2u;
+    const int k0 = (first_tile + step) * KT;
     if (k0 + KT <= a.n_k) {
 #pragma unroll
       for (int r = 0; r < CHW; ++r) {
@@ -116,24 +137,53 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
   wa.init(lane, a.scale);
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < ntiles) issue(s, s);
+    if (s < my_tiles) issue(s, s);
   wa.load_q(Qp + (int64_t)min(my_q, a.n_q - 1) * a.q_sr);
 
   // The ring index is a compile-time constant in each unrolled copy.
-  for (int t0 = 0; t0 < ntiles; t0 += NS) {
+  for (int t0 = 0; t0 < n_steps; t0 += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
       const int t = t0 + u;
-      if (t < ntiles) {
-        if (NS == 3 && t + 1 < ntiles) wait_vmcnt<2 * CHW>();
+      if (t < n_steps) {
+        if (NS == 3 && t + 1 < my_tiles) wait_vmcnt<2 * CHW>();
         else wait_vmcnt<0>();
         __syncthreads();
-        if (t + NS - 1 < ntiles) issue(t + NS - 1, (u + NS - 1) % NS);
-        if (t * KT < wv_keys) wa.tile(Ks[u], Vs[u], t * KT, lim, lim_min);  // else no visible key
+        if (t + NS - 1 < my_tiles) issue(t + NS - 1, (u + NS - 1) % NS);
+        const int k0 = (first_tile + t) * KT;
+        if (t < my_tiles && k0 < wv_keys)  // else no visible key
+          wa.tile(Ks[u][kg], Vs[u][kg], k0, lim, lim_min);
       }
     }
   }
   wait_vmcnt<0>();  // no load may still target LDS when the workgroup ends
+
+  if constexpr (KS == 2) {
+    // Group 1 hands its state to group 0 through the (now idle) ring:
+    // accumulator j of lane l of query block w at Ks-float [w][j][l] (32 a
+    // lane: exactly the K ring), m and l at Vs-float [w][0 or 1][l].
+    float* acc_x = (float*)&Ks[0][0][0] + wave * 32 * 64 + lane;
+    float* ml_x = (float*)&Vs[0][0][0] + wave * 2 * 64 + lane;
+    __syncthreads();  // every wave is done with the tiles
+    if (kg == 1) {
+      ml_x[0] = wa.m;
+      ml_x[64] = wa.l;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc_x[i * 64] = wa.o0[i];
+        acc_x[(16 + i) * 64] = wa.o1[i];
+      }
+    }
+    __syncthreads();
+    if (kg == 1) return;
+    f32x16 p0, p1;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      p0[i] = acc_x[i * 64];
+      p1[i] = acc_x[(16 + i) * 64];
+    }
+    wa.merge(ml_x[0], ml_x[64], p0, p1);
+  }
 
   const float inv = wa.inv_sum();
   wa.store(Op + (int64_t)min(my_q, a.n_q - 1) * a.o_sr, inv, my_q < a.n_q);
@@ -141,12 +191,12 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
     a.lse[(int64_t)(b * a.h + hh) * a.n_q + my_q] = wa.row_lse(inv);
 }
 
-template <int NW, int NS, int WPE>
+template <int NW, int NS, int WPE, int KS = 1>
 hipError_t launch_cfg(const AttnArgs& a, hipStream_t s, LaunchEvents ev) {
   constexpr int QT = NW * 32;
   dim3 grid(a.B * a.h, (a.n_q + QT - 1) / QT);
   void* args[] = {(void*)&a};
-  return launch_kernel((const void*)attn_fwd_bf16_d64_kernel<NW, NS, WPE>, grid, dim3(NW * 64),
+  return launch_kernel((const void*)attn_fwd_bf16_d64_kernel<NW, NS, WPE, KS>, grid, dim3(NW * KS * 64),
                             args, 0, s, ev.start, ev.stop, 0);
 }
 
@@ -160,6 +210,7 @@ hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, L
     case 3: return launch_cfg<8, 2, 4>(a, s, ev);
     case 4: return launch_cfg<8, 3, 4>(a, s, ev);
     case 5: return launch_cfg<8, 3, 3>(a, s, ev);
+    case 6: return launch_cfg<4, 2, 4, 2>(a, s, ev);
     default: return hipErrorInvalidValue;
   }
 }
@@ -178,6 +229,18 @@ hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents e
   const int64_t wg8 = (int64_t)a.B * a.h * ((a.n_q + 255) / 256);
   if (!a.causal && !a.padded && wg8 >= 2 * (int64_t)device_compute_units())
     return launch_attn_bf16_d64_cfg(a, 3, s, ev);
+  // At most one 4-wave workgroup per compute unit over at least 1024 keys:
+  // two key groups per workgroup (one wave per SIMD is too few to hide a
+  // tile's latencies, and each wave's chain of tiles is halved).  Measured on
+  // MI355X, same box, unmasked: 1 x 8 x 4096 58.0 -> 45.5 us, 1 x 4 x 8192
+  // 107 -> 85 us, 1 x 16 x 2048 29.5 -> 24.9 us, 2 x 8 x 1024 15.8 -> 13.9
+  // us; causal: 1 x 8 x 4096 52.0 -> 41.8 us, 2 x 16 x 1024 16.6 -> 15.2 us.
+  // With two workgroups per compute unit (4 x 16 x 1024) it gains nothing,
+  // and it loses where the key range is short (32 x 8 x 100: 6.7 -> 7.6 us;
+  // 16 x 8 x 512 causal: 12.9 -> 15.1 us).
+  const int64_t wg4 = (int64_t)a.B * a.h * ((a.n_q + 127) / 128);
+  if (wg4 <= (int64_t)device_compute_units() && a.n_k >= 1024)
+    return launch_attn_bf16_d64_cfg(a, 6, s, ev);
   // Otherwise 4-wave workgroups (128 queries) with a 2-tile ring and four
   // waves per SIMD are fastest, for short and long sequences alike.
   return launch_attn_bf16_d64_cfg(a, 0, s, ev);

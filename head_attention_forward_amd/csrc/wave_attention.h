@@ -312,6 +312,24 @@ struct WaveAttention {
     }
   }
 
+  // Fold in the state (m2, l2, p0, p1) of the same queries over another set
+  // of keys: both parts are rescaled to the larger reference value, which is
+  // the streaming softmax's own update.  A part that saw no key (m at the
+  // sentinel, l and the accumulators 0) gets the factor 0, or 1 when
+  // neither did.
+  __device__ __forceinline__ void merge(float m2, float l2, const f32x16& p0, const f32x16& p1) {
+    const float mn = fmaxf(m, m2);
+    const float a1 = fast_exp2((m - mn) * c2);
+    const float a2 = fast_exp2((m2 - mn) * c2);
+    m = mn;
+    l = l * a1 + l2 * a2;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      o0[i] = o0[i] * a1 + p0[i] * a2;
+      o1[i] = o1[i] * a1 + p1[i] * a2;
+    }
+  }
+
   // 1 / (row sum of weights); a cross-lane exchange: call with all lanes active.
   __device__ __forceinline__ float inv_sum() const { return 1.f / sum_halves(l); }
 

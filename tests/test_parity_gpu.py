@@ -201,6 +201,38 @@ def test_sdpa_unmasked_eight_wave_workgroups(dev):
         assert lerr <= 2.0 ** -8 + 1e-6
 
 
+KEY_SPLIT = [
+    # (B, h, n_q, n_k, mask, key_lengths): at most one 4-wave workgroup per
+    # compute unit over at least 1024 keys, where the launch takes two key
+    # groups per workgroup
+    (1, 2, 300, 1500, 0, None),            # ragged query and key tiles
+    (1, 3, 1100, 1100, 1, None),           # causal: the second group sees part or none of a tile
+    (2, 2, 200, 2000, 2, [1, 1500]),       # one visible key: the second group sees nothing
+    (2, 1, 1030, 1030, 3, [1030, 700]),    # causal + padding
+    (1, 1, 33, 4096, 0, None),             # one wave of queries per workgroup has 1 query
+    (1, 8, 128, 1024, 2, [1024]),          # exactly 16 key tiles, 8 per group
+]
+
+
+@pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", KEY_SPLIT)
+def test_sdpa_key_split(dev, B, h, n_q, n_k, mask, kl):
+    """The two-key-group workgroups against the oracle on every row, and
+    their row log-sum-exp (the backward pass's input) to 2^-8."""
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.bfloat16, seed=7 * n_q + n_k)
+    announce("sdpa_forward bf16 key split", dict(B=B, h=h, n_q=n_q, n_k=n_k, mask=mask, kl=kl))
+    Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
+    O = hafa.sdpa_forward(Qd, Kd, Vd, 0.125, mask, kl)
+    O2, lse = hafa.sdpa_forward_lse(Qd, Kd, Vd, 0.125, mask, kl)
+    torch.cuda.synchronize()
+    assert torch.equal(O, O2)
+    kla = None if kl is None else np.array(kl)
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"key split {B}x{h}x{n_q}x{n_k} m{mask}")
+    want_l = oracle.row_logsumexp(to_f64(Q), to_f64(K), 0.125, mask, kla)
+    lerr = float(np.abs(to_f64(lse) - want_l).max())
+    print(f"  lse max_abs={lerr:.2e}", flush=True)
+    assert lerr <= 2.0 ** -8 + 1e-6
+
+
 # ------------------------------------------------------------------ edge shapes
 
 EDGE = [
