@@ -746,7 +746,7 @@ def cpu_baseline(w, x, target_s):
 # name (the name recorded with each counter entry).
 _COMMON_SOURCES = ("device.h", "kernels.h")
 KERNEL_SOURCES = {
-    "attn_fwd_bf16_d64_kernel": ("attn_bf16.hip", "attn_decode_bf16.hip", "wave_attention.h"),
+    "attn_fwd_bf16_d64_kernel": ("attn_bf16.hip", "attn_decode_bf16.hip", "wave_attention.h", "device_info.hip"),
     "attn_decode_bf16_d64_kernel": ("attn_decode_bf16.hip", "attn_bf16.hip", "wave_attention.h",
                                     "mha_api.hip", "device_info.hip"),
     "attn_decode_merge_kernel": ("attn_decode_bf16.hip", "wave_attention.h", "mha_api.hip",

@@ -139,6 +139,13 @@ WORKLOADS = {
         "long_causal_sdpa", "sdpa", "bf16", B=4, n_q=4096, n_k=4096, h=16, d_k=64, d_v=64,
         mask=MASK_CAUSAL,
         description="bare causal attention, bf16, B=4 h=16 n=4096 d=64"),
+    # The long causal attention at batch 1 and 8 heads: 256 query tiles of
+    # 128, at most one workgroup per compute unit, which the launch serves
+    # with two key groups per workgroup.
+    "long_causal_b1_sdpa": Workload(
+        "long_causal_b1_sdpa", "sdpa", "bf16", B=1, n_q=4096, n_k=4096, h=8, d_k=64, d_v=64,
+        mask=MASK_CAUSAL,
+        description="bare causal attention at small batch, bf16, B=1 h=8 n=4096 d=64"),
     # Training's backward pass over the long causal shape: gradients of the
     # attention for an upstream gradient dO ~ N(0, 1).
     "long_causal_sdpa_bwd": Workload(
