@@ -38,7 +38,10 @@ __device__ __forceinline__ void wait_lgkmcnt0() { __builtin_amdgcn_s_waitcnt(15 
 // per-lane 32-bit byte offset (no vector address arithmetic); lane l writes
 // LDS byte address lds + 16 l.  Inline assembly, so that the compiler does
 // not wait for it before every LDS read; kernels wait for it explicitly
-// (vmcnt) before the barrier that publishes the data.
+// (vmcnt) before the barrier that publishes the data.  The copy takes its
+// LDS address from M0, and on this chip family an LDS-DMA instruction must
+// not directly follow a scalar write of M0 (one wait state in between); the
+// compiler cannot insert that inside an asm block, hence the s_nop.
 __device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsigned lds) {
   // The base is wave-uniform; readfirstlane pins it to SGPRs for the saddr operand.
   const unsigned long long p = (unsigned long long)(size_t)sbase;
@@ -47,20 +50,21 @@ __device__ __forceinline__ void dma16_s(const void* sbase, unsigned voff, unsign
   const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)p);
   const unsigned long long sp = ((unsigned long long)hi << 32) | (unsigned long long)lo;
   const unsigned ls = (unsigned)__builtin_amdgcn_readfirstlane(lds);  // wave-uniform: pin to an SGPR
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(ls), "v"(voff), "s"((const void*)(size_t)sp)
                : "memory", "m0");
 }
 
-// 4-byte global -> LDS copy per lane (same addressing as dma16_s; lane l
-// writes LDS byte address lds + 4 l): 64 consecutive floats per wave.
+// 4-byte global -> LDS copy per lane (same addressing and M0 wait state as
+// dma16_s; lane l writes LDS byte address lds + 4 l): 64 consecutive floats
+// per wave.
 __device__ __forceinline__ void dma4_s(const void* sbase, unsigned voff, unsigned lds) {
   const unsigned long long p = (unsigned long long)(size_t)sbase;
   const unsigned hi = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)(p >> 32));
   const unsigned lo = (unsigned)__builtin_amdgcn_readfirstlane((unsigned)p);
   const unsigned long long sp = ((unsigned long long)hi << 32) | (unsigned long long)lo;
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2"
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, %2"
                :
                : "s"(lds), "v"(voff), "s"((const void*)(size_t)sp)
                : "memory", "m0");
