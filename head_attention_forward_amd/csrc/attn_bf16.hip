@@ -30,8 +30,8 @@ namespace {
 
 using namespace dev;
 
-// WPE waves per SIMD (4: <= 128 VGPRs, 3: <= 168); LDS allows four for NW * NS <= 16.
-// KS key groups of NW waves each (1 or 2).
+// WPE waves per SIMD (4: <= 128 VGPRs, 3: <= 168).  KS key groups of NW
+// waves each (1 or 2).  LDS: NS * KS * 16 KB per workgroup.
 template <int NW, int NS, int WPE, int KS>
 __global__ __launch_bounds__(NW * KS * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
