@@ -66,6 +66,8 @@ def parse_args():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true")
     p.add_argument("--no-graph", action="store_true", help="time eager launches only")
+    p.add_argument("--no-mfma-probe", action="store_true",
+                   help="skip the sustained matrix-core rate measured beside MFMA-bound kernels")
     p.add_argument("--copy-calibration-mib", type=int, default=0,
                    help="also run a plain device copy of this many MiB (counter calibration)")
     return p.parse_args()
@@ -808,6 +810,36 @@ def recorded_traffic(workload, kernel):
 
 # ----------------------------------------------------------------------------- main
 
+PROBE_ITERS = 16384  # products per chain of the matrix-core probe (a launch of a few ms)
+
+
+def sustained_mfma_tflops(lib, sp, dev, launches=3):
+    """The dense bf16 rate the matrix cores sustain on this device now: the
+    matrix-core probe (mha_mfma_probe, random-bit operands, four waves of
+    four independent product chains per workgroup, four workgroups per
+    compute unit, no memory traffic) timed with launch events on the bench
+    stream, one untimed launch first.  Returns TFLOP/s."""
+    import numpy as np
+    import torch
+    from head_attention_forward_amd import _hip
+    grid = 4 * torch.cuda.get_device_properties(dev).multi_processor_count
+    sink = torch.empty((grid, 256), dtype=torch.float32, device=dev)
+    P = ctypes.c_void_p(sink.data_ptr())
+    if lib.mha_mfma_probe(0, grid, PROBE_ITERS, P, sp) != 0:
+        raise RuntimeError("matrix-core probe launch failed")
+    pool = _hip.EventPool(2 * launches)
+    n = ctypes.c_int()
+    for i in range(launches):
+        st = lib.mha_mfma_probe_timed(0, grid, PROBE_ITERS, P, sp, pool.ptr(2 * i), 2, ctypes.byref(n))
+        if st != 0 or n.value != 1:
+            raise RuntimeError(f"timed matrix-core probe failed with status {st}")
+    torch.cuda.synchronize()
+    ms = float(np.mean([pool.elapsed_ms(2 * i, 2 * i + 1) for i in range(launches)]))
+    pool.close()
+    flops = float(grid) * 16 * PROBE_ITERS * 2 * 32 * 32 * 16
+    return flops / (ms * 1e-3) / 1e12
+
+
 def main():
     args = parse_args()
     if args.gpus != 1:
@@ -938,6 +970,17 @@ def main():
                     peak=peak_flops, unit="TFLOP/s", frac=round(dom["tflops"] / peak_flops, 4))
     roof.update(traffic=traffic, kernel=dom["name"], avg_us=dom["avg_us"],
                 algorithmic_flops=dom["flops"], algorithmic_bytes=dom["bytes"])
+    # Beside an MFMA-bound kernel, the rate the matrix cores sustain on this
+    # box in the same run (the shader clock under dense products is below the
+    # 2.4 GHz of the nominal peak): context for `frac`, which stays nominal.
+    if roof["bound"] == "mfma" and w.dtype == "bf16" and w.kind != "mfma" and not args.no_mfma_probe:
+        probe = sustained_mfma_tflops(step.lib, sp, dev)
+        roof["sustained"] = dict(probe_tflops=round(probe, 1), frac=round(dom["tflops"] / probe, 4),
+                                 probe="mha_mfma_probe: random-bit bf16 operands, 4 workgroups of "
+                                       "4 waves per compute unit, 4 chains of %d "
+                                       "v_mfma_f32_32x32x16_bf16 per wave" % PROBE_ITERS)
+        log(f"sustained matrix-core rate: {probe:.1f} TFLOP/s; {dom['name']} at "
+            f"{100 * dom['tflops'] / probe:.1f}% of it")
 
     nominal = w.nominal_attention_flops()
     att = next((k for k in kernels if k["has_attention"]), None)
