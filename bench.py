@@ -17,8 +17,10 @@ step left in the 256 MB Infinity Cache.
 Prints one JSON line: the metric (attention forward TFLOP/s counted as
 4*B*h*n_q*n_k*d_k per step, and its fraction of the bf16 MFMA peak), the
 per-kernel durations (HIP launch events recorded by the library around each
-kernel of each timed step), the roofline of the dominant kernel, and the
-fp64 CPU oracle timed on a bounded sample of the same workload on the host.
+kernel of each timed step), the roofline of the dominant kernel (for an
+MFMA-bound one also the rate the matrix cores sustain in the same run,
+measured with the library's matrix-core probe), and the fp64 CPU oracle
+timed on a bounded sample of the same workload on the host.
 """
 
 import argparse
