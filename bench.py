@@ -755,7 +755,8 @@ KERNEL_SOURCES = {
                                     "mha_api.hip", "device_info.hip"),
     "attn_decode_merge_kernel": ("attn_decode_bf16.hip", "wave_attention.h", "mha_api.hip",
                                  "device_info.hip"),
-    "attn_fwd_f32_d64_kernel": ("attn_f32.hip",),
+    "attn_fwd_f32_d64_kernel": ("attn_f32.hip", "device_info.hip"),
+    "attn_fwd_f32_d64_wave_kernel": ("attn_f32.hip", "device_info.hip"),
     "proj_attn_bf16_kernel": ("proj_attn_bf16.hip", "wave_attention.h", "mha_api.hip", "device_info.hip"),
     "proj_attn2_bf16_kernel": ("proj_attn_bf16.hip", "wave_attention.h", "mha_api.hip", "device_info.hip"),
     "gemm_bf16_kernel": ("gemm_bf16.hip", "mha_api.hip"),

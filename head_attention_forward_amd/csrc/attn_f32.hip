@@ -12,6 +12,13 @@
 // accumulator).  A workgroup of 256 threads (32 queries) shares 64-key K and
 // V tiles in LDS; rows are padded to 68 floats so that the keys a group
 // reads at once fall in different banks.
+//
+// Launches too small to give every compute unit a workgroup that way (the
+// single-head 64-query shape, for one) take a second kernel with a whole
+// wave per query instead: lane j scores key j of the tile, the wave reduces
+// the tile's maximum and sum across lanes, and lane d accumulates output
+// column d -- about a tenth of the other kernel's vector instructions per
+// wave, so the launch's one round of waves finishes sooner.
 #include "kernels.h"
 
 #include <math.h>
@@ -167,12 +174,123 @@ __global__ __launch_bounds__(NT) void attn_fwd_f32_d64_kernel(const AttnArgs a) 
   }
 }
 
+// Maximum and sum over the 64 lanes of a wave (butterfly over lane ^ 1 ..
+// lane ^ 32; every lane ends with the result).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+constexpr int SQ = 4;  // waves (queries) per workgroup of the one-wave-per-query kernel
+
+// One wave per query.  The workgroup's SQ waves take consecutive queries of
+// one (batch, head) and share each 64-key K and V tile in LDS.  Per tile,
+// lane j forms the score of key k0 + j (four partial sums over d, so that
+// the products do not wait on each other), the wave takes the tile's
+// maximum, rescales its running sum and accumulator (the streaming softmax
+// of the other kernel, per tile instead of per lane), and lane d adds
+// sum_j p_j V[k0 + j][d] with the weights p_j passed through LDS.
+__global__ __launch_bounds__(SQ * 64) void attn_fwd_f32_d64_wave_kernel(const AttnArgs a) {
+  __shared__ __attribute__((aligned(16))) float Ks[KT * RS];
+  __shared__ __attribute__((aligned(16))) float Vs[KT * D];
+  __shared__ __attribute__((aligned(16))) float Ps[SQ][KT];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int bh = blockIdx.x;
+  const int b = bh / a.h;
+  const int hh = bh - b * a.h;
+  const int q0 = (int)blockIdx.y * SQ;
+  const int my_q = q0 + wave;
+  const bool active = my_q < a.n_q;  // wave-uniform
+  const int qc = min(my_q, a.n_q - 1);
+
+  const float* Qp = (const float*)a.Q + b * a.q_sb + hh * a.q_sh;
+  const float* Kp = (const float*)a.K + b * a.k_sb + hh * a.k_sh;
+  const float* Vp = (const float*)a.V + b * a.v_sb + hh * a.v_sh;
+  float* Op = (float*)a.O + b * a.o_sb + hh * a.o_sh;
+
+  int L = a.n_k;
+  if (a.padded) L = min(L, a.key_len[b]);
+  const int wg_last = min(q0 + SQ, a.n_q) - 1;
+  const int wg_keys = a.causal ? min(L, wg_last + 1) : L;
+  const int lim = a.causal ? min(L, qc + 1) : L;
+
+  // The query row in every lane (all lanes read the same 256 bytes).
+  float q[D];
+  {
+    const float4* src = (const float4*)(Qp + (int64_t)qc * a.q_sr);
+#pragma unroll
+    for (int j = 0; j < D / 4; ++j) {
+      const float4 v = src[j];
+      q[4 * j] = v.x; q[4 * j + 1] = v.y; q[4 * j + 2] = v.z; q[4 * j + 3] = v.w;
+    }
+  }
+
+  float m = -INFINITY, l = 0.f, acc = 0.f;  // acc: output column `lane`
+  for (int k0 = 0; k0 < wg_keys; k0 += KT) {
+    __syncthreads();  // every wave is done with the previous tile
+    for (int c = tid; c < KT * D / 4; c += SQ * 64) {
+      const int row = c / (D / 4);
+      const int dc = c % (D / 4);
+      const int key = min(k0 + row, a.n_k - 1);  // rows past n_k: never visible
+      *(float4*)&Ks[row * RS + 4 * dc] = *(const float4*)(Kp + (int64_t)key * a.k_sr + 4 * dc);
+      *(float4*)&Vs[row * D + 4 * dc] = *(const float4*)(Vp + (int64_t)key * a.v_sr + 4 * dc);
+    }
+    __syncthreads();
+    if (!active || k0 >= lim) continue;  // wave-uniform: no visible key in this tile
+
+    float d0 = 0.f, d1 = 0.f, d2 = 0.f, d3 = 0.f;
+    const float* krow = &Ks[lane * RS];
+#pragma unroll
+    for (int d = 0; d < D; d += 4) {
+      const float4 kv = *(const float4*)&krow[d];
+      d0 = fmaf(q[d], kv.x, d0);
+      d1 = fmaf(q[d + 1], kv.y, d1);
+      d2 = fmaf(q[d + 2], kv.z, d2);
+      d3 = fmaf(q[d + 3], kv.w, d3);
+    }
+    const bool vis = k0 + lane < lim;
+    const float sc = vis ? ((d0 + d1) + (d2 + d3)) * a.scale : -INFINITY;
+    const float m_new = fmaxf(m, wave_max(sc));  // finite: key k0 is visible
+    const float alpha = expf(m - m_new);         // exp(-inf) = 0 on the first visible tile
+    const float p = vis ? expf(sc - m_new) : 0.f;
+    l = l * alpha + wave_sum(p);
+    m = m_new;
+    Ps[wave][lane] = p;  // this wave's weights, read back by every lane below
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int j = 0; j < KT; j += 4) {
+      const float4 pw = *(const float4*)&Ps[wave][j];
+      a0 = fmaf(pw.x, Vs[j * D + lane], a0);
+      a1 = fmaf(pw.y, Vs[(j + 1) * D + lane], a1);
+      a2 = fmaf(pw.z, Vs[(j + 2) * D + lane], a2);
+      a3 = fmaf(pw.w, Vs[(j + 3) * D + lane], a3);
+    }
+    acc = acc * alpha + ((a0 + a1) + (a2 + a3));
+  }
+  if (active) Op[(int64_t)my_q * a.o_sr + lane] = acc / l;
+}
+
 }  // namespace
 
 hipError_t launch_attn_f32_d64(const AttnArgs& a, hipStream_t s, LaunchEvents ev) {
-  const int nqt = (a.n_q + QB - 1) / QB;
-  dim3 grid(a.B * a.h, nqt);
   void* args[] = {(void*)&a};
+  const int nqt = (a.n_q + QB - 1) / QB;
+  // Fewer 32-query workgroups than compute units: one wave per query.
+  if ((int64_t)a.B * a.h * nqt < device_compute_units()) {
+    dim3 grid(a.B * a.h, (a.n_q + SQ - 1) / SQ);
+    return launch_kernel((const void*)attn_fwd_f32_d64_wave_kernel, grid, dim3(SQ * 64), args, 0, s,
+                         ev.start, ev.stop, 0);
+  }
+  dim3 grid(a.B * a.h, nqt);
   return launch_kernel((const void*)attn_fwd_f32_d64_kernel, grid, dim3(NT), args, 0, s, ev.start,
                             ev.stop, 0);
 }

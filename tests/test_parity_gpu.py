@@ -300,6 +300,20 @@ def test_sdpa_f32_edges(dev, B, h, n_q, n_k, mask, kl):
     assert_f32_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"f32 edge {n_q}x{n_k} m{mask}")
 
 
+@pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", [(4, 16, 300, 300, 1, None),
+                                                 (2, 64, 100, 129, 2, [5, 129]),
+                                                 (8, 32, 33, 70, 0, None)])
+def test_sdpa_f32_eight_lane_kernel(dev, B, h, n_q, n_k, mask, kl):
+    """Launches with at least one 32-query workgroup per compute unit take
+    the eight-lanes-per-query fp32 kernel (the smaller ones above take the
+    wave-per-query kernel); every output element against the oracle."""
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.float32, seed=11 + n_q)
+    announce("sdpa_forward f32 eight-lane kernel", dict(B=B, h=h, n_q=n_q, n_k=n_k, mask=mask, kl=kl))
+    O = run_sdpa(dev, Q, K, V, 0.125, mask, kl)
+    torch.cuda.synchronize()
+    assert_f32_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"f32 {B}x{h}x{n_q}x{n_k} m{mask}")
+
+
 @pytest.mark.parametrize("B,mask", [(256, 2), (256, 3), (257, 3), (1024, 2), (1024, 3)])
 def test_sdpa_bf16_max_padded_batch(dev, B, mask):
     """Per-batch key lengths up to the largest padded batch (1024; they
