@@ -1,7 +1,8 @@
-"""GPU parity on seeded random shapes: bare attention, the multi-head block
-(one- and two-heads-per-workgroup fused kernels, the staged path) and the
-small-batch decoding step, each against the fp64 oracle with the bf16
-tolerances of the benchmark spec (max-abs 2e-2, relative L2 5e-3).
+"""GPU parity on seeded random shapes: bare attention (one and two key
+groups per workgroup, and fp32), the multi-head block (one- and
+two-heads-per-workgroup fused kernels, the staged path) and the small-batch
+decoding step, each against the fp64 oracle with the tolerances of the
+north star (bf16: max-abs 2e-2, relative L2 5e-3; fp32: max-abs 1e-5).
 
 The shapes come from a fixed numpy generator, so every run checks the same
 cases; each case is announced (flushed) before its launch.  Sizes are kept
@@ -81,6 +82,37 @@ def _decode_cases(n=10, seed=13):
     return cases
 
 
+def _key_split_cases(n=8, seed=14):
+    """Shapes with at most one 128-query workgroup per compute unit over at
+    least 1024 keys (the launch takes two key groups per workgroup)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        B, h = int(rng.integers(1, 4)), int(rng.integers(1, 5))
+        mask = int(rng.integers(0, 4))
+        if mask & 1:  # causal: as many queries as keys
+            n_q = n_k = int(rng.integers(1024, 1500))
+        else:
+            n_q, n_k = int(rng.integers(33, 600)), int(rng.integers(1024, 3000))
+        if B * h * n_q * n_k > 6_000_000:
+            continue
+        cases.append((B, h, n_q, n_k, mask))
+    return cases
+
+
+def _f32_cases(n=8, seed=15):
+    """Small fp32 launches (the wave-per-query kernel)."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    while len(cases) < n:
+        B, h = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        mask = int(rng.integers(0, 4))
+        n_q = int(rng.integers(1, 300))
+        n_k = n_q if mask & 1 else int(rng.integers(1, 400))
+        cases.append((B, h, n_q, n_k, mask))
+    return cases
+
+
 @pytest.fixture(scope="module")
 def dev():
     if not torch.cuda.is_available():
@@ -136,3 +168,36 @@ def test_random_decode(dev, B, h, n_q, n_k, mask):
     want = oracle.sdpa_ref(to_f64(x["Q"]), to_f64(x["K"]), to_f64(x["V"]), x["scale"], mask,
                            None if kl is None else kl.numpy())
     _close(O, want, f"decode {B}x{h}x{n_q}x{n_k} m{mask}")
+
+
+@pytest.mark.parametrize("B,h,n_q,n_k,mask", _key_split_cases())
+def test_random_sdpa_key_split(dev, B, h, n_q, n_k, mask):
+    w = WORKLOADS["long_causal_sdpa"].replace(name="random", B=B, h=h, n_q=n_q, n_k=n_k, mask=mask,
+                                              key_len_range=None, description="random")
+    x = generate(w, seed=B * 131 + n_q * 31 + n_k)
+    kl = x["key_lengths"]
+    print(f"[gpu case] sdpa_forward key split B={B} h={h} n_q={n_q} n_k={n_k} mask={mask} "
+          f"kl={None if kl is None else kl.tolist()}", flush=True)
+    O = hafa.sdpa_forward(x["Q"].to(dev), x["K"].to(dev), x["V"].to(dev), x["scale"], mask, kl)
+    torch.cuda.synchronize()
+    want = oracle.sdpa_ref(to_f64(x["Q"]), to_f64(x["K"]), to_f64(x["V"]), x["scale"], mask,
+                           None if kl is None else kl.numpy())
+    _close(O, want, f"sdpa key split {B}x{h}x{n_q}x{n_k} m{mask}")
+
+
+@pytest.mark.parametrize("B,h,n_q,n_k,mask", _f32_cases())
+def test_random_sdpa_f32(dev, B, h, n_q, n_k, mask):
+    w = WORKLOADS["sdpa_f32_tiny"].replace(name="random", B=B, h=h, n_q=n_q, n_k=n_k, mask=mask,
+                                           key_len_range=None, description="random")
+    x = generate(w, seed=B * 17 + n_q * 31 + n_k)
+    kl = x["key_lengths"]
+    print(f"[gpu case] sdpa_forward fp32 B={B} h={h} n_q={n_q} n_k={n_k} mask={mask}", flush=True)
+    O = hafa.sdpa_forward(x["Q"].to(dev), x["K"].to(dev), x["V"].to(dev), x["scale"], mask, kl)
+    torch.cuda.synchronize()
+    want = oracle.sdpa_ref(to_f64(x["Q"]), to_f64(x["K"]), to_f64(x["V"]), x["scale"], mask,
+                           None if kl is None else kl.numpy())
+    g = to_f64(O)
+    assert np.all(np.isfinite(g))
+    err = float(np.abs(g - want).max())
+    print(f"  fp32 {B}x{h}x{n_q}x{n_k} m{mask}: max_abs={err:.3e}", flush=True)
+    assert err <= 1e-5, err
