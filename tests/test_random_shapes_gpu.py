@@ -1,8 +1,8 @@
 """GPU parity on seeded random shapes: bare attention (one and two key
 groups per workgroup, and fp32), the multi-head block (one- and
 two-heads-per-workgroup fused kernels, the staged path) and the small-batch
-decoding step, each against the fp64 oracle with the tolerances of the
-north star (bf16: max-abs 2e-2, relative L2 5e-3; fp32: max-abs 1e-5).
+decoding step, each against the fp64 oracle within the parity bars (bf16:
+max-abs 2e-2, relative L2 5e-3; fp32: max-abs 1e-5).
 
 The shapes come from a fixed numpy generator, so every run checks the same
 cases; each case is announced (flushed) before its launch.  Sizes are kept
