@@ -233,6 +233,22 @@ def test_sdpa_key_split(dev, B, h, n_q, n_k, mask, kl):
     assert lerr <= 2.0 ** -8 + 1e-6
 
 
+def test_sdpa_key_split_padded_chunks(dev):
+    """A padded batch beyond one launch (256 batches per launch) over more
+    than 1024 keys: both chunks take the two-key-group workgroups; every
+    batch's length is honoured (one of them a single key)."""
+    B, h, n_q, n_k = 300, 1, 40, 1100
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.bfloat16, seed=300)
+    g = torch.Generator("cpu")
+    g.manual_seed(301)
+    kl = torch.randint(1, n_k + 1, (B,), generator=g).tolist()
+    kl[0], kl[257], kl[-1] = 1, n_k, 700
+    announce("sdpa_forward bf16 key split, padded, two launches", dict(B=B, n_q=n_q, n_k=n_k))
+    O = run_sdpa(dev, Q, K, V, 0.125, 2, kl)
+    torch.cuda.synchronize()
+    assert_bf16_close(O, ref_sdpa(Q, K, V, 0.125, 2, kl), "key split padded chunks")
+
+
 # ------------------------------------------------------------------ edge shapes
 
 EDGE = [
