@@ -330,6 +330,22 @@ def test_sdpa_f32_eight_lane_kernel(dev, B, h, n_q, n_k, mask, kl):
     assert_f32_close(O, ref_sdpa(Q, K, V, 0.125, mask, kl), f"f32 {B}x{h}x{n_q}x{n_k} m{mask}")
 
 
+def test_sdpa_f32_padded_chunks(dev):
+    """fp32 over a padded batch beyond one launch: the first 256 batches fill
+    the compute units (eight lanes per query), the other 44 do not (one wave
+    per query); every batch's length is honoured."""
+    B, h, n_q, n_k = 300, 1, 5, 70
+    Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.float32, seed=302)
+    g = torch.Generator("cpu")
+    g.manual_seed(303)
+    kl = torch.randint(1, n_k + 1, (B,), generator=g).tolist()
+    kl[0], kl[256], kl[-1] = 1, n_k, 1
+    announce("sdpa_forward f32 padded, two launches", dict(B=B, n_q=n_q, n_k=n_k))
+    O = run_sdpa(dev, Q, K, V, 0.125, 2, kl)
+    torch.cuda.synchronize()
+    assert_f32_close(O, ref_sdpa(Q, K, V, 0.125, 2, kl), "f32 padded chunks")
+
+
 @pytest.mark.parametrize("B,mask", [(256, 2), (256, 3), (257, 3), (1024, 2), (1024, 3)])
 def test_sdpa_bf16_max_padded_batch(dev, B, mask):
     """Per-batch key lengths up to the largest padded batch (1024; they
