@@ -14,15 +14,15 @@
 //   buffers, NS-1 tiles ahead of the one being computed; 16-byte chunks are
 //   XOR-swizzled so that both LDS read patterns are conflict-free.  A wave
 //   skips the tiles none of its queries can see (causal).
-//   Key split (KS = 2, for launches too small to give every SIMD several
-//   waves): the workgroup holds two groups of NW waves over the same
-//   queries; group 0 takes the first half of the query tile's key tiles,
-//   group 1 the second half, each through its own ring slot of every stage.
-//   At the end group 1 hands its softmax state (reference value, sum,
-//   accumulators) to group 0 through LDS, which merges the two (the
+//   Key split (KS = 2 or 4, for launches too small to give every SIMD
+//   several waves): the workgroup holds KS groups of NW waves over the same
+//   queries; group j takes the j-th of KS consecutive runs of the query
+//   tile's key tiles, each group through its own ring slot of every stage.
+//   At the end groups 1 .. KS-1 hand their softmax states (reference value,
+//   sum, accumulators) to group 0 through LDS, which merges them (the
 //   streaming softmax's own rescaling rule) and writes the output.  The
-//   longest chain of dependent tiles a wave walks is halved and twice as
-//   many waves share each SIMD.
+//   longest chain of dependent tiles a wave walks shrinks KS-fold and KS
+//   times as many waves share each SIMD.
 #include "wave_attention.h"
 
 namespace mha {
@@ -31,17 +31,20 @@ namespace {
 using namespace dev;
 
 // WPE waves per SIMD (4: <= 128 VGPRs, 3: <= 168).  KS key groups of NW
-// waves each (1 or 2).  LDS: NS * KS * 16 KB per workgroup.
+// waves each (1, 2 or 4).  LDS: NS * KS * 16 KB per workgroup.
 template <int NW, int NS, int WPE, int KS>
 __global__ __launch_bounds__(NW * KS * 64) __attribute__((amdgpu_waves_per_eu(WPE, WPE)))
 void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
   static_assert(NS == 2 || NS == 3, "ring depth");
-  static_assert(KS == 1 || (KS == 2 && NS == 2), "key split: two groups, two-slot ring");
+  static_assert(KS == 1 || ((KS == 2 || KS == 4) && NS == 2), "key split: two or four groups, two-slot ring");
   constexpr int BLK = KT * D * 2 / 1024;  // 1 KB blocks per tile and matrix
   constexpr int CHW = BLK / NW;           // load instructions per wave, tile and matrix
   constexpr int QT = NW * 32;
   static_assert(CHW * NW == BLK, "waves must split the tile evenly");
-  static_assert(KS == 1 || NW * 32 * 64 * 4 <= NS * KS * KT * D * 2, "merge buffer fits the K ring");
+  // Merge buffers (the key split): groups 1 and 2 in the K ring, group 3 and
+  // the reference values and sums in the V ring.
+  static_assert(KS == 1 || (KS < 4 ? 1 : 2) * NW * 32 * 64 * 4 <= NS * KS * KT * D * 2, "merge: K ring");
+  static_assert(KS < 4 || NW * 32 * 64 * 4 + 3 * NW * 2 * 64 * 4 <= NS * KS * KT * D * 2, "merge: V ring");
 
   // Ring slot s of group j: Ks[s][j], Vs[s][j].
   __shared__ __attribute__((aligned(1024))) __bf16 Ks[NS][KS][KT * D];
@@ -158,14 +161,20 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
   }
   wait_vmcnt<0>();  // no load may still target LDS when the workgroup ends
 
-  if constexpr (KS == 2) {
-    // Group 1 hands its state to group 0 through the (now idle) ring:
-    // accumulator j of lane l of query block w at Ks-float [w][j][l] (32 a
-    // lane: exactly the K ring), m and l at Vs-float [w][0 or 1][l].
-    float* acc_x = (float*)&Ks[0][0][0] + wave * 32 * 64 + lane;
-    float* ml_x = (float*)&Vs[0][0][0] + wave * 2 * 64 + lane;
+  if constexpr (KS > 1) {
+    // Groups 1 .. KS-1 hand their states to group 0 through the (now idle)
+    // ring.  Group j's accumulators: 32 floats a lane, float i of lane l of
+    // query block w at [w][i][l] in a 32 KB region (the K ring's halves,
+    // then the V ring's first); m and l at [j - 1][w][0 or 1][l] after them.
+    constexpr int ACC = NW * 32 * 64;  // floats of one group's accumulators
+    auto acc_of = [&](int j) -> float* {
+      return j <= 2 ? (float*)&Ks[0][0][0] + (j - 1) * ACC : (float*)&Vs[0][0][0] + (j - 3) * ACC;
+    };
+    float* ml_base = (float*)&Vs[0][0][0] + (KS == 4 ? ACC : 0);
     __syncthreads();  // every wave is done with the tiles
-    if (kg == 1) {
+    if (kg > 0) {
+      float* acc_x = acc_of(kg) + wave * 32 * 64 + lane;
+      float* ml_x = ml_base + ((kg - 1) * NW + wave) * 2 * 64 + lane;
       ml_x[0] = wa.m;
       ml_x[64] = wa.l;
 #pragma unroll
@@ -175,14 +184,19 @@ void attn_fwd_bf16_d64_kernel(const AttnArgs a) {
       }
     }
     __syncthreads();
-    if (kg == 1) return;
-    f32x16 p0, p1;
+    if (kg > 0) return;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      p0[i] = acc_x[i * 64];
-      p1[i] = acc_x[(16 + i) * 64];
+    for (int j = 1; j < KS; ++j) {
+      const float* acc_x = acc_of(j) + wave * 32 * 64 + lane;
+      const float* ml_x = ml_base + ((j - 1) * NW + wave) * 2 * 64 + lane;
+      f32x16 p0, p1;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        p0[i] = acc_x[i * 64];
+        p1[i] = acc_x[(16 + i) * 64];
+      }
+      wa.merge(ml_x[0], ml_x[64], p0, p1);
     }
-    wa.merge(ml_x[0], ml_x[64], p0, p1);
   }
 
   const float inv = wa.inv_sum();
@@ -211,6 +225,7 @@ hipError_t launch_attn_bf16_d64_cfg(const AttnArgs& a, int cfg, hipStream_t s, L
     case 4: return launch_cfg<8, 3, 4>(a, s, ev);
     case 5: return launch_cfg<8, 3, 3>(a, s, ev);
     case 6: return launch_cfg<4, 2, 4, 2>(a, s, ev);
+    case 7: return launch_cfg<4, 2, 4, 4>(a, s, ev);
     default: return hipErrorInvalidValue;
   }
 }
@@ -238,7 +253,13 @@ hipError_t launch_attn_bf16_d64(const AttnArgs& a, hipStream_t s, LaunchEvents e
   // With two workgroups per compute unit (4 x 16 x 1024) it gains nothing,
   // and it loses where the key range is short (32 x 8 x 100: 6.7 -> 7.6 us;
   // 16 x 8 x 512 causal: 12.9 -> 15.1 us).
+  // From 2048 keys on, four key groups (16 waves, all 128 KB of LDS ring):
+  // 1 x 8 x 4096 49.4 -> 44.7 us, causal 42.1 -> 37.1 us, 1 x 4 x 8192
+  // 90 -> 79 us, 1 x 16 x 2048 25.8 -> 25.1 us against two groups; at 1024
+  // keys two groups stay ahead (2 x 8 x 1024 14.1 vs 14.7 us).
   const int64_t wg4 = (int64_t)a.B * a.h * ((a.n_q + 127) / 128);
+  if (wg4 <= (int64_t)device_compute_units() && a.n_k >= 2048)
+    return launch_attn_bf16_d64_cfg(a, 7, s, ev);
   if (wg4 <= (int64_t)device_compute_units() && a.n_k >= 1024)
     return launch_attn_bf16_d64_cfg(a, 6, s, ev);
   // Otherwise 4-wave workgroups (128 queries) with a 2-tile ring and four

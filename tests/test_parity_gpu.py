@@ -204,20 +204,25 @@ def test_sdpa_unmasked_eight_wave_workgroups(dev):
 KEY_SPLIT = [
     # (B, h, n_q, n_k, mask, key_lengths): at most one 4-wave workgroup per
     # compute unit over at least 1024 keys, where the launch takes two key
-    # groups per workgroup
+    # groups per workgroup (four from 2048 keys on)
     (1, 2, 300, 1500, 0, None),            # ragged query and key tiles
     (1, 3, 1100, 1100, 1, None),           # causal: the second group sees part or none of a tile
     (2, 2, 200, 2000, 2, [1, 1500]),       # one visible key: the second group sees nothing
     (2, 1, 1030, 1030, 3, [1030, 700]),    # causal + padding
-    (1, 1, 33, 4096, 0, None),             # one wave of queries per workgroup has 1 query
+    (1, 1, 33, 4096, 0, None),             # four groups; one wave of queries has 1 query
     (1, 8, 128, 1024, 2, [1024]),          # exactly 16 key tiles, 8 per group
+    # from 2048 keys on, four key groups
+    (1, 2, 300, 2500, 0, None),            # ragged: 40 tiles, 10 per group
+    (1, 2, 2100, 2100, 1, None),           # causal: early query tiles leave groups 1-3 idle
+    (2, 1, 100, 3000, 2, [1, 2999]),       # one visible key: groups 1-3 see nothing
+    (1, 3, 64, 2048, 2, [2048]),           # exactly 32 tiles, 8 per group
 ]
 
 
 @pytest.mark.parametrize("B,h,n_q,n_k,mask,kl", KEY_SPLIT)
 def test_sdpa_key_split(dev, B, h, n_q, n_k, mask, kl):
-    """The two-key-group workgroups against the oracle on every row, and
-    their row log-sum-exp (the backward pass's input) to 2^-8."""
+    """The two- and four-key-group workgroups against the oracle on every
+    row, and their row log-sum-exp (the backward pass's input) to 2^-8."""
     Q, K, V = sdpa_inputs(B, h, n_q, n_k, torch.bfloat16, seed=7 * n_q + n_k)
     announce("sdpa_forward bf16 key split", dict(B=B, h=h, n_q=n_q, n_k=n_k, mask=mask, kl=kl))
     Qd, Kd, Vd = (t.to(dev) for t in (Q, K, V))
