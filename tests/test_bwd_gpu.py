@@ -73,6 +73,10 @@ CASES = [
     (4, 8, 100, 100, 0, None, "the encoder block's heads"),
     # more padded batches than one launch carries lengths for (two launches per kernel)
     (300, 1, 20, 20, 3, [1 + (i * 7) % 20 for i in range(300)], "300 padded batches"),
+    # forwards whose workgroups split the keys over two or four groups of waves
+    (1, 2, 200, 1500, 0, None, "two key groups in the forward"),
+    (1, 2, 1100, 1100, 1, None, "causal, two key groups in the forward"),
+    (1, 2, 300, 2500, 2, [2500], "four key groups in the forward"),
 ]
 
 
